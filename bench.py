@@ -1,0 +1,189 @@
+"""Benchmark of the DLRM sparse hot path on one MI355X.
+
+One step = the whole path over one synthetic batch of the multi-hot bf16
+workload (26 tables, D=128, B=16384, bag lengths truncated-geometric on
+[1,100] with mean 20, Zipf(1.05) rows):
+    emb_bag_fwd -> dlrm_interact_fwd -> dlrm_interact_bwd -> emb_bag_bwd_adagrad
+(sort / unique / segment-reduce / row-wise Adagrad in place on the bf16
+tables, all integer outputs requested).  Inputs are resident in HBM before the
+timed region; R pre-generated batches rotate.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, batch, n_samples: int):
+    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import oracle
+    from recommendation_model_sparse_amd.synth import subset_tables
+
+    cores = len(os.sched_getaffinity(0))
+    S = np.arange(n_samples)
+    sub_wl, sub, row_ids = batch.sample_subset(S)
+    tabs = subset_tables(wl, row_ids)
+    states = [np.zeros(len(r), np.float32) for r in row_ids]
+    g = batch.grad_out()[S]
+    t0 = time.perf_counter()
+    pooled, _ = oracle.emb_bag_fwd(tabs, sub.indices, sub.offsets, sub.weights, len(S), threads=cores)
+    p32 = pooled.astype(np.float32)
+    oracle.interact_fwd(sub.dense, p32, threads=cores)
+    _, gp, _, _ = oracle.interact_bwd(g, sub.dense, p32, threads=cores)
+    oracle.emb_bag_bwd_adagrad(tabs, states, sub.indices, sub.offsets, sub.weights, len(S),
+                               gp.astype(np.float32), wl.lr, wl.eps)
+    dt = time.perf_counter() - t0
+    return {"value": len(S) / dt, "unit": "samples/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(S)} of {wl.B} samples of one batch ({sub.nnz} lookups): the full step "
+                      f"(pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--cpu-samples", type=int, default=8192)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
+              f"single-GPU: tables are not sharded and no collective runs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from recommendation_model_sparse_amd import (AdagradOutputs, dlrm_interact_bwd, dlrm_interact_fwd,
+                                                 dlrm_synth_fill_table, emb_bag_bwd_adagrad,
+                                                 emb_bag_bwd_workspace_size, emb_bag_fwd, synth)
+    from recommendation_model_sparse_amd.configs import make_config
+
+    dev = torch.device("cuda:0")
+    wl = make_config(3)
+    log(f"[bench] workload {wl.name}: {wl.note}")
+    t0 = time.time()
+    tabs = []
+    for t, v in enumerate(wl.rows):
+        x = torch.empty((v, wl.D), dtype=torch.bfloat16, device=dev)
+        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
+        tabs.append(x)
+    states = [torch.zeros(v, dtype=torch.float32, device=dev) for v in wl.rows]
+    torch.cuda.synchronize()
+    log(f"[bench] tables {wl.table_bytes() / 1e9:.2f} GB filled in {time.time() - t0:.1f}s")
+
+    batches, host_batches = [], []
+    for i in range(args.rotate):
+        b = wl.batch(i)
+        host_batches.append(b)
+        batches.append(dict(idx=torch.from_numpy(b.indices).to(dev),
+                            off=torch.from_numpy(b.offsets).to(dev),
+                            dense=torch.from_numpy(b.dense).to(dev),
+                            g=torch.from_numpy(b.grad_out()).to(dev), nnz=b.nnz))
+        log(f"[bench] batch {i}: nnz={b.nnz}")
+    max_nnz = max(b["nnz"] for b in batches)
+    ws = torch.empty(emb_bag_bwd_workspace_size(wl.rows, wl.D, wl.B, max_nnz), dtype=torch.uint8, device=dev)
+    outs = AdagradOutputs(max_nnz, dev)
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
+    gdense = torch.empty((wl.B, wl.D), dtype=torch.float32, device=dev)
+    gpooled = torch.empty_like(pooled)
+    names = ["emb_bag_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_adagrad"]
+
+    def step(i, ev=None):
+        b = batches[i % len(batches)]
+        if ev is not None:
+            ev[0].record()
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+        if ev is not None:
+            ev[1].record()
+        dlrm_interact_fwd(b["dense"], pooled, out=inter)
+        if ev is not None:
+            ev[2].record()
+        dlrm_interact_bwd(b["g"], b["dense"], pooled, grad_dense=gdense, grad_pooled=gpooled)
+        if ev is not None:
+            ev[3].record()
+        emb_bag_bwd_adagrad(tabs, states, b["idx"], b["off"], None, gpooled, wl.lr, wl.eps,
+                            workspace=ws, outputs=outs)
+        if ev is not None:
+            ev[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole-step wall clock between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / args.steps * 1e3
+
+    # per-call HIP event times on the launching stream, over a second identical region
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
+               for k, n in enumerate(names)}
+    log("[bench] per call (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in call_ms.items()))
+
+    nnz_avg = float(np.mean([b["nnz"] for b in batches]))
+    es = wl.elem_size
+    gathered = nnz_avg * wl.D * es
+    k1_bytes = gathered + nnz_avg * 8 + (wl.T * wl.B + 1) * 8 + wl.B * wl.T * wl.D * 4
+    k1_s = call_ms["emb_bag_fwd"] / 1e3
+    gathered_gbps = gathered / k1_s / 1e9
+    k1_gbps = k1_bytes / k1_s / 1e9
+
+    res = {
+        "metric": "samples/sec + gathered-embedding GB/s (fraction of HBM peak), 1 MI355X",
+        "value": wl.B / (ms / 1e3),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 tables, fp32 accumulation",
+        "data": "synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), Zipf(1.05) rows)",
+        "config": {"workload": "multi-hot bf16 training step: 26 tables, D=128, B=16384, "
+                               "bag length truncated-geometric [1,100] mean 20, Zipf(1.05), "
+                               "V log-uniform [1e3,1e7]",
+                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "nnz_avg": nnz_avg,
+                   "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
+        "gathered_GBps": gathered_gbps,
+        "gathered_frac_of_hbm_peak": gathered_gbps / HBM_PEAK_GBPS,
+        "fwd_samples_per_s": wl.B / ((call_ms["emb_bag_fwd"] + call_ms["dlrm_interact_fwd"]) / 1e3),
+        "call_ms": call_ms,
+        "roofline": {"bound": "hbm", "kernel": "emb_bag_fwd (k_pool_wave_per_bag, bf16, G=16)",
+                     "achieved": k1_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": k1_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": k1_bytes},
+    }
+    if not args.no_cpu:
+        log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")
+        res["cpu_baseline"] = cpu_baseline(wl, host_batches[0], args.cpu_samples)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

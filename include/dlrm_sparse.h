@@ -1,0 +1,181 @@
+/*
+ * dlrm_sparse.h -- C ABI of the DLRM sparse hot path for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute is defined on these pages:
+ *   [P5] robocikowo.com "DLRM" (technologie-ai): paragraph "Forward pass",
+ *        stages (2) lookup, (3) pairwise dots / upper triangle, (4) the
+ *        concatenation with the bottom-MLP output; the paragraph on the
+ *        embedding tables (E_i: V_i x D, indexed lookup); the paragraph on
+ *        the interaction layer (N vectors = bottom-MLP output + N-1
+ *        embeddings, N(N-1)/2 values); the training sentence (SGD/Adagrad).
+ *   [P2] notes.helloworld.co.in "Deep Learning Recommendation Model (DLRM)",
+ *        section "The architecture".
+ *   [P4] vinsonli.com "The embedding table is the model".
+ *   [P1] technolynx.com "DLRM explained", section "How does DLRM actually work?".
+ * Where the pages leave a step open (bag pooling, triu order, backward,
+ * row-wise Adagrad), the reading taken is stated at the call.
+ *
+ * Conventions common to every call
+ *   - Pointers are DEVICE pointers unless marked (host).  Host arrays are
+ *     read before the call returns.
+ *   - The caller allocates and owns every device buffer, including the
+ *     workspace, and keeps it alive until the work on `stream` completes.
+ *     The library allocates no device memory and keeps no mutable state, so
+ *     calls on different streams may run concurrently on distinct buffers.
+ *   - Every call enqueues on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns without waiting, except with DLRM_FLAG_CHECK_INDICES, which
+ *     synchronises the stream to report the result of the check.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing has been enqueued and outputs are untouched.  A failed
+ *     launch returns DLRM_ERR_HIP.
+ *   - Bags are table-major: bag (t, b) has id t*B + b; offsets has T*B + 1
+ *     entries, offsets[0] = 0, offsets[T*B] = nnz, non-decreasing, and every
+ *     index of a bag of table t lies in [0, rows[t]).  Breaking these is
+ *     undefined behaviour unless DLRM_FLAG_CHECK_INDICES is given.
+ *   - Outputs must not alias inputs.
+ *   - Limits: 1 <= T <= 64; 1 <= D <= 512 with D*sizeof(elem) a multiple of
+ *     16 bytes (D % 4 == 0 for fp32 tables, D % 8 == 0 for bf16); T*B < 2^31;
+ *     nnz < 2^31; table pointers 16-byte aligned; indices/offsets 8-byte
+ *     aligned; float buffers 16-byte aligned.
+ */
+#ifndef DLRM_SPARSE_H
+#define DLRM_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *dlrm_stream_t;
+
+/* Table element type.  bf16 values are the upper 16 bits of an fp32. */
+typedef enum { DLRM_F32 = 0, DLRM_BF16 = 1 } dlrm_dtype;
+
+enum {
+    DLRM_OK = 0,
+    DLRM_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment          */
+    DLRM_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits          */
+    DLRM_ERR_HIP = -3,         /* a HIP launch or runtime call failed            */
+    DLRM_ERR_INDEX_RANGE = -4, /* CHECK_INDICES found a bad index or offset      */
+    DLRM_ERR_WORKSPACE = -5    /* workspace missing or smaller than required     */
+};
+
+/* Validate offsets and indices on the device before the work (a debug aid):
+ * the call synchronises `stream` and returns DLRM_ERR_INDEX_RANGE if any
+ * offset decreases, offsets[0] != 0, offsets[T*B] != nnz, or an index lies
+ * outside its table.  With this flag the call is not graph-capturable. */
+#define DLRM_FLAG_CHECK_INDICES 1u
+
+/*
+ * Embedding-bag lookup with sum pooling ([P5] stage (2) and the table
+ * paragraph; [P1] one lookup per sparse feature; [P2] the vectors come out
+ * at equal width D).  A multi-valued feature is a bag of indices; its rows
+ * are summed, or weighted by one fp32 weight per lookup:
+ *
+ *     out[b][t][d] = sum_{j in [offsets[t*B+b], offsets[t*B+b+1])} w_j * E_t[indices[j]][d]
+ *
+ * w_j = 1 when per_sample_weights is NULL; an empty bag gives zeros.
+ * Accumulation is fp32 (bf16 rows widen exactly).  The summation order is
+ * fixed, so results are bitwise reproducible.
+ *
+ *   tables  (host) [T] device pointers, table t row-major [rows[t]][D] of `dtype`
+ *   rows    (host) [T] row counts V_t >= 1
+ *   indices [nnz] int64; offsets [T*B+1] int64; per_sample_weights [nnz] fp32 or NULL
+ *   out     [B][T][D] fp32 (written in full)
+ */
+int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                const float *per_sample_weights, int64_t B, int64_t nnz, float *out,
+                uint32_t flags, dlrm_stream_t stream);
+
+/*
+ * Dot-product interaction, forward ([P5] stage (3) and the interaction
+ * paragraph; [P2] "The architecture"; [P4]).  Per sample the N vectors are
+ * the rows of X (N x D): row 0 the dense (bottom-MLP) vector, rows 1..N-1 the
+ * pooled embeddings of tables 0..N-2.  The output row holds the strict upper
+ * triangle of X X^T, N(N-1)/2 values listed row by row (i < j, i then j
+ * ascending), followed by the dense vector ([P5] stage (4): interaction
+ * values first, then the bottom-MLP output):
+ *
+ *     out[b] = [ <x0,x1>, <x0,x2>, ..., <x_{N-2},x_{N-1}>, dense[b][0..D-1] ]
+ *
+ *   dense  [B][D] fp32; pooled [B][N-1][D] fp32 (the layout emb_bag_fwd writes)
+ *   out    [B][N(N-1)/2 + D] fp32
+ *   Limits: 1 <= N <= 65, D % 4 == 0, D <= 512.  fp32 arithmetic.
+ */
+int dlrm_interact_fwd(const float *dense, const float *pooled, int64_t B, int32_t N, int32_t D,
+                      float *out, dlrm_stream_t stream);
+
+/*
+ * Dot-product interaction, backward: the derivative of dlrm_interact_fwd
+ * (the pages give the forward map and say it is trained by gradient descent,
+ * [P5] training sentence).  With g = grad_out[b], G the symmetric N x N
+ * matrix with zero diagonal and G[i][j] = G[j][i] = g[p(i,j)] (p the triu
+ * position above):
+ *
+ *     dX = G X;   grad_dense[b] = dX[0] + g[P .. P+D-1];   grad_pooled[b][t] = dX[t+1]
+ *
+ *   grad_out [B][P+D]; dense [B][D]; pooled [B][N-1][D]  (all fp32)
+ *   grad_dense [B][D]; grad_pooled [B][N-1][D]           (fp32, written in full)
+ *   Same limits as the forward.
+ */
+int dlrm_interact_bwd(const float *grad_out, const float *dense, const float *pooled, int64_t B,
+                      int32_t N, int32_t D, float *grad_dense, float *grad_pooled,
+                      dlrm_stream_t stream);
+
+/* Bytes of device workspace emb_bag_bwd_adagrad needs for these sizes
+ * (0 on invalid sizes).  rows is a host array of T row counts. */
+size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int32_t D, int64_t B,
+                                  int64_t nnz);
+
+/*
+ * Embedding backward with row-wise Adagrad, applied in place ([P5] training
+ * sentence names SGD/Adagrad; the rest is the reading stated here).  The
+ * pooling is linear in the table, so row r of table t receives
+ *
+ *     G[d] = sum over lookups j of (t, r) of  w_j * grad_pooled[b(j)][t][d]
+ *
+ * Steps: key_j = rowbase[t] + indices[j] (rowbase = exclusive prefix sum of
+ * rows); a stable sort of the keys; unique keys and their segments; the
+ * per-segment sum G (fp32, fixed order: bitwise reproducible); then, for
+ * each unique row only,
+ *
+ *     s      <- s + (1/D) * sum_d G[d]^2        (state[t][r], fp32)
+ *     E[r,d] <- E[r,d] - lr * G[d] / (sqrt(s) + eps)
+ *
+ * (Duchi, Hazan & Singer 2011, with one accumulator per row).  Rows that no
+ * lookup touches are not written.  bf16 tables are updated in fp32 and
+ * stored round-to-nearest-even.
+ *
+ *   tables  (host) [T] device pointers [rows[t]][D] of `dtype`, updated in place
+ *   state   (host) [T] device pointers [rows[t]] fp32, updated in place
+ *   rows    (host) [T]; sum of rows must be <= 2^32
+ *   indices, offsets, per_sample_weights: as emb_bag_fwd (weights may be NULL)
+ *   grad_pooled [B][T][D] fp32
+ *   workspace: >= emb_bag_bwd_workspace_size(T, rows, D, B, nnz) bytes, 256-byte aligned
+ *   Optional outputs (written when non-NULL):
+ *     unique_keys_out     [nnz] int64: the U distinct keys, ascending (first U entries)
+ *     segment_offsets_out [nnz+1] int64: first sorted position of each key; entry U = nnz
+ *     sorted_pos_out      [nnz] int32: original position of each sorted position
+ *     num_unique_out      [1] int64: U
+ *   Limits: D a power of two in [4, 512] (bf16: [8, 512]).
+ */
+int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
+                        int32_t D, int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                        const float *per_sample_weights, int64_t B, int64_t nnz,
+                        const float *grad_pooled, float lr, float eps, void *workspace,
+                        size_t workspace_bytes, int64_t *unique_keys_out,
+                        int64_t *segment_offsets_out, int32_t *sorted_pos_out,
+                        int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream);
+
+/* Static description of a status code. */
+const char *dlrm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLRM_SPARSE_H */

@@ -1,0 +1,20 @@
+"""MI355X-native DLRM sparse hot path: embedding-bag lookup, dot-product
+interaction (forward/backward) and the sparse row-wise Adagrad step, as HIP
+kernels for gfx950 behind a C ABI (``include/dlrm_sparse.h``).
+
+The functions below are thin ctypes wrappers of that ABI; see ``binding``.
+"""
+from .binding import (  # noqa: F401
+    DLRM_BF16,
+    DLRM_F32,
+    DLRM_FLAG_CHECK_INDICES,
+    AdagradOutputs,
+    DlrmError,
+    dlrm_interact_bwd,
+    dlrm_interact_fwd,
+    dlrm_status_string,
+    dlrm_synth_fill_table,
+    emb_bag_bwd_adagrad,
+    emb_bag_bwd_workspace_size,
+    emb_bag_fwd,
+)

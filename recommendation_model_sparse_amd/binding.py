@@ -1,0 +1,217 @@
+"""Python binding of ``libdlrm_sparse.so`` (ctypes; argument marshalling only).
+
+Each function has the name of the C entry point it calls and passes device
+pointers of torch tensors plus the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback: if the
+library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdlrm_sparse.so")
+
+DLRM_F32, DLRM_BF16 = 0, 1
+DLRM_FLAG_CHECK_INDICES = 1
+
+_lib = None
+
+
+class DlrmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, u32, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                          ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
+                                          ctypes.c_size_t)
+        L.emb_bag_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, u32, p]
+        L.dlrm_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p]
+        L.dlrm_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p]
+        L.emb_bag_bwd_workspace_size.argtypes = [i32, p, i32, i64, i64]
+        L.emb_bag_bwd_workspace_size.restype = sz
+        L.emb_bag_bwd_adagrad.argtypes = [p, p, p, i32, i32, i32, p, p, p, i64, i64, p, f32, f32,
+                                          p, sz, p, p, p, p, u32, p]
+        L.dlrm_status_string.argtypes = [ctypes.c_int]
+        L.dlrm_status_string.restype = ctypes.c_char_p
+        L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
+        for f in (L.emb_bag_fwd, L.dlrm_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
+                  L.dlrm_synth_fill_table):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dlrm_status_string(int(status)).decode()
+
+
+dlrm_status_string = status_string
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise DlrmError(rc, what)
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DLRM_F32
+    if t.dtype == torch.bfloat16:
+        return DLRM_BF16
+    raise TypeError(f"table dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _tables(tables: Sequence[torch.Tensor]):
+    T = len(tables)
+    if T == 0:
+        raise ValueError("no tables")
+    D = tables[0].shape[1]
+    code = _dtype_code(tables[0])
+    for t in tables:
+        if t.dim() != 2 or t.shape[1] != D or _dtype_code(t) != code or not t.is_contiguous():
+            raise ValueError("tables must be contiguous [V_t, D] of one dtype")
+    ptrs = (ctypes.c_void_p * T)(*[t.data_ptr() for t in tables])
+    rows = (ctypes.c_int64 * T)(*[t.shape[0] for t in tables])
+    return T, D, code, ptrs, rows
+
+
+def _contig(t: Optional[torch.Tensor], dtype, name):
+    if t is None:
+        return None
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous {dtype}")
+    return t
+
+
+def emb_bag_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: torch.Tensor,
+                per_sample_weights: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """Pooled embeddings [B, T, D] fp32 (C: emb_bag_fwd)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    indices = _contig(indices, torch.int64, "indices")
+    offsets = _contig(offsets, torch.int64, "offsets")
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    B = (offsets.numel() - 1) // T
+    if offsets.numel() != T * B + 1:
+        raise ValueError("offsets must have T*B+1 entries")
+    dev = tables[0].device
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    _check(lib().emb_bag_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
+                             indices.numel(), _ptr(out), flags, _stream(dev)), "emb_bag_fwd")
+    return out
+
+
+def dlrm_interact_fwd(dense: torch.Tensor, pooled: torch.Tensor,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[B, N(N-1)/2 + D] fp32 (C: dlrm_interact_fwd); pooled is [B, N-1, D]."""
+    dense = _contig(dense, torch.float32, "dense")
+    pooled = _contig(pooled, torch.float32, "pooled")
+    B, D = dense.shape
+    N = pooled.shape[1] + 1
+    P = N * (N - 1) // 2
+    if out is None:
+        out = torch.empty((B, P + D), dtype=torch.float32, device=dense.device)
+    _check(lib().dlrm_interact_fwd(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out),
+                                   _stream(dense.device)), "dlrm_interact_fwd")
+    return out
+
+
+def dlrm_interact_bwd(grad_out: torch.Tensor, dense: torch.Tensor, pooled: torch.Tensor,
+                      grad_dense: Optional[torch.Tensor] = None,
+                      grad_pooled: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(grad_dense [B, D], grad_pooled [B, N-1, D]) (C: dlrm_interact_bwd)."""
+    grad_out = _contig(grad_out, torch.float32, "grad_out")
+    dense = _contig(dense, torch.float32, "dense")
+    pooled = _contig(pooled, torch.float32, "pooled")
+    B, D = dense.shape
+    N = pooled.shape[1] + 1
+    if grad_dense is None:
+        grad_dense = torch.empty_like(dense)
+    if grad_pooled is None:
+        grad_pooled = torch.empty_like(pooled)
+    _check(lib().dlrm_interact_bwd(_ptr(grad_out), _ptr(dense), _ptr(pooled), B, N, D,
+                                   _ptr(grad_dense), _ptr(grad_pooled), _stream(dense.device)),
+           "dlrm_interact_bwd")
+    return grad_dense, grad_pooled
+
+
+def emb_bag_bwd_workspace_size(rows: Sequence[int], D: int, B: int, nnz: int) -> int:
+    T = len(rows)
+    r = (ctypes.c_int64 * T)(*rows)
+    return int(lib().emb_bag_bwd_workspace_size(T, r, D, B, nnz))
+
+
+class AdagradOutputs:
+    """Optional integer outputs of emb_bag_bwd_adagrad (device tensors)."""
+
+    def __init__(self, nnz: int, device):
+        n1 = max(nnz, 1)
+        self.unique_keys = torch.empty(n1, dtype=torch.int64, device=device)
+        self.segment_offsets = torch.empty(n1 + 1, dtype=torch.int64, device=device)
+        self.sorted_pos = torch.empty(n1, dtype=torch.int32, device=device)
+        self.num_unique = torch.empty(1, dtype=torch.int64, device=device)
+
+
+def emb_bag_bwd_adagrad(tables: Sequence[torch.Tensor], state: Sequence[torch.Tensor],
+                        indices: torch.Tensor, offsets: torch.Tensor,
+                        per_sample_weights: Optional[torch.Tensor], grad_pooled: torch.Tensor,
+                        lr: float, eps: float, workspace: Optional[torch.Tensor] = None,
+                        outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
+    """Row-wise Adagrad on the tables and states, in place (C: emb_bag_bwd_adagrad)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    if len(state) != T:
+        raise ValueError("one state vector per table")
+    for s, t in zip(state, tables):
+        if s.dtype != torch.float32 or s.numel() != t.shape[0] or not s.is_contiguous():
+            raise ValueError("state[t] must be contiguous fp32 [V_t]")
+    sptrs = (ctypes.c_void_p * T)(*[s.data_ptr() for s in state])
+    indices = _contig(indices, torch.int64, "indices")
+    offsets = _contig(offsets, torch.int64, "offsets")
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
+    B = (offsets.numel() - 1) // T
+    nnz = indices.numel()
+    dev = tables[0].device
+    need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = outputs
+    _check(lib().emb_bag_bwd_adagrad(
+        ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B, nnz,
+        _ptr(grad_pooled), float(lr), float(eps), _ptr(workspace), workspace.numel(),
+        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
+        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
+        _stream(dev)), "emb_bag_bwd_adagrad")
+    return o
+
+
+def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) -> None:
+    """Fill ``table`` with the counter-hash contents of table ``t`` (input generation)."""
+    if not table.is_contiguous() or table.dim() != 2:
+        raise ValueError("table must be contiguous [V, D]")
+    _check(lib().dlrm_synth_fill_table(_ptr(table), _dtype_code(table), table.shape[0],
+                                       table.shape[1], t, seed, float(scale),
+                                       _stream(table.device)), "dlrm_synth_fill_table")

@@ -1,0 +1,360 @@
+// Embedding-bag lookup with sum / weighted-sum pooling (the lookup stage of the DLRM forward
+// pass: robocikowo.com "DLRM", paragraph "Forward pass", stage (2), and its paragraph on the
+// embedding tables E_i: V_i x D).
+//
+// The operation is a gather of random table rows, so it is bound by HBM latency and bandwidth.
+// Design for gfx950:
+//   - A row is D*s bytes = G chunks of 16 bytes; a lane group of G lanes covers one row with
+//     one 16-byte load per lane (global_load_dwordx4), so every row read is fully coalesced.
+//   - Multi-hot bags: one wavefront per bag.  The wave loads up to 64 of the bag's indices
+//     with one coalesced load, broadcasts them with cross-lane permutes, and its 64/G lane
+//     groups each issue U row loads before the first use, so 64/G*U rows of the bag are in
+//     flight at once.  Group partial sums are combined in a fixed butterfly.
+//   - One-hot / short bags: each lane group owns BPG bags and issues the first row of all of
+//     them before accumulating.
+//   - Blocks are remapped so each XCD walks a contiguous range of bags; bags are table-major,
+//     so each XCD's L2 serves about T/8 tables and keeps more of their hot rows.
+//   - fp32 accumulation in a fixed order: results are bitwise reproducible; a bag of one row
+//     returns that row exactly.
+#include "common.h"
+
+namespace dlrm {
+namespace {
+
+struct PoolArgs {
+    const char *tables[kMaxTables];
+    const int64_t *indices;
+    const int64_t *offsets;
+    const float *weights;
+    float *out;
+    uint32_t B;
+    uint32_t nbags;
+    int32_t T;
+    int32_t D;
+    uint32_t row_bytes;
+    uint32_t nblocks;  // blocks launched (a multiple of 8)
+};
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<DLRM_F32> {
+    static constexpr int kPerChunk = 4;
+};
+template <>
+struct Elem<DLRM_BF16> {
+    static constexpr int kPerChunk = 8;
+};
+
+// acc += w * (16-byte chunk widened to fp32)
+template <int DT, bool WEIGHTED>
+__device__ __forceinline__ void accumulate(float *acc, const uint4 &v, float w) {
+    if constexpr (DT == DLRM_F32) {
+        const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                            __uint_as_float(v.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = WEIGHTED ? fmaf(w, x[e], acc[e]) : acc[e] + x[e];
+    } else {
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = bf16_lo(q[e]), hi = bf16_hi(q[e]);
+            acc[2 * e] = WEIGHTED ? fmaf(w, lo, acc[2 * e]) : acc[2 * e] + lo;
+            acc[2 * e + 1] = WEIGHTED ? fmaf(w, hi, acc[2 * e + 1]) : acc[2 * e + 1] + hi;
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_chunk(float *dst, const float *acc) {
+    constexpr int EPC = Elem<DT>::kPerChunk;
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4)
+        *reinterpret_cast<float4 *>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+}
+
+__device__ __forceinline__ uint4 load_row_chunk(const char *tab, int64_t idx, uint32_t row_bytes) {
+    return *reinterpret_cast<const uint4 *>(tab + static_cast<uint64_t>(idx) * row_bytes);
+}
+
+// One wavefront per bag (multi-hot).  G lanes per row, NG = 64/G groups, U rows per group in flight.
+template <int DT, int G, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
+    constexpr int NG = kWave / G;
+    constexpr int EPC = Elem<DT>::kPerChunk;
+    constexpr int U = 8;
+    const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
+    const uint32_t bag = lb * 4 + (threadIdx.x >> 6);
+    if (bag >= a.nbags) return;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane / G, c = lane % G;
+    const uint32_t t = bag / a.B, b = bag - t * a.B;
+    const char *tab = a.tables[t] + c * 16;
+    const int64_t start = a.offsets[bag], end = a.offsets[bag + 1];
+
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+    for (int64_t base = start; base < end; base += kWave) {
+        const int n = static_cast<int>(min<int64_t>(kWave, end - base));
+        const int64_t my_idx = lane < n ? a.indices[base + lane] : 0;
+        float my_w = 1.f;
+        if constexpr (WEIGHTED) my_w = lane < n ? a.weights[base + lane] : 0.f;
+        for (int r0 = 0; r0 < n; r0 += NG * U) {
+            uint4 v[U];
+            float w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = r0 + u * NG + grp;
+                const int src = r < n ? r : 0;
+                const int64_t idx = __shfl(my_idx, src);
+                w[u] = WEIGHTED ? __shfl(my_w, src) : 1.f;
+                v[u] = r < n ? load_row_chunk(tab, idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (r0 + u * NG + grp < n) accumulate<DT, WEIGHTED>(acc, v[u], w[u]);
+        }
+    }
+    // combine the NG group partials (fixed butterfly: every group ends with identical bits)
+#pragma unroll
+    for (int s = G; s < kWave; s <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], s);
+    if (grp == 0)
+        store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
+}
+
+// One lane group per bag (one-hot or short bags); each group owns BPG bags.
+template <int DT, int G, bool WEIGHTED, int BPG>
+__global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
+    constexpr int NG = kWave / G;
+    constexpr int EPC = Elem<DT>::kPerChunk;
+    const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
+    const uint32_t wave = lb * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int grp = lane / G, c = lane % G;
+    const uint32_t bag0 = wave * (NG * BPG) + grp;
+
+    int64_t s[BPG], e[BPG];
+    const char *tab[BPG];
+#pragma unroll
+    for (int k = 0; k < BPG; ++k) {
+        const uint32_t bag = bag0 + k * NG;
+        const bool ok = bag < a.nbags;
+        s[k] = ok ? a.offsets[bag] : 0;
+        e[k] = ok ? a.offsets[bag + 1] : 0;
+        tab[k] = a.tables[ok ? bag / a.B : 0] + c * 16;
+    }
+    float acc[BPG][EPC];
+#pragma unroll
+    for (int k = 0; k < BPG; ++k)
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) acc[k][q] = 0.f;
+
+    // first row of every bag: BPG row loads in flight per lane
+    {
+        int64_t idx[BPG];
+        float w[BPG];
+#pragma unroll
+        for (int k = 0; k < BPG; ++k) {
+            idx[k] = s[k] < e[k] ? a.indices[s[k]] : 0;
+            w[k] = (WEIGHTED && s[k] < e[k]) ? a.weights[s[k]] : 1.f;
+        }
+        uint4 v[BPG];
+#pragma unroll
+        for (int k = 0; k < BPG; ++k)
+            v[k] = s[k] < e[k] ? load_row_chunk(tab[k], idx[k], a.row_bytes) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < BPG; ++k)
+            if (s[k] < e[k]) accumulate<DT, WEIGHTED>(acc[k], v[k], w[k]);
+    }
+    // remaining rows, four in flight
+#pragma unroll
+    for (int k = 0; k < BPG; ++k) {
+        for (int64_t j = s[k] + 1; j < e[k]; j += 4) {
+            uint4 v[4];
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = j + u < e[k];
+                const int64_t idx = ok ? a.indices[j + u] : 0;
+                w[u] = (WEIGHTED && ok) ? a.weights[j + u] : 1.f;
+                v[u] = ok ? load_row_chunk(tab[k], idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (j + u < e[k]) accumulate<DT, WEIGHTED>(acc[k], v[u], w[u]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < BPG; ++k) {
+        const uint32_t bag = bag0 + k * NG;
+        if (bag < a.nbags) {
+            const uint32_t t = bag / a.B, b = bag - t * a.B;
+            store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc[k]);
+        }
+    }
+}
+
+// Any row width: one thread per (bag, 16-byte chunk).
+template <int DT, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_pool_generic(PoolArgs a, uint32_t chunks) {
+    constexpr int EPC = Elem<DT>::kPerChunk;
+    const uint64_t gid = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const uint64_t bag = gid / chunks;
+    if (bag >= a.nbags) return;
+    const uint32_t c = static_cast<uint32_t>(gid % chunks);
+    const uint32_t t = static_cast<uint32_t>(bag / a.B), b = static_cast<uint32_t>(bag - uint64_t(t) * a.B);
+    const char *tab = a.tables[t] + c * 16;
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    for (int64_t j = a.offsets[bag]; j < a.offsets[bag + 1]; ++j) {
+        const float w = WEIGHTED ? a.weights[j] : 1.f;
+        accumulate<DT, WEIGHTED>(acc, load_row_chunk(tab, a.indices[j], a.row_bytes), w);
+    }
+    store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
+}
+
+// ---------------------------------------------------------------- index / offset check
+
+struct CheckArgs {
+    int64_t rows[kMaxTables];
+    const int64_t *indices;
+    const int64_t *offsets;
+    uint32_t B;
+    uint32_t nbags;
+    int64_t nnz;
+    int *flag;
+};
+
+__global__ void k_set_int(int *p, int v) { *p = v; }
+
+__global__ __launch_bounds__(256) void k_check_csr(CheckArgs a) {
+    const uint64_t bag = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (a.nbags == 0) {
+        if (bag == 0 && (a.offsets[0] != 0 || a.nnz != 0)) *a.flag = 1;
+        return;
+    }
+    if (bag >= a.nbags) return;
+    const int64_t o0 = a.offsets[bag], o1 = a.offsets[bag + 1];
+    bool bad = o1 < o0 || o0 < 0 || o1 > a.nnz;
+    if (bag == 0 && o0 != 0) bad = true;
+    if (bag + 1 == a.nbags && o1 != a.nnz) bad = true;
+    const int64_t V = a.rows[bag / a.B];
+    const int64_t lo = max<int64_t>(o0, 0), hi = min<int64_t>(o1, a.nnz);
+    for (int64_t j = lo; j < hi; ++j) {
+        const int64_t i = a.indices[j];
+        if (i < 0 || i >= V) bad = true;
+    }
+    if (bad) *a.flag = 1;
+}
+
+}  // namespace
+
+// Runs the device-side CSR check; `flag` is 4 bytes of device scratch the caller lends.
+int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
+                        const int64_t *offsets, int64_t B, int64_t nnz, int *flag,
+                        hipStream_t stream) {
+    CheckArgs c{};
+    for (int t = 0; t < T; ++t) c.rows[t] = rows[t];
+    c.indices = indices;
+    c.offsets = offsets;
+    c.B = static_cast<uint32_t>(B);
+    c.nbags = static_cast<uint32_t>(T * B);
+    c.nnz = nnz;
+    c.flag = flag;
+    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, stream, flag, 0);
+    const uint32_t blocks = c.nbags == 0 ? 1 : (c.nbags + 255) / 256;
+    hipLaunchKernelGGL(k_check_csr, dim3(blocks), dim3(256), 0, stream, c);
+    if (hipGetLastError() != hipSuccess) return DLRM_ERR_HIP;
+    int host_flag = 0;
+    if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return DLRM_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return DLRM_ERR_HIP;
+    return host_flag ? DLRM_ERR_INDEX_RANGE : DLRM_OK;
+}
+
+namespace {
+
+template <int DT, int G, bool W>
+void launch_pool(const PoolArgs &a0, bool wave_per_bag, hipStream_t stream) {
+    PoolArgs a = a0;
+    constexpr int NG = kWave / G;
+    if (wave_per_bag) {
+        a.nblocks = round_up_xcd((a.nbags + 3) / 4);
+        hipLaunchKernelGGL((k_pool_wave_per_bag<DT, G, W>), dim3(a.nblocks), dim3(256), 0, stream, a);
+    } else {
+        constexpr int BPG = G >= 64 ? 1 : (G >= 32 ? 2 : 4);
+        const uint64_t per_block = 4ull * NG * BPG;
+        a.nblocks = round_up_xcd((a.nbags + per_block - 1) / per_block);
+        hipLaunchKernelGGL((k_pool_group_per_bag<DT, G, W, BPG>), dim3(a.nblocks), dim3(256), 0,
+                           stream, a);
+    }
+}
+
+template <int DT, bool W>
+void dispatch_g(const PoolArgs &a, uint32_t chunks, bool wave_per_bag, hipStream_t stream) {
+    switch (chunks) {
+        case 4: launch_pool<DT, 4, W>(a, wave_per_bag, stream); break;
+        case 8: launch_pool<DT, 8, W>(a, wave_per_bag, stream); break;
+        case 16: launch_pool<DT, 16, W>(a, wave_per_bag, stream); break;
+        case 32: launch_pool<DT, 32, W>(a, wave_per_bag, stream); break;
+        case 64: launch_pool<DT, 64, W>(a, wave_per_bag, stream); break;
+        default: {
+            const uint64_t threads = static_cast<uint64_t>(a.nbags) * chunks;
+            hipLaunchKernelGGL((k_pool_generic<DT, W>), dim3((threads + 255) / 256), dim3(256), 0,
+                               stream, a, chunks);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                           int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                           const float *per_sample_weights, int64_t B, int64_t nnz, float *out,
+                           uint32_t flags, dlrm_stream_t stream_) {
+    using namespace dlrm;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc = check_batch(tables, rows, T, D, dtype, indices, offsets, per_sample_weights, B, nnz);
+    if (rc != DLRM_OK) return rc;
+    if (B > 0 && (!out || !aligned(out, 16))) return DLRM_ERR_INVALID_ARG;
+    if (flags & ~DLRM_FLAG_CHECK_INDICES) return DLRM_ERR_INVALID_ARG;
+    if (B == 0) {
+        if (nnz != 0) return DLRM_ERR_INVALID_ARG;
+        return DLRM_OK;
+    }
+    if (flags & DLRM_FLAG_CHECK_INDICES) {
+        // the output buffer lends 4 bytes for the flag; it is overwritten below
+        rc = check_csr_on_device(rows, T, indices, offsets, B, nnz, reinterpret_cast<int *>(out),
+                                 stream);
+        if (rc != DLRM_OK) return rc;
+    }
+    PoolArgs a{};
+    for (int t = 0; t < T; ++t) a.tables[t] = static_cast<const char *>(tables[t]);
+    a.indices = indices;
+    a.offsets = offsets;
+    a.weights = per_sample_weights;
+    a.out = out;
+    a.B = static_cast<uint32_t>(B);
+    a.nbags = static_cast<uint32_t>(T * B);
+    a.T = T;
+    a.D = D;
+    a.row_bytes = static_cast<uint32_t>(D * elem_size(dtype));
+    const uint32_t chunks = a.row_bytes / 16;
+    // multi-hot bags (4+ rows on average) get a whole wavefront each
+    const bool wave_per_bag = nnz >= 4 * static_cast<int64_t>(a.nbags);
+    const bool weighted = per_sample_weights != nullptr;
+    if (dtype == DLRM_F32) {
+        if (weighted) dispatch_g<DLRM_F32, true>(a, chunks, wave_per_bag, stream);
+        else dispatch_g<DLRM_F32, false>(a, chunks, wave_per_bag, stream);
+    } else {
+        if (weighted) dispatch_g<DLRM_BF16, true>(a, chunks, wave_per_bag, stream);
+        else dispatch_g<DLRM_BF16, false>(a, chunks, wave_per_bag, stream);
+    }
+    return launch_status();
+}

@@ -1,0 +1,300 @@
+// Dot-product feature interaction, forward and backward (robocikowo.com "DLRM", paragraph
+// "Forward pass", stages (3)-(4), and its paragraph on the interaction layer;
+// notes.helloworld.co.in "Deep Learning Recommendation Model (DLRM)", "The architecture").
+//
+// Per sample, X is N x D (row 0 the dense vector, rows 1..N-1 the pooled embeddings).
+// Forward: the strict upper triangle of X X^T, row by row, then the dense vector.
+// Backward: dX = G X with G the symmetric matrix of the upstream triu gradients.
+//
+// Forward on gfx950: the per-sample Gram X X^T is a dense contraction, so it runs on the matrix
+// cores: v_mfma_f32_16x16x4_f32 (full fp32) over 16-row blocks of X, computing only the
+// blocks on or above the diagonal.  Each lane loads its A/B operands straight from global
+// memory with 16-byte loads (the k order inside a chunk is permuted identically for both
+// operands, which leaves every dot product's set of terms unchanged), so no LDS is needed and
+// one wavefront handles one sample.  A plain-VALU kernel serves shapes the MFMA tiling does not
+// cover (D not a multiple of 16).
+//
+// Backward: one wavefront per (sample, 128-column slice); the lane owns one or two columns d of
+// X in registers, G sits in LDS and is read with broadcast loads, and dX[i][d] = sum_j G[i][j]
+// X[j][d] is a register FMA chain.  Reads X once and writes dX once: HBM-bound.
+#include "common.h"
+
+namespace dlrm {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int triu_pos(int i, int j, int N) {  // i < j
+    return i * N - (i * (i + 1)) / 2 + (j - i - 1);
+}
+
+__device__ __forceinline__ const float *x_row(const float *dense, const float *pooled, uint32_t b,
+                                              int N, int D, int i) {
+    return i == 0 ? dense + static_cast<uint64_t>(b) * D
+                  : pooled + (static_cast<uint64_t>(b) * (N - 1) + (i - 1)) * D;
+}
+
+// NB = ceil(N/16) row blocks; KC = k-chunk width (16 or 32); NCH = D / KC chunks; CHG = chunks
+// whose operands are loaded together.
+template <int NB, int KC, int NCH, int CHG>
+__global__ __launch_bounds__(256) void k_interact_fwd_mfma(const float *__restrict__ dense,
+                                                           const float *__restrict__ pooled,
+                                                           float *__restrict__ out, uint32_t B,
+                                                           int N, int P) {
+    constexpr int D = KC * NCH;
+    constexpr int PL = KC / 4;  // floats per lane per chunk
+    constexpr int NBLK = NB * (NB + 1) / 2;
+    const uint32_t sample = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (sample >= B) return;
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, q = lane >> 4;
+
+    const float *rowp[NB];
+    bool rv[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) {
+        const int i = R * 16 + r16;
+        rv[R] = i < N;
+        rowp[R] = x_row(dense, pooled, sample, N, D, rv[R] ? i : 0) + q * PL;
+    }
+    floatx4 acc[NBLK];
+#pragma unroll
+    for (int k = 0; k < NBLK; ++k) acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += CHG) {
+        float x[NB][CHG][PL];
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int c = 0; c < CHG; ++c)
+#pragma unroll
+                for (int v = 0; v < PL; v += 4) {
+                    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (rv[R]) f = *reinterpret_cast<const float4 *>(rowp[R] + (c0 + c) * KC + v);
+                    x[R][c][v] = f.x;
+                    x[R][c][v + 1] = f.y;
+                    x[R][c][v + 2] = f.z;
+                    x[R][c][v + 3] = f.w;
+                }
+#pragma unroll
+        for (int c = 0; c < CHG; ++c)
+#pragma unroll
+            for (int s = 0; s < PL; ++s) {
+                int k = 0;
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+#pragma unroll
+                    for (int J = I; J < NB; ++J, ++k)
+                        acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[I][c][s], x[J][c][s],
+                                                                      acc[k], 0, 0, 0);
+            }
+    }
+    // D[i][j] of block (I,J) sits in lane j + 16*(i/4), element i%4
+    float *orow = out + static_cast<uint64_t>(sample) * (P + D);
+    int k = 0;
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int J = I; J < NB; ++J, ++k)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int gi = I * 16 + q * 4 + v, gj = J * 16 + r16;
+                if (gi < gj && gj < N) orow[triu_pos(gi, gj, N)] = acc[k][v];
+            }
+    const float *dsrc = dense + static_cast<uint64_t>(sample) * D;
+    for (int d = lane; d < D; d += kWave) orow[P + d] = dsrc[d];
+}
+
+// Any D % 4 == 0: one block per sample, one thread per pair, fp32 FMA chain over d.
+__global__ __launch_bounds__(256) void k_interact_fwd_valu(const float *__restrict__ dense,
+                                                           const float *__restrict__ pooled,
+                                                           float *__restrict__ out, int N, int D,
+                                                           int P) {
+    const uint32_t sample = blockIdx.x;
+    float *orow = out + static_cast<uint64_t>(sample) * (P + D);
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        // invert the row-major triu position
+        int i = 0, rem = p;
+        while (rem >= N - 1 - i) {
+            rem -= N - 1 - i;
+            ++i;
+        }
+        const int j = i + 1 + rem;
+        const float *xi = x_row(dense, pooled, sample, N, D, i);
+        const float *xj = x_row(dense, pooled, sample, N, D, j);
+        float z = 0.f;
+        for (int d = 0; d < D; d += 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(xi + d);
+            const float4 b = *reinterpret_cast<const float4 *>(xj + d);
+            z = fmaf(a.x, b.x, z);
+            z = fmaf(a.y, b.y, z);
+            z = fmaf(a.z, b.z, z);
+            z = fmaf(a.w, b.w, z);
+        }
+        orow[p] = z;
+    }
+    const float *dsrc = dense + static_cast<uint64_t>(sample) * D;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) orow[P + d] = dsrc[d];
+}
+
+// Backward.  NP = padded N (multiple of 4, >= N); CPL = columns per lane (1 or 2).
+template <int NP, int CPL>
+__global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ grad_out,
+                                                      const float *__restrict__ dense,
+                                                      const float *__restrict__ pooled,
+                                                      float *__restrict__ grad_dense,
+                                                      float *__restrict__ grad_pooled, uint32_t B,
+                                                      int N, int D, int P, int slices) {
+    __shared__ float Gs[4][NP][NP];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t gw = static_cast<uint64_t>(blockIdx.x) * 4 + wv;
+    const uint32_t sample = static_cast<uint32_t>(gw / slices);
+    const int slice = static_cast<int>(gw % slices);
+    const bool valid = sample < B;
+    const uint32_t sb = valid ? sample : 0;
+    const float *g = grad_out + static_cast<uint64_t>(sb) * (P + D);
+
+    // G: symmetric, zero diagonal, zero padding
+    for (int e = lane; e < NP * NP; e += kWave) {
+        const int i = e / NP, j = e % NP;
+        float v = 0.f;
+        if (valid && i < N && j < N && i != j) v = g[i < j ? triu_pos(i, j, N) : triu_pos(j, i, N)];
+        Gs[wv][i][j] = v;
+    }
+    __syncthreads();
+
+    const int d0 = slice * (kWave * CPL) + lane * CPL;
+    const bool dv = valid && d0 < D;
+    float x[NP][CPL];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        if (dv && j < N) {
+            const float *src = x_row(dense, pooled, sb, N, D, j) + d0;
+            if constexpr (CPL == 2) {
+                const float2 f = *reinterpret_cast<const float2 *>(src);
+                x[j][0] = f.x;
+                x[j][1] = f.y;
+            } else {
+                x[j][0] = src[0];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) x[j][c] = 0.f;
+        }
+    }
+    if (!dv) return;
+    for (int i = 0; i < N; ++i) {
+        float acc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NP; j += 4) {
+            const float4 gv = *reinterpret_cast<const float4 *>(&Gs[wv][i][j]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                acc[c] = fmaf(gv.x, x[j][c], acc[c]);
+                acc[c] = fmaf(gv.y, x[j + 1][c], acc[c]);
+                acc[c] = fmaf(gv.z, x[j + 2][c], acc[c]);
+                acc[c] = fmaf(gv.w, x[j + 3][c], acc[c]);
+            }
+        }
+        float *dst;
+        if (i == 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] += g[P + d0 + c];
+            dst = grad_dense + static_cast<uint64_t>(sb) * D + d0;
+        } else {
+            dst = grad_pooled + (static_cast<uint64_t>(sb) * (N - 1) + (i - 1)) * D + d0;
+        }
+        if constexpr (CPL == 2) *reinterpret_cast<float2 *>(dst) = make_float2(acc[0], acc[1]);
+        else dst[0] = acc[0];
+    }
+}
+
+template <int NB>
+bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32_t B, int N, int D,
+                     int P, hipStream_t stream) {
+    const dim3 grid((B + 3) / 4), block(256);
+    // operands of CHG chunks are loaded at once: NB*CHG*KC/4 registers, kept <= 64
+    switch (D) {
+        case 16: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 16, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 32: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 64: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 2, (NB <= 4 ? 2 : 1)>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 128: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 4, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 256: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 8, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 512: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 16, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        default: return false;
+    }
+}
+
+template <int NP>
+void launch_bwd(const float *g, const float *dense, const float *pooled, float *gd, float *gp,
+                uint32_t B, int N, int D, int P, hipStream_t stream) {
+    if (D >= 128) {
+        const int slices = (D + 127) / 128;
+        const uint64_t waves = static_cast<uint64_t>(B) * slices;
+        hipLaunchKernelGGL((k_interact_bwd<NP, 2>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
+                           dense, pooled, gd, gp, B, N, D, P, slices);
+    } else {
+        const int slices = (D + 63) / 64;
+        const uint64_t waves = static_cast<uint64_t>(B) * slices;
+        hipLaunchKernelGGL((k_interact_bwd<NP, 1>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
+                           dense, pooled, gd, gp, B, N, D, P, slices);
+    }
+}
+
+int check_interact(const void *a, const void *b, const void *c, int64_t B, int32_t N, int32_t D) {
+    if (B < 0 || N < 1 || N > kMaxTables + 1 || D < 1) return DLRM_ERR_INVALID_ARG;
+    if (D > 512 || D % 4 != 0) return DLRM_ERR_UNSUPPORTED;
+    if (B >= (int64_t(1) << 31) / 4) return DLRM_ERR_UNSUPPORTED;
+    if (B == 0) return DLRM_OK;
+    if (!a || !c || (N > 1 && !b)) return DLRM_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(c, 4) || (b && !aligned(b, 16))) return DLRM_ERR_INVALID_ARG;
+    return DLRM_OK;
+}
+
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_t B, int32_t N,
+                                 int32_t D, float *out, dlrm_stream_t stream_) {
+    using namespace dlrm;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc = check_interact(dense, pooled, out, B, N, D);
+    if (rc != DLRM_OK || B == 0) return rc;
+    const int P = N * (N - 1) / 2;
+    const uint32_t b = static_cast<uint32_t>(B);
+    bool done = false;
+    switch ((N + 15) / 16) {
+        case 1: done = launch_fwd_mfma<1>(dense, pooled, out, b, N, D, P, stream); break;
+        case 2: done = launch_fwd_mfma<2>(dense, pooled, out, b, N, D, P, stream); break;
+        case 3: done = launch_fwd_mfma<3>(dense, pooled, out, b, N, D, P, stream); break;
+        case 4: done = launch_fwd_mfma<4>(dense, pooled, out, b, N, D, P, stream); break;
+        case 5: done = launch_fwd_mfma<5>(dense, pooled, out, b, N, D, P, stream); break;
+    }
+    if (!done)
+        hipLaunchKernelGGL(k_interact_fwd_valu, dim3(b), dim3(256), 0, stream, dense, pooled, out,
+                           N, D, P);
+    return launch_status();
+}
+
+extern "C" int dlrm_interact_bwd(const float *grad_out, const float *dense, const float *pooled,
+                                 int64_t B, int32_t N, int32_t D, float *grad_dense,
+                                 float *grad_pooled, dlrm_stream_t stream_) {
+    using namespace dlrm;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    int rc = check_interact(dense, pooled, grad_dense, B, N, D);
+    if (rc != DLRM_OK || B == 0) return rc;
+    if (!grad_out || !aligned(grad_out, 4) || (N > 1 && (!grad_pooled || !aligned(grad_pooled, 16))))
+        return DLRM_ERR_INVALID_ARG;
+    if (!aligned(grad_dense, 16)) return DLRM_ERR_INVALID_ARG;
+    const int P = N * (N - 1) / 2;
+    const uint32_t b = static_cast<uint32_t>(B);
+    if (N <= 8) launch_bwd<8>(grad_out, dense, pooled, grad_dense, grad_pooled, b, N, D, P, stream);
+    else if (N <= 16) launch_bwd<16>(grad_out, dense, pooled, grad_dense, grad_pooled, b, N, D, P, stream);
+    else if (N <= 32) launch_bwd<32>(grad_out, dense, pooled, grad_dense, grad_pooled, b, N, D, P, stream);
+    else if (N <= 48) launch_bwd<48>(grad_out, dense, pooled, grad_dense, grad_pooled, b, N, D, P, stream);
+    else launch_bwd<68>(grad_out, dense, pooled, grad_dense, grad_pooled, b, N, D, P, stream);
+    return launch_status();
+}

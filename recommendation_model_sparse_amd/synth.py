@@ -300,27 +300,26 @@ class Batch:
         T, B = wl.T, wl.B
         lens = self.bag_lengths()
         new_len = np.empty(T * S, dtype=np.int64)
-        pieces, wpieces, row_ids = [], [], []
-        pos = []
+        pieces, wpieces, row_ids, new_rows = [], [], [], []
         for t in range(T):
             bags = t * B + samples
-            new_len[t * S:(t + 1) * S] = lens[bags]
-            sel = [np.arange(self.offsets[g], self.offsets[g + 1]) for g in bags]
-            sel = np.concatenate(sel) if sel else np.zeros(0, dtype=np.int64)
-            pos.append(sel)
-        offsets = np.zeros(T * S + 1, dtype=np.int64)
-        np.cumsum(new_len, out=offsets[1:])
-        new_rows = []
-        for t in range(T):
-            idx = self.indices[pos[t]]
+            L = lens[bags]
+            new_len[t * S:(t + 1) * S] = L
+            starts = self.offsets[bags]
+            # positions of the selected bags, in order: start of each bag + rank inside it
+            excl = np.cumsum(L) - L
+            pos = np.repeat(starts - excl, L) + np.arange(int(L.sum()), dtype=np.int64)
+            idx = self.indices[pos]
             uniq, inv = np.unique(idx, return_inverse=True)
             if len(uniq) == 0:
                 uniq = np.zeros(1, dtype=np.int64)
             row_ids.append(uniq)
             new_rows.append(int(len(uniq)))
-            pieces.append(inv.astype(np.int64))
+            pieces.append(inv.astype(np.int64).reshape(-1))
             if self.weights is not None:
-                wpieces.append(self.weights[pos[t]])
+                wpieces.append(self.weights[pos])
+        offsets = np.zeros(T * S + 1, dtype=np.int64)
+        np.cumsum(new_len, out=offsets[1:])
         indices = np.concatenate(pieces) if pieces else np.zeros(0, dtype=np.int64)
         weights = np.concatenate(wpieces) if self.weights is not None else None
         sub_wl = wl.with_(B=S, rows=new_rows, name=wl.name + "/subset")

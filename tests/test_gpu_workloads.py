@@ -1,0 +1,169 @@
+"""GPU parity on the five full-size workloads (needs an MI355X).
+
+The GPU runs each workload at its full size, in the launch configuration the
+benchmark times.  The oracle checks sampled batch rows one by one: the sampled
+bags are restricted to the table rows they touch (a monotone renumbering, so
+pooling, sort order and segments are unchanged), and those rows are
+regenerated on the host from the same counter hash the device fill wrote.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recommendation_model_sparse_amd import (
+    AdagradOutputs,
+    dlrm_interact_bwd,
+    dlrm_interact_fwd,
+    dlrm_synth_fill_table,
+    emb_bag_bwd_adagrad,
+    emb_bag_fwd,
+    synth,
+)
+from recommendation_model_sparse_amd.configs import make_config
+from recommendation_model_sparse_amd.synth import subset_tables
+
+from gpu_util import DEV, as_f64, device_tables, rel_err, row_inf_rel, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+POOL_TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_fill_matches_host_hash(dtype):
+    V, D, t = 5000, 128, 7
+    seed = synth.table_seed(123)
+    scale = synth.table_scale(V)
+    x = torch.empty((V, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
+    say(f"[fill] {dtype} V={V}")
+    dlrm_synth_fill_table(x, t, seed, float(scale))
+    rows = np.array([0, 1, 2, 777, V - 1])
+    got = to_host(x)[rows]
+    ref = synth.hash_rows(t, rows, D, seed, scale, dtype)
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
+def sample_rows(B, n, seed):
+    if B <= n:
+        return np.arange(B)
+    rng = np.random.default_rng(seed)
+    s = rng.choice(B, n, replace=False)
+    return np.unique(np.concatenate([s, [0, B - 1]]))
+
+
+def check_forward(wl, batch, tabs, n_samples=256):
+    say(f"[workload] {wl.name} B={wl.B} nnz={batch.nnz} table bytes={wl.table_bytes() / 1e9:.2f} GB "
+        f"weighted={batch.weights is not None}")
+    di, do = to_dev(batch.indices), to_dev(batch.offsets)
+    dw = None if batch.weights is None else to_dev(batch.weights)
+    dense = to_dev(batch.dense)
+    pooled = emb_bag_fwd(tabs, di, do, dw)
+    inter = dlrm_interact_fwd(dense, pooled)
+    torch.cuda.synchronize()
+    S = sample_rows(wl.B, n_samples, wl.seed)
+    sub_wl, sub, row_ids = batch.sample_subset(S)
+    host_tabs = subset_tables(wl, row_ids)
+    ref, scale = oracle.emb_bag_fwd(host_tabs, sub.indices, sub.offsets, sub.weights, len(S))
+    got = pooled[torch.from_numpy(S).to(DEV)].cpu().numpy()
+    err = rel_err(got, ref, scale)
+    say(f"   pooled max rel err {err:.3e} over {len(S)} samples")
+    assert err <= POOL_TOL[wl.dtype]
+    if wl.bags == "onehot":
+        assert np.array_equal(got, ref.astype(np.float32))
+    # interaction on the GPU's own pooled rows
+    iref, iscale = oracle.interact_fwd(batch.dense[S], got)
+    igot = inter[torch.from_numpy(S).to(DEV)].cpu().numpy()
+    ierr = rel_err(igot, iref, iscale)
+    say(f"   interaction max rel err {ierr:.3e}")
+    assert ierr <= 1e-5
+    return pooled, inter
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_workload_forward(k):
+    wl = make_config(k)
+    tabs = device_tables(wl)
+    check_forward(wl, wl.batch(0), tabs)
+    if k == 3:  # the weighted variant
+        check_forward(wl, wl.batch(1, weighted=True), tabs)
+    del tabs
+    torch.cuda.empty_cache()
+
+
+def test_workload_big_tables():
+    """One GPU's share of 8 x 50M-row bf16 tables (102.4 GB), uniform and Zipf(1.2) indices."""
+    wl = make_config(4)
+    tabs = device_tables(wl)
+    try:
+        check_forward(wl, wl.batch(0), tabs, n_samples=512)
+        check_forward(wl.with_(dist="zipf", alpha=1.2), wl.with_(dist="zipf", alpha=1.2).batch(0), tabs,
+                      n_samples=512)
+    finally:
+        del tabs
+        torch.cuda.empty_cache()
+
+
+def test_workload_training_step():
+    """Interaction backward + sort/unique/segment-reduce + row-wise Adagrad on the one-hot fp32 shapes."""
+    wl = make_config(5)
+    b = wl.batch(0)
+    tabs = device_tables(wl)
+    states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
+    say(f"[workload] {wl.name} training step B={wl.B} nnz={b.nnz}")
+    di, do = to_dev(b.indices), to_dev(b.offsets)
+    dense = to_dev(b.dense)
+    pooled = emb_bag_fwd(tabs, di, do)
+    dlrm_interact_fwd(dense, pooled)
+    g = to_dev(b.grad_out())
+    gd, gp = dlrm_interact_bwd(g, dense, pooled)
+    outs = AdagradOutputs(b.nnz, DEV)
+    emb_bag_bwd_adagrad(tabs, states, di, do, None, gp, wl.lr, wl.eps, outputs=outs)
+    torch.cuda.synchronize()
+
+    # interaction backward on sampled rows
+    S = sample_rows(wl.B, 256, 5)
+    pooled_h = pooled.cpu().numpy()
+    rd, rp, md, mp = oracle.interact_bwd(b.grad_out()[S], b.dense[S], pooled_h[S])
+    e1 = rel_err(gd.cpu().numpy()[S], rd, md)
+    e2 = rel_err(gp.cpu().numpy()[S], rp, mp)
+    say(f"   interact_bwd max rel err {e1:.3e} / {e2:.3e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5
+
+    # Adagrad on every lookup, over the touched rows only (monotone renumbering)
+    sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
+    host_tabs = subset_tables(wl, row_ids)
+    host_states = [np.zeros(len(r), np.float32) for r in row_ids]
+    r = oracle.emb_bag_bwd_adagrad(host_tabs, host_states, sub.indices, sub.offsets, None, wl.B,
+                                   gp.cpu().numpy(), wl.lr, wl.eps)
+    U = int(outs.num_unique.item())
+    assert U == r.U
+    assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
+    assert np.array_equal(outs.segment_offsets.cpu().numpy()[:U + 1], r.seg_offsets)
+    rowbase = np.zeros(wl.T + 1, dtype=np.int64)
+    np.cumsum(wl.rows, out=rowbase[1:])
+    tt, rr = r.table_and_row()
+    full_keys = rowbase[tt] + np.array([row_ids[t][x] for t, x in zip(tt, rr)], dtype=np.int64)
+    assert np.array_equal(outs.unique_keys.cpu().numpy()[:U], full_keys)
+    rng = np.random.default_rng(3)
+    worst = 0.0
+    for t in range(wl.T):
+        sel = tt == t
+        rows_t = row_ids[t][rr[sel]]
+        if len(rows_t):
+            got = tabs[t][torch.from_numpy(rows_t).to(DEV)].cpu().numpy().astype(np.float64)
+            e = row_inf_rel(got, r.new_rows[sel])
+            worst = max(worst, e)
+            assert e <= 1e-4
+            gs = states[t][torch.from_numpy(rows_t).to(DEV)].cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(gs - r.new_state[sel]) <= 1e-4 * np.abs(r.new_state[sel]))
+        # untouched rows: unchanged (bit-exact against the hash), state still zero
+        cand = rng.integers(0, wl.rows[t], 512)
+        cand = np.setdiff1d(cand, row_ids[t])
+        if len(cand):
+            got = tabs[t][torch.from_numpy(cand).to(DEV)].cpu().numpy()
+            assert np.array_equal(got.view(np.uint8), wl.table_rows(t, cand).view(np.uint8))
+            assert torch.all(states[t][torch.from_numpy(cand).to(DEV)] == 0)
+    say(f"   Adagrad U={U} worst row rel err {worst:.3e}")
+    del tabs, states
+    torch.cuda.empty_cache()
