@@ -62,6 +62,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-samples", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--dist", choices=["zipf", "uniform"], default="zipf",
+                    help="row distribution of the lookups (uniform: a cache-cold control)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
@@ -69,6 +73,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 3 copies of 1 GiB")
+        return
     from recommendation_model_sparse_amd import (AdagradOutputs, dlrm_interact_bwd, dlrm_interact_fwd,
                                                  dlrm_synth_fill_table, emb_bag_bwd_adagrad,
                                                  emb_bag_bwd_workspace_size, emb_bag_fwd, synth)
@@ -76,6 +88,8 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = make_config(3)
+    if args.dist == "uniform":
+        wl = wl.with_(dist="uniform")
     log(f"[bench] workload {wl.name}: {wl.note}")
     t0 = time.time()
     tabs = []
@@ -164,10 +178,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 tables, fp32 accumulation",
-        "data": "synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), Zipf(1.05) rows)",
+        "data": f"synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), {args.dist} rows)",
         "config": {"workload": "multi-hot bf16 training step: 26 tables, D=128, B=16384, "
-                               "bag length truncated-geometric [1,100] mean 20, Zipf(1.05), "
-                               "V log-uniform [1e3,1e7]",
+                               "bag length truncated-geometric [1,100] mean 20, "
+                               + ("Zipf(1.05)" if args.dist == "zipf" else "uniform") +
+                               " rows, V log-uniform [1e3,1e7]",
                    "global_batch": wl.B, "tables": wl.T, "D": wl.D, "nnz_avg": nnz_avg,
                    "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
         "gathered_GBps": gathered_gbps,

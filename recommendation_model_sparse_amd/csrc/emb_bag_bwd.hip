@@ -4,21 +4,24 @@
 // looked it up).
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
-//   K4  expand: key_j = rowbase[t] + idx_j, val_j = j, bag_of[j] (one block per 256 bags,
-//       offsets staged in LDS, binary search per position).
-//   K5  stable LSD radix sort of (key, position), 8-bit digits, ceil(bits(sum V - 1)/8) passes.
-//       Per pass: per-tile digit histograms, a per-digit scan across tiles, and a scatter that
-//       ranks each key inside its tile with wavefront ballots (stable: ties keep order).
+//   K4  expand: for lookup j of bag (t, b): key_j = rowbase[t] + idx_j, and the payloads
+//       pos_j = j, grow_j = b*T + t (the row of grad_pooled it reads) and, when weighted,
+//       w_j.  One block per 256 bags; bag offsets and bag rows staged in LDS.
+//   K5  stable LSD radix sort of the keys carrying the payloads, 8-bit digits,
+//       ceil(bits(sum V - 1)/8) passes.  Per pass: per-tile digit histograms, a per-digit
+//       scan across tiles, and a scatter that ranks each key inside its tile with wavefront
+//       ballots (stable: ties keep their order).
 //   K6  unique keys and segment offsets (flag = key differs from its predecessor; a scan of
 //       the flags), written only when the caller asks for them.
 //   K7  chunked segment reduction fused with the update.  The sorted sequence is cut into
-//       chunks of G positions; a lane group walks its chunk in order, summing
-//       w * grad_pooled[bag] rows (one lane per 1..8 columns).  A segment that lies inside
-//       one chunk is finished on the spot: row-wise Adagrad on the prefetched table row and
-//       state.  A segment that crosses chunk boundaries leaves one partial sum per chunk
-//       (slot A: the piece that began before the chunk, slot B: the piece that runs past it),
-//       and K7b, launched over chunks, finishes each such segment from the chunk where it
-//       starts by adding its partials in chunk order.  Every sum has a fixed order, so the
+//       chunks of G positions (G = D/W lanes, W = 4 fp32 columns per lane); a lane group walks
+//       its chunk in order with U gradient rows in flight, summing w * grad_pooled rows.  A
+//       segment inside one chunk is finished on the spot: row-wise Adagrad on the table row
+//       and state prefetched with the gradient rows.  A segment that crosses chunk boundaries
+//       leaves one partial sum per chunk (slot A: the piece that began in an earlier chunk,
+//       slot B: the piece that runs past the chunk), and K7b finishes each such segment with
+//       a whole wavefront: it finds the segment's last chunk by galloping search, adds the
+//       partials in chunk order and applies the update.  Every sum has a fixed order, so the
 //       update is bitwise reproducible; no atomics.
 #include "common.h"
 
@@ -33,46 +36,70 @@ namespace {
 constexpr int kSortItems = 16;
 constexpr int kSortTile = 256 * kSortItems;  // keys per sort / segment block
 
+// floor(n / d) for n < 2^31 by multiply-high (Granlund & Montgomery 1994; Hacker's Delight 10-9).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+    return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 // ---------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t keys_a, keys_b, vals_a, vals_b, bag_of, counts, totals, flag, seg_count, part_a, part_b,
-        total;
+    size_t keys[2], pos[2], grow[2], wgt[2], counts, totals, flag, seg_count, seg_offsets,
+        chunk_seg, part_a, part_b, total;
     uint32_t nblk;    // sort / segment tiles
-    uint32_t nchunk;  // K7 chunks
-    int G, W;
+    uint32_t nchunk;  // K7 chunks of CS sorted positions
+    int G, W, CS;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// lanes per row (G) and fp32 columns per lane (W) of the K7 kernels
 bool bwd_geometry(int32_t D, int *G, int *W) {
     if (D < 4 || D > 512 || (D & (D - 1)) != 0) return false;
-    *G = D >= 64 ? 64 : D;
-    *W = D / *G;
+    *W = D >= 512 ? 8 : 4;
+    *G = D / *W;
     return true;
 }
+
+// sorted positions per K7 chunk: G lanes times MP positions per lane (at most 64)
+inline int chunk_positions(int G) { return G * (G >= 16 ? 64 / G : 4); }
 
 Layout make_layout(int32_t D, int64_t nnz) {
     Layout L{};
     bwd_geometry(D, &L.G, &L.W);
+    L.CS = chunk_positions(L.G);
     const size_t n = static_cast<size_t>(nnz > 0 ? nnz : 1);
     L.nblk = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
-    L.nchunk = static_cast<uint32_t>((n + L.G - 1) / L.G);
+    L.nchunk = static_cast<uint32_t>((n + L.CS - 1) / L.CS);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
         off += align256(bytes);
         return at;
     };
-    L.keys_a = take(4 * n);
-    L.keys_b = take(4 * n);
-    L.vals_a = take(4 * n);
-    L.vals_b = take(4 * n);
-    L.bag_of = take(4 * n);
+    for (int i = 0; i < 2; ++i) {
+        L.keys[i] = take(4 * n);
+        L.pos[i] = take(4 * n);
+        L.grow[i] = take(4 * n);
+        L.wgt[i] = take(4 * n);
+    }
     L.counts = take(4 * 256 * static_cast<size_t>(L.nblk));
     L.totals = take(4 * 256);
     L.flag = take(4);
     L.seg_count = take(4 * static_cast<size_t>(L.nblk));
+    L.seg_offsets = take(8 * (n + 1));
+    L.chunk_seg = take(4 * static_cast<size_t>(L.nchunk));
     L.part_a = take(4 * static_cast<size_t>(L.nchunk) * D);
     L.part_b = take(4 * static_cast<size_t>(L.nchunk) * D);
     L.total = off;
@@ -115,18 +142,28 @@ struct ExpandArgs {
     uint32_t rowbase[kMaxTables];
     const int64_t *offsets;
     const int64_t *indices;
+    const float *weights;
     uint32_t *keys;
-    uint32_t *vals;
-    uint32_t *bag_of;
+    uint32_t *pos;
+    uint32_t *grow;
+    uint32_t *wgt;
     uint32_t B;
+    uint32_t T;
     uint32_t nbags;
 };
 
 __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
     __shared__ int64_t so[257];
+    __shared__ uint32_t s_grow[256], s_base[256];
     const uint32_t g0 = blockIdx.x * 256u;
     const int nb = static_cast<int>(min(256u, a.nbags - g0));
     for (int i = threadIdx.x; i <= nb; i += 256) so[i] = a.offsets[g0 + i];
+    if (static_cast<int>(threadIdx.x) < nb) {
+        const uint32_t bag = g0 + threadIdx.x;
+        const uint32_t t = bag / a.B, b = bag - t * a.B;
+        s_grow[threadIdx.x] = b * a.T + t;
+        s_base[threadIdx.x] = a.rowbase[t];
+    }
     __syncthreads();
     const int64_t p0 = so[0], p1 = so[nb];
     for (int64_t j = p0 + threadIdx.x; j < p1; j += 256) {
@@ -136,11 +173,10 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
             if (so[mid] <= j) lo = mid;
             else hi = mid;
         }
-        const uint32_t bag = g0 + lo;
-        const uint32_t t = bag / a.B;
-        a.keys[j] = a.rowbase[t] + static_cast<uint32_t>(a.indices[j]);
-        a.vals[j] = static_cast<uint32_t>(j);
-        a.bag_of[j] = bag;
+        a.keys[j] = s_base[lo] + static_cast<uint32_t>(a.indices[j]);
+        a.pos[j] = static_cast<uint32_t>(j);
+        a.grow[j] = s_grow[lo];
+        if (a.weights) a.wgt[j] = __float_as_uint(a.weights[j]);
     }
 }
 
@@ -156,7 +192,8 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const uint32_t k = base + i * 256 + threadIdx.x;
-        if (k < n) atomicAdd(&h[(keys[k] >> shift) & 255u], 1u);
+        const uint32_t key = keys[min(k, n - 1)];
+        if (k < n) atomicAdd(&h[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     counts[threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
@@ -180,11 +217,17 @@ __global__ __launch_bounds__(256) void k_radix_scan(uint32_t *__restrict__ count
     if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
-__global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t *__restrict__ kin,
-                                                       const uint32_t *__restrict__ vin,
-                                                       uint32_t *__restrict__ kout,
-                                                       uint32_t *__restrict__ vout, uint32_t n,
-                                                       int shift, const uint32_t *__restrict__ counts,
+struct SortIO {
+    const uint32_t *kin;
+    uint32_t *kout;
+    const uint32_t *pin[3];  // payload words in (position, grad row, weight)
+    uint32_t *pout[3];
+};
+
+// NP payload words travel with each key.
+template <int NP>
+__global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, int shift,
+                                                       const uint32_t *__restrict__ counts,
                                                        uint32_t nblk,
                                                        const uint32_t *__restrict__ totals) {
     __shared__ uint32_t dbase[256];
@@ -199,12 +242,13 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t *__restric
     }
     __syncthreads();
     const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + (tid & 63);
-    uint32_t key[kSortItems], val[kSortItems], loc[kSortItems];
+    uint32_t key[kSortItems], loc[kSortItems], pay[NP][kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
-        const uint32_t k = base + i * kWave;
-        key[i] = k < n ? kin[k] : 0u;
-        val[i] = k < n ? vin[k] : 0u;
+        const uint32_t k = min(base + i * kWave, n - 1);  // unconditional loads
+        key[i] = io.kin[k];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) pay[q][i] = io.pin[q][k];
     }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
@@ -236,11 +280,13 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t *__restric
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
-        if (base + i * kWave < n) {
+        const uint32_t k = base + i * kWave;
+        if (k < n) {
             const uint32_t d = (key[i] >> shift) & 255u;
-            const uint32_t pos = wcnt[w][d] + loc[i];
-            kout[pos] = key[i];
-            vout[pos] = val[i];
+            const uint32_t p = wcnt[w][d] + loc[i];
+            io.kout[p] = key[i];
+#pragma unroll
+            for (int q = 0; q < NP; ++q) io.pout[q][p] = pay[q][i];
         }
     }
 }
@@ -279,17 +325,20 @@ __global__ __launch_bounds__(256) void k_seg_scan(uint32_t *__restrict__ bcount,
     }
     if (threadIdx.x == 0) {
         if (num_unique) *num_unique = tot;
-        if (seg_offsets) seg_offsets[tot] = n;
+        seg_offsets[tot] = n;
     }
 }
 
+// Writes segment offsets (and unique keys when asked), and for every chunk of CS sorted
+// positions the segment index of the chunk's last position.
 __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ keys, uint32_t n,
                                                    const uint32_t *__restrict__ bbase,
                                                    int64_t *__restrict__ unique_keys,
-                                                   int64_t *__restrict__ seg_offsets) {
+                                                   int64_t *__restrict__ seg_offsets,
+                                                   uint32_t *__restrict__ chunk_seg, uint32_t CS) {
     __shared__ uint32_t wtot[4];
-    const int tid = threadIdx.x, w = tid >> 6;
-    const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + (tid & 63);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + lane;
     uint64_t masks[kSortItems];
     uint32_t wsum = 0;
 #pragma unroll
@@ -297,7 +346,7 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
         masks[i] = __ballot(seg_flag(keys, base + i * kWave, n));
         wsum += __popcll(masks[i]);
     }
-    if ((tid & 63) == 0) wtot[w] = wsum;
+    if (lane == 0) wtot[w] = wsum;
     __syncthreads();
     uint32_t run = bbase[blockIdx.x];
     for (int k = 0; k < w; ++k) run += wtot[k];
@@ -305,11 +354,13 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const uint32_t k = base + i * kWave;
-        if ((masks[i] >> (tid & 63)) & 1ull) {
-            const uint32_t seg = run + __popcll(masks[i] & lt);
-            if (unique_keys) unique_keys[seg] = keys[k];
-            if (seg_offsets) seg_offsets[seg] = k;
+        const bool flag = (masks[i] >> lane) & 1ull;
+        const uint32_t seg_incl = run + __popcll(masks[i] & lt) + (flag ? 1u : 0u);  // flags in [0, k]
+        if (flag) {
+            if (unique_keys) unique_keys[seg_incl - 1] = keys[k];
+            seg_offsets[seg_incl - 1] = k;
         }
+        if (k < n && ((k + 1) % CS == 0 || k + 1 == n)) chunk_seg[k / CS] = seg_incl - 1;
         run += __popcll(masks[i]);
     }
 }
@@ -325,18 +376,19 @@ struct AdagradArgs {
     char *tables[kMaxTables];
     float *state[kMaxTables];
     uint32_t rowbase[kMaxTables];
-    const uint32_t *skeys;
-    const uint32_t *perm;
-    const uint32_t *bag_of;
-    const float *weights;
-    const float *grad;  // [B][T][D]
+    const uint32_t *skeys;        // sorted keys
+    const uint32_t *sgrow;        // grad_pooled row of each sorted position
+    const float *swgt;            // weight of each sorted position (weighted only)
+    const float *grad;            // [B][T][D]
+    const int64_t *seg_offsets;   // [U+1]
+    const uint32_t *chunk_seg;    // [nchunk]: segment of the chunk's last position
     float *part_a;
     float *part_b;
     uint32_t n;
     uint32_t nchunk;
-    uint32_t B;
     int32_t T;
     int32_t D;
+    FastDiv divT;
     float lr;
     float eps;
     float inv_D;
@@ -402,6 +454,21 @@ struct RowIO {
     }
 };
 
+struct TableLDS {
+    char *tab[kMaxTables];
+    float *state[kMaxTables];
+    uint32_t rowbase[kMaxTables];
+};
+
+__device__ __forceinline__ void stage_tables(const AdagradArgs &a, TableLDS &s) {
+    if (static_cast<int>(threadIdx.x) < a.T) {
+        s.tab[threadIdx.x] = a.tables[threadIdx.x];
+        s.state[threadIdx.x] = a.state[threadIdx.x];
+        s.rowbase[threadIdx.x] = a.rowbase[threadIdx.x];
+    }
+    __syncthreads();
+}
+
 template <int W>
 __device__ __forceinline__ void load_f32(const float *p, float *x) {
     RowIO<DLRM_F32, W>::load(reinterpret_cast<const char *>(p), x);
@@ -419,193 +486,301 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// Row-wise Adagrad on one row: s += mean(G^2); row -= lr * G / (sqrt(s) + eps).
+// Loads and stores through the global address space (pointers staged in LDS would otherwise be
+// generic/flat, and flat loads also count against the LDS wait counter).
+#define DLRM_GLOBAL __attribute__((address_space(1)))
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int WORDS>
+__device__ __forceinline__ void gload_words(const void *p, uint32_t *w) {
+    if constexpr (WORDS == 1) {
+        w[0] = *(const DLRM_GLOBAL uint32_t *)p;
+    } else if constexpr (WORDS == 2) {
+        const u32x2 v = *(const DLRM_GLOBAL u32x2 *)p;
+        w[0] = v.x, w[1] = v.y;
+    } else {
+        const DLRM_GLOBAL u32x4 *q = (const DLRM_GLOBAL u32x4 *)p;
+#pragma unroll
+        for (int i = 0; i < WORDS / 4; ++i) {
+            const u32x4 v = q[i];
+            w[4 * i] = v.x, w[4 * i + 1] = v.y, w[4 * i + 2] = v.z, w[4 * i + 3] = v.w;
+        }
+    }
+}
+
+template <int WORDS>
+__device__ __forceinline__ void gstore_words(void *p, const uint32_t *w) {
+    if constexpr (WORDS == 1) {
+        *(DLRM_GLOBAL uint32_t *)p = w[0];
+    } else if constexpr (WORDS == 2) {
+        *(DLRM_GLOBAL u32x2 *)p = u32x2{w[0], w[1]};
+    } else {
+        DLRM_GLOBAL u32x4 *q = (DLRM_GLOBAL u32x4 *)p;
+#pragma unroll
+        for (int i = 0; i < WORDS / 4; ++i) q[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    }
+}
+
+// W table elements as 32-bit words: fp32 one per word, bf16 two per word.
+template <int DT, int W>
+struct TabWords {
+    static constexpr int N = DT == DLRM_BF16 ? W / 2 : W;
+    static __device__ __forceinline__ void to_f32(const uint32_t *w, float *x) {
+        if constexpr (DT == DLRM_F32) {
+#pragma unroll
+            for (int e = 0; e < W; ++e) x[e] = __uint_as_float(w[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < W / 2; ++e) x[2 * e] = bf16_lo(w[e]), x[2 * e + 1] = bf16_hi(w[e]);
+        }
+    }
+    static __device__ __forceinline__ void from_f32(const float *x, uint32_t *w) {
+        if constexpr (DT == DLRM_F32) {
+#pragma unroll
+            for (int e = 0; e < W; ++e) w[e] = __float_as_uint(x[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < W / 2; ++e) w[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
+        }
+    }
+};
+
+// Row-wise Adagrad on one row (the lane's W columns): s += mean(G^2); row -= lr*G/(sqrt(s)+eps).
+// `row` points at the lane's first column of the row, `old` holds those columns as stored.
 template <int DT, int W, int G>
-__device__ __forceinline__ void adagrad_row(const AdagradArgs &a, uint32_t t, uint32_t r, int c,
-                                            const float *g, const float *old_row, float old_state) {
+__device__ __forceinline__ void adagrad_row(const AdagradArgs &a, char *row, float *state, int c,
+                                            const float *g, const uint32_t *old, float old_state) {
+    using TW = TabWords<DT, W>;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < W; ++e) ss = fmaf(g[e], g[e], ss);
     ss = group_sum<G>(ss);
     const float s_new = old_state + ss * a.inv_D;
-    const float den = sqrtf(s_new) + a.eps;
-    float nw[W];
+    const float step = a.lr / (sqrtf(s_new) + a.eps);
+    float x[W];
+    TW::to_f32(old, x);
 #pragma unroll
-    for (int e = 0; e < W; ++e) nw[e] = old_row[e] - a.lr * g[e] / den;
-    constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
-    RowIO<DT, W>::store(a.tables[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES, nw);
-    if (c == 0) a.state[t][r] = s_new;
+    for (int e = 0; e < W; ++e) x[e] = fmaf(-step, g[e], x[e]);
+    uint32_t nw[TW::N];
+    TW::from_f32(x, nw);
+    gstore_words<TW::N>(row, nw);
+    if (c == 0) *(DLRM_GLOBAL float *)state = s_new;
 }
 
-template <int DT, int W, int G, bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
-    constexpr int NG = kWave / G;
-    constexpr int U = 8;
-    constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
-    const int lane = threadIdx.x & 63, grp = lane / G, c = lane % G, gbase = grp * G;
-    const uint32_t chunk = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NG + grp;
-    if (chunk >= a.nchunk) return;  // group-uniform
-    const uint32_t lo = chunk * G, hi = min(lo + G, a.n), cnt = hi - lo;
+// Per sorted position, staged in LDS by the lane that owns it and read back as broadcasts.
+struct PosMeta {
+    const float *grad_row;  // grad_pooled row of the position
+    char *tab_row;          // table row it updates (only where a segment starts)
+    float *state;           // that row's accumulator (only where a segment starts)
+    float w;
+    uint32_t pad;
+};
 
-    // per-position metadata, one position per lane of the group
-    const uint32_t k = lo + c;
-    const bool have = k < hi;
-    const uint32_t mykey = have ? a.skeys[k] : 0u;
-    const uint32_t j = have ? a.perm[k] : 0u;
-    const uint32_t mybag = have ? a.bag_of[j] : 0u;
-    const float myw = (WEIGHTED && have) ? a.weights[j] : 1.f;
-    const uint32_t key_lo = a.skeys[lo];
-    bool open_before = lo > 0 && a.skeys[lo - 1] == key_lo;  // first piece began in an earlier chunk
+// Chunk of CS = G*MP sorted positions per lane group of G lanes; U gradient rows in flight.
+template <int DT, int W, int G, int MP, bool WEIGHTED, int U>
+__global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
+    using TW = TabWords<DT, W>;
+    constexpr int NG = kWave / G;
+    constexpr int CS = G * MP;
+    constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
+    static_assert(CS <= 64, "start flags live in one 64-bit mask");
+    __shared__ PosMeta meta[4][NG][CS];
+    __shared__ TableLDS sl;
+    stage_tables(a, sl);
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane / G, c = lane % G;
+    const uint32_t chunk = (blockIdx.x * 4 + wv) * NG + grp;
+    if (chunk >= a.nchunk) return;  // group-uniform
+    const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n), cnt = hi - lo;
+    PosMeta *pm = meta[wv][grp];
+
+    // build the chunk's metadata: lane c owns positions lo + c + m*G
+    uint64_t starts = 0;  // bit r: position lo + r opens a segment
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+        const uint32_t r = c + m * G, k = lo + r;
+        const bool have = k < hi;
+        const uint32_t kk = have ? k : hi - 1;  // loads stay unconditional
+        const uint32_t key = a.skeys[kk];
+        const uint32_t prev = a.skeys[kk > 0 ? kk - 1 : 0];
+        const uint32_t grow = a.sgrow[kk];
+        const float w = WEIGHTED ? a.swgt[kk] : 1.f;
+        const bool st = have && (kk == 0 || key != prev);
+        const uint32_t t = grow - fast_div(grow, a.divT) * a.divT.d;
+        const uint32_t row = key - sl.rowbase[t];
+        PosMeta p;
+        p.grad_row = a.grad + static_cast<uint64_t>(grow) * a.D;
+        p.tab_row = sl.tab[t] + static_cast<uint64_t>(row) * a.D * ES;
+        p.state = sl.state[t] + row;
+        p.w = w;
+        p.pad = 0;
+        if (have) pm[r] = p;
+        const uint64_t bal = __ballot(st);
+        starts |= ((bal >> (grp * G)) & (G == 64 ? ~0ull : ((1ull << G) - 1))) << (m * G);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    bool open_before = !(starts & 1ull);  // the first piece began in an earlier chunk
     const bool runs_past = hi < a.n && a.skeys[hi] == a.skeys[hi - 1];
 
     float acc[W];
 #pragma unroll
     for (int e = 0; e < W; ++e) acc[e] = 0.f;
-    uint32_t cur = key_lo, cur_t = 0, cur_r = 0;
-    float cur_row[W], cur_state = 0.f;
+    char *cur_row_ptr = nullptr;
+    float *cur_state = nullptr;
+    uint32_t cur_row[TW::N];
+    float cur_s = 0.f;
 #pragma unroll
-    for (int e = 0; e < W; ++e) cur_row[e] = 0.f;
+    for (int e = 0; e < TW::N; ++e) cur_row[e] = 0u;
 
     for (uint32_t r0 = 0; r0 < cnt; r0 += U) {
-        float gr[U][W], tr[U][W], st[U], wu[U];
-        uint32_t key[U], tt[U], rr[U];
-        bool starts[U];
+        // Every load below is unconditional (positions past the chunk re-read its last one,
+        // positions that open no segment re-read their own gradient row in place of a table
+        // row), so no branch separates the loads and all of them are in flight together.
+        PosMeta mu[U];
+        uint32_t gr[U][W], tr[U][TW::N];
+        float st[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mu[u] = pm[min(r0 + u, cnt - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) gload_words<W>(mu[u].grad_row + c * W, gr[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool s_u = (starts >> (r0 + u)) & 1ull;  // bits past cnt are 0
+            const void *tp = s_u ? static_cast<const void *>(mu[u].tab_row + c * W * ES)
+                                 : static_cast<const void *>(mu[u].grad_row + c * W);
+            const void *sp = s_u ? static_cast<const void *>(mu[u].state)
+                                 : static_cast<const void *>(mu[u].grad_row);
+            gload_words<TW::N>(tp, tr[u]);
+            st[u] = *(const DLRM_GLOBAL float *)sp;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t r = r0 + u;
-            const bool ok = r < cnt;
-            const int src = gbase + (ok ? static_cast<int>(r) : 0);
-            key[u] = __shfl(mykey, src);
-            const uint32_t bag = __shfl(mybag, src);
-            wu[u] = WEIGHTED ? __shfl(myw, src) : 1.f;
-            // does position lo + r open a new segment?  (the first one may continue one)
-            const uint32_t prev = __shfl(mykey, gbase + (r > 0 && ok ? static_cast<int>(r) - 1 : 0));
-            starts[u] = ok && (r == 0 ? !open_before : key[u] != prev);
-            tt[u] = bag / a.B;
-            const uint32_t b = bag - tt[u] * a.B;
-            rr[u] = key[u] - a.rowbase[tt[u]];
-            if (ok) load_f32<W>(a.grad + (static_cast<uint64_t>(b) * a.T + tt[u]) * a.D + c * W, gr[u]);
-            else {
-#pragma unroll
-                for (int e = 0; e < W; ++e) gr[u][e] = 0.f;
-            }
-            if (starts[u]) {
-                RowIO<DT, W>::load(a.tables[tt[u]] + (static_cast<uint64_t>(rr[u]) * a.D + c * W) * ES,
-                                   tr[u]);
-                st[u] = a.state[tt[u]][rr[u]];
-            } else {
-#pragma unroll
-                for (int e = 0; e < W; ++e) tr[u][e] = 0.f;
-                st[u] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (r0 + u >= cnt) break;
-            if (starts[u]) {
-                if (r0 + u > 0) {  // close the previous segment: it ended inside this chunk
+            if (r >= cnt) break;
+            if ((starts >> r) & 1ull) {
+                if (r > 0) {  // the previous piece ended inside this chunk
                     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-                    else adagrad_row<DT, W, G>(a, cur_t, cur_r, c, acc, cur_row, cur_state);
+                    else adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
                 }
                 open_before = false;
-                cur = key[u];
-                cur_t = tt[u];
-                cur_r = rr[u];
+                cur_row_ptr = mu[u].tab_row + c * W * ES;
+                cur_state = mu[u].state;
+                cur_s = st[u];
 #pragma unroll
-                for (int e = 0; e < W; ++e) {
-                    cur_row[e] = tr[u][e];
-                    acc[e] = 0.f;
-                }
-                cur_state = st[u];
+                for (int e = 0; e < TW::N; ++e) cur_row[e] = tr[u][e];
+#pragma unroll
+                for (int e = 0; e < W; ++e) acc[e] = 0.f;
             }
 #pragma unroll
-            for (int e = 0; e < W; ++e) acc[e] = WEIGHTED ? fmaf(wu[u], gr[u][e], acc[e]) : acc[e] + gr[u][e];
+            for (int e = 0; e < W; ++e) {
+                const float g = __uint_as_float(gr[u][e]);
+                acc[e] = WEIGHTED ? fmaf(mu[u].w, g, acc[e]) : acc[e] + g;
+            }
         }
     }
     // the last piece of the chunk
-    (void)cur;
     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
     else if (runs_past) store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    else adagrad_row<DT, W, G>(a, cur_t, cur_r, c, acc, cur_row, cur_state);
+    else adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
 }
 
-// Finishes the segments that cross chunk boundaries, each from the chunk where it starts.
-template <int DT, int W, int G>
+// One block per chunk: finishes the segment that starts in this chunk and runs past it,
+// adding its partials in chunk order (slot B here, slot A of every later chunk it covers).
+template <int DT, int W, int G, int CS>
 __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
-    constexpr int NG = kWave / G;
+    constexpr int NS = 256 / G;  // partial rows read per pass of the block
+    constexpr int U = 4;
     constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
-    constexpr int BATCH = 16;
-    const int lane = threadIdx.x & 63, grp = lane / G, c = lane % G;
-    const uint32_t chunk = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NG + grp;
-    if (chunk >= a.nchunk) return;
-    const uint32_t lo = chunk * G, hi = min(lo + G, a.n);
-    if (hi >= a.n) return;
-    const uint32_t K = a.skeys[hi - 1];
-    if (a.skeys[hi] != K) return;  // the last segment of this chunk ends here
-    // does that segment start inside this chunk?
-    if (a.skeys[lo] == K && lo > 0 && a.skeys[lo - 1] == K) return;
-    // its piece in this chunk is in slot B (also when it starts exactly at lo)
+    __shared__ float red[NS][G * W];
+    __shared__ TableLDS sl;
+    stage_tables(a, sl);
+    const int sub = threadIdx.x / G, c = threadIdx.x % G;
+    const uint32_t chunk = blockIdx.x;
+    const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n);
+    if (hi >= a.n) return;  // block-uniform exits (no barrier after them)
+    if (a.skeys[hi] != a.skeys[hi - 1]) return;  // nothing runs past this chunk
+    const uint32_t u = a.chunk_seg[chunk];
+    const int64_t s = a.seg_offsets[u], e = a.seg_offsets[u + 1];
+    if (s < lo) return;  // it started in an earlier chunk
+    const uint32_t ce = static_cast<uint32_t>((e - 1) / CS);  // last chunk it covers
     float acc[W];
-    load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    // add slot A of the following chunks while the segment continues into them
-    for (uint32_t c1 = chunk + 1;; c1 += BATCH) {
-        bool in[BATCH];
-        float pa[BATCH][W];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const uint64_t pos = static_cast<uint64_t>(c1 + i) * G;
-            in[i] = pos < a.n && a.skeys[pos] == K;
-            if (in[i]) load_f32<W>(a.part_a + static_cast<uint64_t>(c1 + i) * a.D + c * W, pa[i]);
-        }
-        bool more = true;
+    for (int q = 0; q < W; ++q) acc[q] = 0.f;
+    if (sub == 0) load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+    for (uint32_t c1 = chunk + 1 + sub; c1 <= ce; c1 += NS * U) {
+        uint32_t pa[U][W];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            if (!in[i]) {
-                more = false;
-                break;
-            }
+        for (int k = 0; k < U; ++k)  // unconditional loads (clamped), all in flight together
+            gload_words<W>(a.part_a + static_cast<uint64_t>(min(c1 + k * NS, ce)) * a.D + c * W, pa[k]);
 #pragma unroll
-            for (int e = 0; e < W; ++e) acc[e] += pa[i][e];
-        }
-        if (!more) break;
+        for (int k = 0; k < U; ++k)
+            if (c1 + k * NS <= ce)
+#pragma unroll
+                for (int q = 0; q < W; ++q) acc[q] += __uint_as_float(pa[k][q]);
     }
-    // table and row of K
-    const uint32_t bag = a.bag_of[a.perm[hi - 1]];
-    const uint32_t t = bag / a.B;
-    const uint32_t r = K - a.rowbase[t];
-    float row[W];
-    RowIO<DT, W>::load(a.tables[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES, row);
-    adagrad_row<DT, W, G>(a, t, r, c, acc, row, a.state[t][r]);
+    // combine the NS row slots in a fixed order
+#pragma unroll
+    for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+        float x = red[0][c * W + q];
+        for (int k = 1; k < NS; ++k) x += red[k][c * W + q];
+        acc[q] = x;
+    }
+    const uint32_t K = a.skeys[hi - 1];
+    const uint32_t grow = a.sgrow[hi - 1];
+    const uint32_t t = grow - fast_div(grow, a.divT) * a.divT.d;
+    const uint32_t r = K - sl.rowbase[t];
+    char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
+    uint32_t old[TabWords<DT, W>::N];
+    gload_words<TabWords<DT, W>::N>(row, old);
+    adagrad_row<DT, W, G>(a, row, sl.state[t] + r, c, acc, old, *(const DLRM_GLOBAL float *)(sl.state[t] + r));
 }
+
+template <int G>
+constexpr int chunk_mp() { return G >= 16 ? 64 / G : 4; }
 
 template <int DT, int W, int G>
 void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
     constexpr int NG = kWave / G;
+    constexpr int MP = chunk_mp<G>();
+    constexpr int U = 8;
     const uint32_t blocks = (a.nchunk + 4 * NG - 1) / (4 * NG);
     if (weighted)
-        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, true>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, false>), dim3(blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_seg_finish<DT, W, G>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, false, U>), dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_seg_finish<DT, W, G, G * MP>), dim3(a.nchunk), dim3(256), 0, stream, a);
 }
 
 template <int DT>
 void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t stream) {
-    if (G == 64) {
-        switch (W) {
-            case 1: launch_k7<DT, 1, 64>(a, weighted, stream); break;
-            case 2: launch_k7<DT, 2, 64>(a, weighted, stream); break;
-            case 4: launch_k7<DT, 4, 64>(a, weighted, stream); break;
-            case 8: launch_k7<DT, 8, 64>(a, weighted, stream); break;
-        }
-    } else {
-        switch (G) {
-            case 4: launch_k7<DT, 1, 4>(a, weighted, stream); break;
-            case 8: launch_k7<DT, 1, 8>(a, weighted, stream); break;
-            case 16: launch_k7<DT, 1, 16>(a, weighted, stream); break;
-            case 32: launch_k7<DT, 1, 32>(a, weighted, stream); break;
-        }
+    if (W == 8) {
+        launch_k7<DT, 8, 64>(a, weighted, stream);
+        return;
     }
+    switch (G) {
+        case 1: launch_k7<DT, 4, 1>(a, weighted, stream); break;
+        case 2: launch_k7<DT, 4, 2>(a, weighted, stream); break;
+        case 4: launch_k7<DT, 4, 4>(a, weighted, stream); break;
+        case 8: launch_k7<DT, 4, 8>(a, weighted, stream); break;
+        case 16: launch_k7<DT, 4, 16>(a, weighted, stream); break;
+        case 32: launch_k7<DT, 4, 32>(a, weighted, stream); break;
+        case 64: launch_k7<DT, 4, 64>(a, weighted, stream); break;
+    }
+}
+
+template <int NP>
+void launch_scatter(const SortIO &io, uint32_t n, int shift, const uint32_t *counts, uint32_t nblk,
+                    const uint32_t *totals, hipStream_t stream) {
+    hipLaunchKernelGGL(k_radix_scatter<NP>, dim3(nblk), dim3(256), 0, stream, io, n, shift, counts,
+                       nblk, totals);
 }
 
 }  // namespace
@@ -647,6 +822,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     const Layout L = make_layout(D, nnz);
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)) return DLRM_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
+    auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
 
     if (flags & DLRM_FLAG_CHECK_INDICES) {
         rc = check_csr_on_device(rows, T, indices, offsets, B, nnz,
@@ -661,14 +837,8 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
         return launch_status();
     }
     const uint32_t n = static_cast<uint32_t>(nnz);
-    uint32_t *keys_a = reinterpret_cast<uint32_t *>(ws + L.keys_a);
-    uint32_t *keys_b = reinterpret_cast<uint32_t *>(ws + L.keys_b);
-    uint32_t *vals_a = reinterpret_cast<uint32_t *>(ws + L.vals_a);
-    uint32_t *vals_b = reinterpret_cast<uint32_t *>(ws + L.vals_b);
-    uint32_t *bag_of = reinterpret_cast<uint32_t *>(ws + L.bag_of);
-    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + L.counts);
-    uint32_t *totals = reinterpret_cast<uint32_t *>(ws + L.totals);
-    uint32_t *seg_count = reinterpret_cast<uint32_t *>(ws + L.seg_count);
+    const bool weighted = per_sample_weights != nullptr;
+    const int NP = weighted ? 3 : 2;  // payloads: position, grad row, (weight)
 
     // K4
     ExpandArgs ea{};
@@ -679,10 +849,13 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     }
     ea.offsets = offsets;
     ea.indices = indices;
-    ea.keys = keys_a;
-    ea.vals = vals_a;
-    ea.bag_of = bag_of;
+    ea.weights = per_sample_weights;
+    ea.keys = u32(L.keys[0]);
+    ea.pos = u32(L.pos[0]);
+    ea.grow = u32(L.grow[0]);
+    ea.wgt = u32(L.wgt[0]);
     ea.B = static_cast<uint32_t>(B);
+    ea.T = static_cast<uint32_t>(T);
     ea.nbags = static_cast<uint32_t>(T * B);
     hipLaunchKernelGGL(k_expand, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
@@ -690,37 +863,42 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     int bits = 0;
     while (bits < 32 && ((sumV - 1) >> bits) != 0) ++bits;
     const int passes = (bits + 7) / 8;
-    uint32_t *kin = keys_a, *vin = vals_a, *kout = keys_b, *vout = vals_b;
+    int cur = 0;
+    uint32_t *counts = u32(L.counts), *totals = u32(L.totals);
     for (int p = 0; p < passes; ++p) {
         const bool last = p + 1 == passes;
-        uint32_t *vdst = (last && sorted_pos_out) ? reinterpret_cast<uint32_t *>(sorted_pos_out) : vout;
-        hipLaunchKernelGGL(k_radix_hist, dim3(L.nblk), dim3(256), 0, stream, kin, n, 8 * p, counts, L.nblk);
+        SortIO io{};
+        io.kin = u32(L.keys[cur]);
+        io.kout = u32(L.keys[cur ^ 1]);
+        io.pin[0] = u32(L.pos[cur]);
+        io.pout[0] = (last && sorted_pos_out) ? reinterpret_cast<uint32_t *>(sorted_pos_out) : u32(L.pos[cur ^ 1]);
+        io.pin[1] = u32(L.grow[cur]);
+        io.pout[1] = u32(L.grow[cur ^ 1]);
+        io.pin[2] = u32(L.wgt[cur]);
+        io.pout[2] = u32(L.wgt[cur ^ 1]);
+        hipLaunchKernelGGL(k_radix_hist, dim3(L.nblk), dim3(256), 0, stream, io.kin, n, 8 * p, counts, L.nblk);
         hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(256), 0, stream, counts, L.nblk, totals);
-        hipLaunchKernelGGL(k_radix_scatter, dim3(L.nblk), dim3(256), 0, stream, kin, vin, kout, vdst,
-                           n, 8 * p, counts, L.nblk, totals);
-        kin = kout;
-        vin = vdst;
-        kout = (kout == keys_b) ? keys_a : keys_b;
-        vout = (vout == vals_b) ? vals_a : vals_b;
+        if (NP == 3) launch_scatter<3>(io, n, 8 * p, counts, L.nblk, totals, stream);
+        else launch_scatter<2>(io, n, 8 * p, counts, L.nblk, totals, stream);
+        cur ^= 1;
     }
-    const uint32_t *skeys = kin;
-    const uint32_t *perm = vin;
-    if (passes == 0 && sorted_pos_out) {
-        if (hipMemcpyAsync(sorted_pos_out, vals_a, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice,
-                           stream) != hipSuccess)
+    const uint32_t *skeys = u32(L.keys[cur]);
+    if (sorted_pos_out && passes == 0) {
+        if (hipMemcpyAsync(sorted_pos_out, u32(L.pos[0]), sizeof(uint32_t) * n,
+                           hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return DLRM_ERR_HIP;
-        perm = reinterpret_cast<const uint32_t *>(sorted_pos_out);
     }
 
-    // K6
-    if (want_seg) {
-        hipLaunchKernelGGL(k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
-        hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
-                           num_unique_out, segment_offsets_out);
-        if (unique_keys_out || segment_offsets_out)
-            hipLaunchKernelGGL(k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
-                               unique_keys_out, segment_offsets_out);
-    }
+    // K6 (always: K7's finisher reads the segment offsets)
+    uint32_t *seg_count = u32(L.seg_count);
+    int64_t *seg_offsets = segment_offsets_out ? segment_offsets_out
+                                               : reinterpret_cast<int64_t *>(ws + L.seg_offsets);
+    uint32_t *chunk_seg = u32(L.chunk_seg);
+    hipLaunchKernelGGL(k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
+    hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
+                       num_unique_out, seg_offsets);
+    hipLaunchKernelGGL(k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
+                       unique_keys_out, seg_offsets, chunk_seg, static_cast<uint32_t>(L.CS));
 
     // K7
     AdagradArgs a{};
@@ -730,21 +908,21 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
         a.rowbase[t] = ea.rowbase[t];
     }
     a.skeys = skeys;
-    a.perm = perm;
-    a.bag_of = bag_of;
-    a.weights = per_sample_weights;
+    a.sgrow = u32(L.grow[cur]);
+    a.swgt = reinterpret_cast<const float *>(u32(L.wgt[cur]));
     a.grad = grad_pooled;
+    a.seg_offsets = seg_offsets;
+    a.chunk_seg = chunk_seg;
     a.part_a = reinterpret_cast<float *>(ws + L.part_a);
     a.part_b = reinterpret_cast<float *>(ws + L.part_b);
     a.n = n;
     a.nchunk = L.nchunk;
-    a.B = static_cast<uint32_t>(B);
     a.T = T;
     a.D = D;
+    a.divT = make_fastdiv(static_cast<uint32_t>(T));
     a.lr = lr;
     a.eps = eps;
     a.inv_D = 1.0f / static_cast<float>(D);
-    const bool weighted = per_sample_weights != nullptr;
     if (dtype == DLRM_F32) dispatch_k7<DLRM_F32>(a, L.G, L.W, weighted, stream);
     else dispatch_k7<DLRM_BF16>(a, L.G, L.W, weighted, stream);
     return launch_status();
