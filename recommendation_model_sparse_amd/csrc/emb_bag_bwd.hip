@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
 
 struct Layout {
     size_t keys[2], pos[2], grow[2], wgt[2], counts, totals, flag, seg_count, seg_offsets,
-        chunk_seg, part_a, part_b, total;
+        chunk_seg, fin_count, fin_list, part_a, part_b, total;
     uint32_t nblk;    // sort / segment tiles
     uint32_t nchunk;  // K7 chunks of CS sorted positions
     int G, W, CS;
@@ -100,6 +100,8 @@ Layout make_layout(int32_t D, int64_t nnz) {
     L.seg_count = take(4 * static_cast<size_t>(L.nblk));
     L.seg_offsets = take(8 * (n + 1));
     L.chunk_seg = take(4 * static_cast<size_t>(L.nchunk));
+    L.fin_count = take(4);
+    L.fin_list = take(4 * static_cast<size_t>(L.nchunk));
     L.part_a = take(4 * static_cast<size_t>(L.nchunk) * D);
     L.part_b = take(4 * static_cast<size_t>(L.nchunk) * D);
     L.total = off;
@@ -224,24 +226,29 @@ struct SortIO {
     uint32_t *pout[3];
 };
 
-// NP payload words travel with each key.
+// NP payload words travel with each key.  Each 256-thread block ranks its tile of 4096 keys
+// stably with wavefront ballots, stages the tile in LDS in sorted order, and writes it out in
+// runs of equal digits, so the global stores are contiguous.
 template <int NP>
 __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, int shift,
                                                        const uint32_t *__restrict__ counts,
                                                        uint32_t nblk,
                                                        const uint32_t *__restrict__ totals) {
-    __shared__ uint32_t dbase[256];
+    __shared__ uint32_t gbase[256];  // global start of this block's run of digit d
+    __shared__ uint32_t lbase[256];  // start of digit d inside the block's sorted tile
     __shared__ uint32_t wcnt[4][256];
+    __shared__ uint32_t stage[kSortTile];
     const int tid = threadIdx.x, w = tid >> 6;
     {
         uint32_t tot;
         const uint32_t excl = block_exclusive_scan(totals[tid], &tot);
-        dbase[tid] = excl + counts[tid * nblk + blockIdx.x];
+        gbase[tid] = excl + counts[tid * nblk + blockIdx.x];
 #pragma unroll
         for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
     }
     __syncthreads();
-    const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + (tid & 63);
+    const uint32_t tile0 = blockIdx.x * kSortTile;
+    const uint32_t base = tile0 + w * (kSortTile / 4) + (tid & 63);
     uint32_t key[kSortItems], loc[kSortItems], pay[NP][kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
@@ -270,23 +277,47 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     }
     __syncthreads();
     {
-        const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid];
-        const uint32_t b = dbase[tid];
-        wcnt[0][tid] = b;
-        wcnt[1][tid] = b + c0;
-        wcnt[2][tid] = b + c0 + c1;
-        wcnt[3][tid] = b + c0 + c1 + c2;
+        const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid], c3 = wcnt[3][tid];
+        uint32_t tot;
+        const uint32_t ls = block_exclusive_scan(c0 + c1 + c2 + c3, &tot);
+        lbase[tid] = ls;
+        wcnt[0][tid] = ls;
+        wcnt[1][tid] = ls + c0;
+        wcnt[2][tid] = ls + c0 + c1;
+        wcnt[3][tid] = ls + c0 + c1 + c2;
     }
     __syncthreads();
+    const uint32_t nvalid = min(static_cast<uint32_t>(kSortTile), n - tile0);
+    // keys: stage in sorted order, then write runs
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
-        const uint32_t k = base + i * kWave;
-        if (k < n) {
-            const uint32_t d = (key[i] >> shift) & 255u;
-            const uint32_t p = wcnt[w][d] + loc[i];
-            io.kout[p] = key[i];
+        if (base + i * kWave < n) {
+            loc[i] += wcnt[w][(key[i] >> shift) & 255u];  // position in the sorted tile
+            stage[loc[i]] = key[i];
+        }
+    }
+    __syncthreads();
+    uint32_t dst[kSortItems];
 #pragma unroll
-            for (int q = 0; q < NP; ++q) io.pout[q][p] = pay[q][i];
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t q = j * 256 + tid;
+        const uint32_t k = stage[min(q, nvalid - 1)];
+        const uint32_t d = (k >> shift) & 255u;
+        dst[j] = gbase[d] + (q - lbase[d]);
+        if (q < nvalid) io.kout[dst[j]] = k;
+    }
+    // payloads, one staged pass each
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortItems; ++i)
+            if (base + i * kWave < n) stage[loc[i]] = pay[p][i];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t q = j * 256 + tid;
+            if (q < nvalid) io.pout[p][dst[j]] = stage[q];
         }
     }
 }
@@ -311,7 +342,8 @@ __global__ __launch_bounds__(256) void k_seg_count(const uint32_t *__restrict__ 
 // One block: exclusive scan of the per-tile segment counts; U and the closing offset.
 __global__ __launch_bounds__(256) void k_seg_scan(uint32_t *__restrict__ bcount, uint32_t nblk,
                                                   uint32_t n, int64_t *__restrict__ num_unique,
-                                                  int64_t *__restrict__ seg_offsets) {
+                                                  int64_t *__restrict__ seg_offsets,
+                                                  uint32_t *__restrict__ fin_count) {
     const uint32_t per = (nblk + 255) / 256;
     const uint32_t b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
     uint32_t s = 0;
@@ -326,6 +358,7 @@ __global__ __launch_bounds__(256) void k_seg_scan(uint32_t *__restrict__ bcount,
     if (threadIdx.x == 0) {
         if (num_unique) *num_unique = tot;
         seg_offsets[tot] = n;
+        *fin_count = 0;  // the finisher worklist of this call starts empty
     }
 }
 
@@ -382,6 +415,8 @@ struct AdagradArgs {
     const float *grad;            // [B][T][D]
     const int64_t *seg_offsets;   // [U+1]
     const uint32_t *chunk_seg;    // [nchunk]: segment of the chunk's last position
+    uint32_t *fin_count;          // number of chunks in fin_list
+    uint32_t *fin_list;           // chunks where a chunk-crossing segment starts
     float *part_a;
     float *part_b;
     uint32_t n;
@@ -684,63 +719,73 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     }
     // the last piece of the chunk
     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    else if (runs_past) store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    else adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+    else if (runs_past) {
+        store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+        // the segment starting here crosses into later chunks: queue it for the finisher
+        // (list order is arbitrary; each entry's work is fixed, so results do not depend on it)
+        if (c == 0) a.fin_list[atomicAdd(a.fin_count, 1u)] = chunk;
+    } else {
+        adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+    }
 }
 
-// One block per chunk: finishes the segment that starts in this chunk and runs past it,
-// adding its partials in chunk order (slot B here, slot A of every later chunk it covers).
+// Finishes the chunk-crossing segments: a grid-stride loop over the worklist K7 filled, one
+// listed chunk per block at a time.  The segment's partials are added in chunk order (slot B of
+// its first chunk, then slot A of every later chunk it covers), then the row is updated.
 template <int DT, int W, int G, int CS>
 __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
     constexpr int NS = 256 / G;  // partial rows read per pass of the block
-    constexpr int U = 4;
+    constexpr int U = 8;
     constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
     __shared__ float red[NS][G * W];
     __shared__ TableLDS sl;
     stage_tables(a, sl);
     const int sub = threadIdx.x / G, c = threadIdx.x % G;
-    const uint32_t chunk = blockIdx.x;
-    const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n);
-    if (hi >= a.n) return;  // block-uniform exits (no barrier after them)
-    if (a.skeys[hi] != a.skeys[hi - 1]) return;  // nothing runs past this chunk
-    const uint32_t u = a.chunk_seg[chunk];
-    const int64_t s = a.seg_offsets[u], e = a.seg_offsets[u + 1];
-    if (s < lo) return;  // it started in an earlier chunk
-    const uint32_t ce = static_cast<uint32_t>((e - 1) / CS);  // last chunk it covers
-    float acc[W];
+    const uint32_t count = *a.fin_count;
+    for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {  // block-uniform
+        const uint32_t chunk = a.fin_list[item];
+        const uint32_t lo = chunk * CS, hi = lo + CS;
+        const uint32_t u = a.chunk_seg[chunk];
+        const uint32_t ce = static_cast<uint32_t>((a.seg_offsets[u + 1] - 1) / CS);  // last chunk it covers
+        float acc[W];
 #pragma unroll
-    for (int q = 0; q < W; ++q) acc[q] = 0.f;
-    if (sub == 0) load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    for (uint32_t c1 = chunk + 1 + sub; c1 <= ce; c1 += NS * U) {
-        uint32_t pa[U][W];
+        for (int q = 0; q < W; ++q) acc[q] = 0.f;
+        if (sub == 0) load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+        for (uint32_t c1 = chunk + 1 + sub; c1 <= ce; c1 += NS * U) {
+            uint32_t pa[U][W];
 #pragma unroll
-        for (int k = 0; k < U; ++k)  // unconditional loads (clamped), all in flight together
-            gload_words<W>(a.part_a + static_cast<uint64_t>(min(c1 + k * NS, ce)) * a.D + c * W, pa[k]);
+            for (int k = 0; k < U; ++k)  // unconditional loads (clamped), all in flight together
+                gload_words<W>(a.part_a + static_cast<uint64_t>(min(c1 + k * NS, ce)) * a.D + c * W, pa[k]);
 #pragma unroll
-        for (int k = 0; k < U; ++k)
-            if (c1 + k * NS <= ce)
+            for (int k = 0; k < U; ++k)
+                if (c1 + k * NS <= ce)
 #pragma unroll
-                for (int q = 0; q < W; ++q) acc[q] += __uint_as_float(pa[k][q]);
+                    for (int q = 0; q < W; ++q) acc[q] += __uint_as_float(pa[k][q]);
+        }
+        // combine the NS row slots in a fixed order
+#pragma unroll
+        for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
+        __syncthreads();
+        if (sub == 0) {
+#pragma unroll
+            for (int q = 0; q < W; ++q) {
+                float x = red[0][c * W + q];
+                for (int k = 1; k < NS; ++k) x += red[k][c * W + q];
+                acc[q] = x;
+            }
+            const uint32_t K = a.skeys[hi - 1];
+            const uint32_t grow = a.sgrow[hi - 1];
+            const uint32_t t = grow - fast_div(grow, a.divT) * a.divT.d;
+            const uint32_t r = K - sl.rowbase[t];
+            char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
+            uint32_t old[TabWords<DT, W>::N];
+            gload_words<TabWords<DT, W>::N>(row, old);
+            adagrad_row<DT, W, G>(a, row, sl.state[t] + r, c, acc, old,
+                                  *(const DLRM_GLOBAL float *)(sl.state[t] + r));
+        }
+        __syncthreads();  // red[] is reused by the next item
+        (void)lo;
     }
-    // combine the NS row slots in a fixed order
-#pragma unroll
-    for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
-    __syncthreads();
-    if (sub != 0) return;
-#pragma unroll
-    for (int q = 0; q < W; ++q) {
-        float x = red[0][c * W + q];
-        for (int k = 1; k < NS; ++k) x += red[k][c * W + q];
-        acc[q] = x;
-    }
-    const uint32_t K = a.skeys[hi - 1];
-    const uint32_t grow = a.sgrow[hi - 1];
-    const uint32_t t = grow - fast_div(grow, a.divT) * a.divT.d;
-    const uint32_t r = K - sl.rowbase[t];
-    char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
-    uint32_t old[TabWords<DT, W>::N];
-    gload_words<TabWords<DT, W>::N>(row, old);
-    adagrad_row<DT, W, G>(a, row, sl.state[t] + r, c, acc, old, *(const DLRM_GLOBAL float *)(sl.state[t] + r));
 }
 
 template <int G>
@@ -756,7 +801,8 @@ void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
         hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, false, U>), dim3(blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_seg_finish<DT, W, G, G * MP>), dim3(a.nchunk), dim3(256), 0, stream, a);
+    const uint32_t fin_blocks = a.nchunk < 2048 ? a.nchunk : 2048;
+    hipLaunchKernelGGL((k_seg_finish<DT, W, G, G * MP>), dim3(fin_blocks), dim3(256), 0, stream, a);
 }
 
 template <int DT>
@@ -896,7 +942,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     uint32_t *chunk_seg = u32(L.chunk_seg);
     hipLaunchKernelGGL(k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
     hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
-                       num_unique_out, seg_offsets);
+                       num_unique_out, seg_offsets, u32(L.fin_count));
     hipLaunchKernelGGL(k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
                        unique_keys_out, seg_offsets, chunk_seg, static_cast<uint32_t>(L.CS));
 
@@ -913,6 +959,8 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     a.grad = grad_pooled;
     a.seg_offsets = seg_offsets;
     a.chunk_seg = chunk_seg;
+    a.fin_count = u32(L.fin_count);
+    a.fin_list = u32(L.fin_list);
     a.part_a = reinterpret_cast<float *>(ws + L.part_a);
     a.part_b = reinterpret_cast<float *>(ws + L.part_b);
     a.n = n;
