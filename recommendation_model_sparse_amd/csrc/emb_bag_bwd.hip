@@ -36,6 +36,14 @@ namespace {
 constexpr int kSortItems = 16;
 constexpr int kSortTile = 256 * kSortItems;  // keys per sort / segment block
 
+#ifndef DLRM_K7_U
+#define DLRM_K7_U 8  // gradient rows in flight per lane group
+#endif
+#ifndef DLRM_K7_BRANCH_PREFETCH
+#define DLRM_K7_BRANCH_PREFETCH 1  // 1: load table rows only where a segment starts
+#endif
+
+
 // floor(n / d) for n < 2^31 by multiply-high (Granlund & Montgomery 1994; Hacker's Delight 10-9).
 struct FastDiv {
     uint32_t d, m, s;
@@ -513,11 +521,22 @@ __device__ __forceinline__ void store_f32(float *p, const float *x) {
     RowIO<DLRM_F32, W>::store(reinterpret_cast<char *>(p), x);
 }
 
-// Sum of x over the G lanes of this lane group (butterfly: identical bits in every lane).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of x over the G lanes of this lane group; every lane ends with the same bits (each step
+// adds two partial sums that commute).  Within 16-lane rows the exchange is DPP (quad
+// permutes, half-row and row mirrors); across rows it is a cross-lane permute.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+    if constexpr (G >= 16) x += dpp_f32<0x140>(x); // row_mirror
 #pragma unroll
-    for (int s = 1; s < G; s <<= 1) x += __shfl_xor(x, s);
+    for (int s = 16; s < G; s <<= 1) x += __shfl_xor(x, s);
     return x;
 }
 
@@ -577,7 +596,11 @@ struct TabWords {
             for (int e = 0; e < W; ++e) w[e] = __float_as_uint(x[e]);
         } else {
 #pragma unroll
-            for (int e = 0; e < W / 2; ++e) w[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
+            for (int e = 0; e < W / 2; ++e) {  // v_cvt_pk_bf16_f32: round to nearest even
+                const __bf16 lo = static_cast<__bf16>(x[2 * e]), hi = static_cast<__bf16>(x[2 * e + 1]);
+                w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+            }
         }
     }
 };
@@ -593,7 +616,8 @@ __device__ __forceinline__ void adagrad_row(const AdagradArgs &a, char *row, flo
     for (int e = 0; e < W; ++e) ss = fmaf(g[e], g[e], ss);
     ss = group_sum<G>(ss);
     const float s_new = old_state + ss * a.inv_D;
-    const float step = a.lr / (sqrtf(s_new) + a.eps);
+    // hardware square root and reciprocal (about 1 ulp each)
+    const float step = a.lr * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(s_new) + a.eps);
     float x[W];
     TW::to_f32(old, x);
 #pragma unroll
@@ -658,6 +682,35 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    if (starts == 0) {
+        // no segment starts here: the whole chunk continues one that began earlier, so it is
+        // streamed straight into slot A with no per-position bookkeeping
+        float acc[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) acc[e] = 0.f;
+        for (uint32_t r0 = 0; r0 < cnt; r0 += U) {
+            uint32_t gr[U][W];
+            float wu[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const PosMeta &p = pm[min(r0 + u, cnt - 1)];
+                gload_words<W>(p.grad_row + c * W, gr[u]);
+                wu[u] = p.w;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (r0 + u < cnt) {
+#pragma unroll
+                    for (int e = 0; e < W; ++e) {
+                        const float g = __uint_as_float(gr[u][e]);
+                        acc[e] = WEIGHTED ? fmaf(wu[u], g, acc[e]) : acc[e] + g;
+                    }
+                }
+            }
+        }
+        store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+        return;
+    }
     bool open_before = !(starts & 1ull);  // the first piece began in an earlier chunk
     const bool runs_past = hi < a.n && a.skeys[hi] == a.skeys[hi - 1];
 
@@ -685,12 +738,19 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool s_u = (starts >> (r0 + u)) & 1ull;  // bits past cnt are 0
+#if DLRM_K7_BRANCH_PREFETCH
+            if (s_u) {
+                gload_words<TW::N>(mu[u].tab_row + c * W * ES, tr[u]);
+                st[u] = *(const DLRM_GLOBAL float *)mu[u].state;
+            }
+#else
             const void *tp = s_u ? static_cast<const void *>(mu[u].tab_row + c * W * ES)
                                  : static_cast<const void *>(mu[u].grad_row + c * W);
             const void *sp = s_u ? static_cast<const void *>(mu[u].state)
                                  : static_cast<const void *>(mu[u].grad_row);
             gload_words<TW::N>(tp, tr[u]);
             st[u] = *(const DLRM_GLOBAL float *)sp;
+#endif
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -795,7 +855,7 @@ template <int DT, int W, int G>
 void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
     constexpr int NG = kWave / G;
     constexpr int MP = chunk_mp<G>();
-    constexpr int U = 8;
+    constexpr int U = DLRM_K7_U;
     const uint32_t blocks = (a.nchunk + 4 * NG - 1) / (4 * NG);
     if (weighted)
         hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
