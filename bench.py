@@ -60,7 +60,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=4)
-    ap.add_argument("--cpu-samples", type=int, default=8192)
+    ap.add_argument("--cpu-samples", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
@@ -82,7 +82,8 @@ def main():
         log("[bench] copy probe: 3 copies of 1 GiB")
         return
     from recommendation_model_sparse_amd import (AdagradOutputs, dlrm_interact_bwd, dlrm_interact_fwd,
-                                                 dlrm_synth_fill_table, emb_bag_bwd_adagrad,
+                                                 dlrm_synth_fill_table, dlrm_trace_enable,
+                                                 dlrm_trace_read, emb_bag_bwd_adagrad,
                                                  emb_bag_bwd_workspace_size, emb_bag_fwd, synth)
     from recommendation_model_sparse_amd.configs import make_config
 
@@ -158,13 +159,43 @@ def main():
                for k, n in enumerate(names)}
     log("[bench] per call (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in call_ms.items()))
 
+    # per-kernel HIP event times recorded by the library itself (dlrm_trace_*), third region
+    dlrm_trace_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    trace = dlrm_trace_read()
+    dlrm_trace_enable(False)
+    kern_ms = {k: ms / args.steps for k, (n, ms) in trace.items()}  # per step
+    kern_launch_ms = {k: ms / n for k, (n, ms) in trace.items()}    # per launch
+    log("[bench] per kernel (ms/step): " + ", ".join(f"{k}={v:.4f}" for k, v in
+                                                     sorted(kern_ms.items(), key=lambda x: -x[1])))
+
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
+    U_last = int(outs.num_unique.item())
     es = wl.elem_size
-    gathered = nnz_avg * wl.D * es
-    k1_bytes = gathered + nnz_avg * 8 + (wl.T * wl.B + 1) * 8 + wl.B * wl.T * wl.D * 4
+    D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
+    gathered = nnz_avg * D * es
+    # algorithmic bytes per launch of the main kernels
+    alg = {
+        "pool_wave_per_bag": gathered + nnz_avg * 8 + (T * B + 1) * 8 + B * T * D * 4,
+        "seg_reduce_adagrad": nnz_avg * (4 * D + 8) + U_last * (2 * D * es + 8),
+        "interact_fwd_mfma": B * (N * D * 4 + (P + D) * 4),
+        "interact_bwd": B * ((P + D) * 4 + 2 * N * D * 4),
+        "radix_scatter": nnz_avg * 3 * 4 * 2,
+        "radix_hist": nnz_avg * 4,
+        "expand": nnz_avg * (8 + 4 * 3) + (T * B + 1) * 8,
+    }
+    kernels = {}
+    for k, b_alg in alg.items():
+        if k in kern_launch_ms:
+            gbps = b_alg / (kern_launch_ms[k] / 1e3) / 1e9
+            kernels[k] = {"ms_per_launch": kern_launch_ms[k], "ms_per_step": kern_ms[k],
+                          "algorithmic_bytes": b_alg, "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
+    dominant = max(kern_ms, key=lambda k: kern_ms[k])
+    dom = kernels.get(dominant)
     k1_s = call_ms["emb_bag_fwd"] / 1e3
     gathered_gbps = gathered / k1_s / 1e9
-    k1_gbps = k1_bytes / k1_s / 1e9
 
     res = {
         "metric": "samples/sec + gathered-embedding GB/s (fraction of HBM peak), 1 MI355X",
@@ -188,11 +219,15 @@ def main():
         "gathered_GBps": gathered_gbps,
         "gathered_frac_of_hbm_peak": gathered_gbps / HBM_PEAK_GBPS,
         "fwd_samples_per_s": wl.B / ((call_ms["emb_bag_fwd"] + call_ms["dlrm_interact_fwd"]) / 1e3),
+        "unique_rows": U_last,
         "call_ms": call_ms,
-        "roofline": {"bound": "hbm", "kernel": "emb_bag_fwd (k_pool_wave_per_bag, bf16, G=16)",
-                     "achieved": k1_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": k1_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "algorithmic_bytes_per_launch": k1_bytes},
+        "kernel_ms_per_step": kern_ms,
+        "roofline": {"bound": "hbm", "kernel": dominant,
+                     "achieved": dom["GBps"] if dom else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom["frac_hbm_peak"] if dom else None, "traffic": None,
+                     "ms_per_launch": kern_launch_ms[dominant],
+                     "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
+        "kernels": kernels,
     }
     if not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")

@@ -20,8 +20,9 @@
  *     read before the call returns.
  *   - The caller allocates and owns every device buffer, including the
  *     workspace, and keeps it alive until the work on `stream` completes.
- *     The library allocates no device memory and keeps no mutable state, so
- *     calls on different streams may run concurrently on distinct buffers.
+ *     The library allocates no device memory and keeps no mutable state
+ *     (apart from the opt-in kernel timing record, dlrm_trace_*), so calls on
+ *     different streams may run concurrently on distinct buffers.
  *   - Every call enqueues on `stream` (a hipStream_t; NULL = the null stream)
  *     and returns without waiting, except with DLRM_FLAG_CHECK_INDICES, which
  *     synchronises the stream to report the result of the check.
@@ -173,6 +174,21 @@ int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t 
 
 /* Static description of a status code. */
 const char *dlrm_status_string(int status);
+
+/*
+ * Kernel timing (diagnostics).  While enabled (dlrm_trace_enable(1)), every kernel the library
+ * launches is bracketed by two HIP events recorded on its stream; disabled (the default), a
+ * launch is unchanged apart from one atomic flag read.  dlrm_trace_read waits for the recorded
+ * kernels to finish, then writes, per kernel name (sorted), the number of launches and their
+ * summed milliseconds, and clears the record.  Process-wide state behind a mutex; calls that
+ * record into a HIP graph capture must not have tracing enabled.
+ *
+ *   names    (host) max_entries * 64 chars, NUL-terminated names
+ *   launches (host) [max_entries];  ms (host) [max_entries];  n_entries (host) entries written
+ */
+int dlrm_trace_enable(int on);
+int dlrm_trace_read(int32_t max_entries, char *names, int64_t *launches, double *ms,
+                    int32_t *n_entries);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     dlrm_interact_fwd,
     dlrm_status_string,
     dlrm_synth_fill_table,
+    dlrm_trace_enable,
+    dlrm_trace_read,
     emb_bag_bwd_adagrad,
     emb_bag_bwd_workspace_size,
     emb_bag_fwd,

@@ -48,8 +48,10 @@ def lib() -> ctypes.CDLL:
         L.dlrm_status_string.argtypes = [ctypes.c_int]
         L.dlrm_status_string.restype = ctypes.c_char_p
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
+        L.dlrm_trace_enable.argtypes = [ctypes.c_int]
+        L.dlrm_trace_read.argtypes = [i32, p, p, p, p]
         for f in (L.emb_bag_fwd, L.dlrm_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
-                  L.dlrm_synth_fill_table):
+                  L.dlrm_synth_fill_table, L.dlrm_trace_enable, L.dlrm_trace_read):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,3 +217,22 @@ def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) 
     _check(lib().dlrm_synth_fill_table(_ptr(table), _dtype_code(table), table.shape[0],
                                        table.shape[1], t, seed, float(scale),
                                        _stream(table.device)), "dlrm_synth_fill_table")
+
+
+def dlrm_trace_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (C: dlrm_trace_enable)."""
+    _check(lib().dlrm_trace_enable(1 if on else 0), "dlrm_trace_enable")
+
+
+def dlrm_trace_read(max_entries: int = 64) -> dict:
+    """{kernel name: (launches, total ms)} since the last read (C: dlrm_trace_read)."""
+    names = ctypes.create_string_buffer(64 * max_entries)
+    launches = (ctypes.c_int64 * max_entries)()
+    ms = (ctypes.c_double * max_entries)()
+    n = ctypes.c_int32(0)
+    _check(lib().dlrm_trace_read(max_entries, names, launches, ms, ctypes.byref(n)), "dlrm_trace_read")
+    out = {}
+    for i in range(n.value):
+        name = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+        out[name] = (int(launches[i]), float(ms[i]))
+    return out

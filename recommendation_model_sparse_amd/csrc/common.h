@@ -36,7 +36,57 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Loads and stores through the global address space (pointers staged in LDS would otherwise be
+// generic/flat, and flat loads also count against the LDS wait counter).
+#define DLRM_GLOBAL __attribute__((address_space(1)))
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int WORDS>
+__device__ __forceinline__ void gload_words(const void *p, uint32_t *w) {
+    if constexpr (WORDS == 1) {
+        w[0] = *(const DLRM_GLOBAL uint32_t *)p;
+    } else if constexpr (WORDS == 2) {
+        const u32x2 v = *(const DLRM_GLOBAL u32x2 *)p;
+        w[0] = v.x, w[1] = v.y;
+    } else {
+        const DLRM_GLOBAL u32x4 *q = (const DLRM_GLOBAL u32x4 *)p;
+#pragma unroll
+        for (int i = 0; i < WORDS / 4; ++i) {
+            const u32x4 v = q[i];
+            w[4 * i] = v.x, w[4 * i + 1] = v.y, w[4 * i + 2] = v.z, w[4 * i + 3] = v.w;
+        }
+    }
+}
+
+template <int WORDS>
+__device__ __forceinline__ void gstore_words(void *p, const uint32_t *w) {
+    if constexpr (WORDS == 1) {
+        *(DLRM_GLOBAL uint32_t *)p = w[0];
+    } else if constexpr (WORDS == 2) {
+        *(DLRM_GLOBAL u32x2 *)p = u32x2{w[0], w[1]};
+    } else {
+        DLRM_GLOBAL u32x4 *q = (DLRM_GLOBAL u32x4 *)p;
+#pragma unroll
+        for (int i = 0; i < WORDS / 4; ++i) q[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    }
+}
+
 // ---------------------------------------------------------------- host helpers
+
+// Kernel timing (trace.cpp): when enabled, each launch is bracketed by HIP events.
+bool trace_on();
+void trace_begin(hipStream_t s);
+void trace_end(const char *name, hipStream_t s);
+
+#define DLRM_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                     \
+    do {                                                                             \
+        const bool dlrm_traced_ = ::dlrm::trace_on();                                \
+        if (dlrm_traced_) ::dlrm::trace_begin(STREAM);                               \
+        hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);          \
+        if (dlrm_traced_) ::dlrm::trace_end(NAME, STREAM);                           \
+    } while (0)
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

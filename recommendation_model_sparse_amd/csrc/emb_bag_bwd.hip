@@ -540,43 +540,6 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// Loads and stores through the global address space (pointers staged in LDS would otherwise be
-// generic/flat, and flat loads also count against the LDS wait counter).
-#define DLRM_GLOBAL __attribute__((address_space(1)))
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-template <int WORDS>
-__device__ __forceinline__ void gload_words(const void *p, uint32_t *w) {
-    if constexpr (WORDS == 1) {
-        w[0] = *(const DLRM_GLOBAL uint32_t *)p;
-    } else if constexpr (WORDS == 2) {
-        const u32x2 v = *(const DLRM_GLOBAL u32x2 *)p;
-        w[0] = v.x, w[1] = v.y;
-    } else {
-        const DLRM_GLOBAL u32x4 *q = (const DLRM_GLOBAL u32x4 *)p;
-#pragma unroll
-        for (int i = 0; i < WORDS / 4; ++i) {
-            const u32x4 v = q[i];
-            w[4 * i] = v.x, w[4 * i + 1] = v.y, w[4 * i + 2] = v.z, w[4 * i + 3] = v.w;
-        }
-    }
-}
-
-template <int WORDS>
-__device__ __forceinline__ void gstore_words(void *p, const uint32_t *w) {
-    if constexpr (WORDS == 1) {
-        *(DLRM_GLOBAL uint32_t *)p = w[0];
-    } else if constexpr (WORDS == 2) {
-        *(DLRM_GLOBAL u32x2 *)p = u32x2{w[0], w[1]};
-    } else {
-        DLRM_GLOBAL u32x4 *q = (DLRM_GLOBAL u32x4 *)p;
-#pragma unroll
-        for (int i = 0; i < WORDS / 4; ++i) q[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    }
-}
-
 // W table elements as 32-bit words: fp32 one per word, bf16 two per word.
 template <int DT, int W>
 struct TabWords {
@@ -858,11 +821,11 @@ void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
     constexpr int U = DLRM_K7_U;
     const uint32_t blocks = (a.nchunk + 4 * NG - 1) / (4 * NG);
     if (weighted)
-        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH("seg_reduce_adagrad", (k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_seg_reduce_adagrad<DT, W, G, MP, false, U>), dim3(blocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH("seg_reduce_adagrad", (k_seg_reduce_adagrad<DT, W, G, MP, false, U>), dim3(blocks), dim3(256), 0, stream, a);
     const uint32_t fin_blocks = a.nchunk < 2048 ? a.nchunk : 2048;
-    hipLaunchKernelGGL((k_seg_finish<DT, W, G, G * MP>), dim3(fin_blocks), dim3(256), 0, stream, a);
+    DLRM_LAUNCH("seg_finish", (k_seg_finish<DT, W, G, G * MP>), dim3(fin_blocks), dim3(256), 0, stream, a);
 }
 
 template <int DT>
@@ -885,7 +848,7 @@ void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t 
 template <int NP>
 void launch_scatter(const SortIO &io, uint32_t n, int shift, const uint32_t *counts, uint32_t nblk,
                     const uint32_t *totals, hipStream_t stream) {
-    hipLaunchKernelGGL(k_radix_scatter<NP>, dim3(nblk), dim3(256), 0, stream, io, n, shift, counts,
+    DLRM_LAUNCH("radix_scatter", k_radix_scatter<NP>, dim3(nblk), dim3(256), 0, stream, io, n, shift, counts,
                        nblk, totals);
 }
 
@@ -938,7 +901,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     const bool want_seg = unique_keys_out || segment_offsets_out || num_unique_out;
     if (nnz == 0) {
         if (want_seg)
-            hipLaunchKernelGGL(k_empty_outputs, dim3(1), dim3(1), 0, stream, num_unique_out,
+            DLRM_LAUNCH("empty_outputs", k_empty_outputs, dim3(1), dim3(1), 0, stream, num_unique_out,
                                segment_offsets_out);
         return launch_status();
     }
@@ -963,7 +926,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     ea.B = static_cast<uint32_t>(B);
     ea.T = static_cast<uint32_t>(T);
     ea.nbags = static_cast<uint32_t>(T * B);
-    hipLaunchKernelGGL(k_expand, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
+    DLRM_LAUNCH("expand", k_expand, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
     // K5: passes over the significant bits of the largest key (sumV - 1)
     int bits = 0;
@@ -982,8 +945,8 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
         io.pout[1] = u32(L.grow[cur ^ 1]);
         io.pin[2] = u32(L.wgt[cur]);
         io.pout[2] = u32(L.wgt[cur ^ 1]);
-        hipLaunchKernelGGL(k_radix_hist, dim3(L.nblk), dim3(256), 0, stream, io.kin, n, 8 * p, counts, L.nblk);
-        hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(256), 0, stream, counts, L.nblk, totals);
+        DLRM_LAUNCH("radix_hist", k_radix_hist, dim3(L.nblk), dim3(256), 0, stream, io.kin, n, 8 * p, counts, L.nblk);
+        DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(256), dim3(256), 0, stream, counts, L.nblk, totals);
         if (NP == 3) launch_scatter<3>(io, n, 8 * p, counts, L.nblk, totals, stream);
         else launch_scatter<2>(io, n, 8 * p, counts, L.nblk, totals, stream);
         cur ^= 1;
@@ -1000,10 +963,10 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     int64_t *seg_offsets = segment_offsets_out ? segment_offsets_out
                                                : reinterpret_cast<int64_t *>(ws + L.seg_offsets);
     uint32_t *chunk_seg = u32(L.chunk_seg);
-    hipLaunchKernelGGL(k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
-    hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
+    DLRM_LAUNCH("seg_count", k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
+    DLRM_LAUNCH("seg_scan", k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
                        num_unique_out, seg_offsets, u32(L.fin_count));
-    hipLaunchKernelGGL(k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
+    DLRM_LAUNCH("seg_write", k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
                        unique_keys_out, seg_offsets, chunk_seg, static_cast<uint32_t>(L.CS));
 
     // K7

@@ -266,9 +266,9 @@ int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
     c.nbags = static_cast<uint32_t>(T * B);
     c.nnz = nnz;
     c.flag = flag;
-    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, stream, flag, 0);
+    DLRM_LAUNCH("set_int", k_set_int, dim3(1), dim3(1), 0, stream, flag, 0);
     const uint32_t blocks = c.nbags == 0 ? 1 : (c.nbags + 255) / 256;
-    hipLaunchKernelGGL(k_check_csr, dim3(blocks), dim3(256), 0, stream, c);
+    DLRM_LAUNCH("check_csr", k_check_csr, dim3(blocks), dim3(256), 0, stream, c);
     if (hipGetLastError() != hipSuccess) return DLRM_ERR_HIP;
     int host_flag = 0;
     if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
@@ -285,12 +285,12 @@ void launch_pool(const PoolArgs &a0, bool wave_per_bag, hipStream_t stream) {
     constexpr int NG = kWave / G;
     if (wave_per_bag) {
         a.nblocks = round_up_xcd((a.nbags + 3) / 4);
-        hipLaunchKernelGGL((k_pool_wave_per_bag<DT, G, W>), dim3(a.nblocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH("pool_wave_per_bag", (k_pool_wave_per_bag<DT, G, W>), dim3(a.nblocks), dim3(256), 0, stream, a);
     } else {
         constexpr int BPG = G >= 64 ? 1 : (G >= 32 ? 2 : 4);
         const uint64_t per_block = 4ull * NG * BPG;
         a.nblocks = round_up_xcd((a.nbags + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_pool_group_per_bag<DT, G, W, BPG>), dim3(a.nblocks), dim3(256), 0,
+        DLRM_LAUNCH("pool_group_per_bag", (k_pool_group_per_bag<DT, G, W, BPG>), dim3(a.nblocks), dim3(256), 0,
                            stream, a);
     }
 }
@@ -305,7 +305,7 @@ void dispatch_g(const PoolArgs &a, uint32_t chunks, bool wave_per_bag, hipStream
         case 64: launch_pool<DT, 64, W>(a, wave_per_bag, stream); break;
         default: {
             const uint64_t threads = static_cast<uint64_t>(a.nbags) * chunks;
-            hipLaunchKernelGGL((k_pool_generic<DT, W>), dim3((threads + 255) / 256), dim3(256), 0,
+            DLRM_LAUNCH("pool_generic", (k_pool_generic<DT, W>), dim3((threads + 255) / 256), dim3(256), 0,
                                stream, a, chunks);
         }
     }

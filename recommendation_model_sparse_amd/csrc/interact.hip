@@ -218,12 +218,12 @@ bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32
     const dim3 grid((B + 3) / 4), block(256);
     // operands of CHG chunks are loaded at once: NB*CHG*KC/4 registers, kept <= 64
     switch (D) {
-        case 16: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 16, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 32: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 64: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 2, (NB <= 4 ? 2 : 1)>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 128: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 4, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 256: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 8, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 512: hipLaunchKernelGGL((k_interact_fwd_mfma<NB, 32, 16, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 16: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 16, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 32: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 64: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 2, (NB <= 4 ? 2 : 1)>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 128: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 4, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 256: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 8, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 512: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 16, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         default: return false;
     }
 }
@@ -234,12 +234,12 @@ void launch_bwd(const float *g, const float *dense, const float *pooled, float *
     if (D >= 128) {
         const int slices = (D + 127) / 128;
         const uint64_t waves = static_cast<uint64_t>(B) * slices;
-        hipLaunchKernelGGL((k_interact_bwd<NP, 2>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
+        DLRM_LAUNCH("interact_bwd", (k_interact_bwd<NP, 2>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
                            dense, pooled, gd, gp, B, N, D, P, slices);
     } else {
         const int slices = (D + 63) / 64;
         const uint64_t waves = static_cast<uint64_t>(B) * slices;
-        hipLaunchKernelGGL((k_interact_bwd<NP, 1>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
+        DLRM_LAUNCH("interact_bwd", (k_interact_bwd<NP, 1>), dim3((waves + 3) / 4), dim3(256), 0, stream, g,
                            dense, pooled, gd, gp, B, N, D, P, slices);
     }
 }
@@ -274,7 +274,7 @@ extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_
         case 5: done = launch_fwd_mfma<5>(dense, pooled, out, b, N, D, P, stream); break;
     }
     if (!done)
-        hipLaunchKernelGGL(k_interact_fwd_valu, dim3(b), dim3(256), 0, stream, dense, pooled, out,
+        DLRM_LAUNCH("interact_fwd_valu", k_interact_fwd_valu, dim3(b), dim3(256), 0, stream, dense, pooled, out,
                            N, D, P);
     return launch_status();
 }

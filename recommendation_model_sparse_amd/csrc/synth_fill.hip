@@ -65,11 +65,11 @@ extern "C" int dlrm_synth_fill_table(void *table, int32_t dtype, int64_t rows, i
     const uint64_t want = (chunks + 255) / 256;
     const uint32_t blocks = static_cast<uint32_t>(want < 256 * 64 ? want : 256 * 64);
     if (dtype == DLRM_F32)
-        hipLaunchKernelGGL(k_fill<DLRM_F32>, dim3(blocks), dim3(256), 0, stream,
+        DLRM_LAUNCH("synth_fill", k_fill<DLRM_F32>, dim3(blocks), dim3(256), 0, stream,
                            static_cast<char *>(table), static_cast<uint64_t>(rows),
                            static_cast<uint32_t>(D), static_cast<uint32_t>(t), seed, scale);
     else
-        hipLaunchKernelGGL(k_fill<DLRM_BF16>, dim3(blocks), dim3(256), 0, stream,
+        DLRM_LAUNCH("synth_fill", k_fill<DLRM_BF16>, dim3(blocks), dim3(256), 0, stream,
                            static_cast<char *>(table), static_cast<uint64_t>(rows),
                            static_cast<uint32_t>(D), static_cast<uint32_t>(t), seed, scale);
     return launch_status();

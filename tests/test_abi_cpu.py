@@ -1,0 +1,167 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports what the headers declare,
+and rejects invalid arguments on the host before anything touches a device.
+
+No call here reaches a kernel launch: every case fails host validation (fake device pointers
+are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from recommendation_model_sparse_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+OK, INVALID, UNSUPPORTED, HIP, INDEX, WORKSPACE = 0, -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    names = set()
+    for h in os.listdir(INCLUDE):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"emb_bag_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
+            "emb_bag_bwd_adagrad", "dlrm_status_string", "dlrm_synth_fill_table",
+            "dlrm_trace_enable", "dlrm_trace_read"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, UNSUPPORTED, HIP, INDEX, WORKSPACE):
+        assert binding.status_string(s)
+    assert "unknown" in binding.status_string(17)
+
+
+def ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def i64s(*vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def fwd(L, tables=None, rows=None, T=1, D=16, dtype=0, idx=FAKE, off=FAKE, w=None, B=4, nnz=4,
+        out=FAKE, flags=0):
+    tables = ptrs(FAKE) if tables is None else tables
+    rows = i64s(10) if rows is None else rows
+    return L.emb_bag_fwd(tables, rows, T, D, dtype, idx, off, w, B, nnz, out, flags, None)
+
+
+def test_emb_bag_fwd_rejects(L):
+    assert fwd(L, T=0) == INVALID
+    assert fwd(L, T=65, tables=ptrs(*[FAKE] * 65), rows=i64s(*[1] * 65)) == INVALID
+    assert fwd(L, D=0) == INVALID
+    assert fwd(L, D=6) == UNSUPPORTED          # fp32 rows must be a multiple of 16 bytes
+    assert fwd(L, D=12, dtype=1) == UNSUPPORTED  # bf16 rows likewise
+    assert fwd(L, D=1024) == UNSUPPORTED
+    assert fwd(L, dtype=7) == INVALID
+    assert fwd(L, B=-1) == INVALID
+    assert fwd(L, nnz=-1) == INVALID
+    assert fwd(L, tables=ptrs(0)) == INVALID
+    assert fwd(L, tables=ptrs(FAKE + 4)) == INVALID   # misaligned table
+    assert fwd(L, rows=i64s(0)) == INVALID
+    assert fwd(L, off=0) == INVALID
+    assert fwd(L, idx=0) == INVALID
+    assert fwd(L, idx=FAKE + 4) == INVALID
+    assert fwd(L, out=0) == INVALID
+    assert fwd(L, out=FAKE + 4) == INVALID
+    assert fwd(L, flags=8) == INVALID
+    assert fwd(L, B=0, nnz=3) == INVALID
+    assert fwd(L, B=0, nnz=0) == OK            # nothing to do, nothing launched
+    assert fwd(L, B=1 << 30, T=2, tables=ptrs(FAKE, FAKE), rows=i64s(1, 1)) == UNSUPPORTED
+
+
+def test_interact_rejects(L):
+    f = L.dlrm_interact_fwd
+    assert f(FAKE, FAKE, 4, 0, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 66, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 5, 6, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 4, 5, 1024, FAKE, None) == UNSUPPORTED
+    assert f(None, FAKE, 4, 5, 16, FAKE, None) == INVALID
+    assert f(FAKE, None, 4, 5, 16, FAKE, None) == INVALID
+    assert f(FAKE + 4, FAKE, 4, 5, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, -1, 5, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 0, 5, 16, FAKE, None) == OK
+    b = L.dlrm_interact_bwd
+    assert b(None, FAKE, FAKE, 4, 5, 16, FAKE, FAKE, None) == INVALID
+    assert b(FAKE, FAKE, FAKE, 4, 5, 16, FAKE, None, None) == INVALID
+    assert b(FAKE, FAKE, FAKE, 4, 5, 16, FAKE + 8, FAKE, None) == INVALID
+    assert b(FAKE, FAKE, FAKE, 4, 5, 6, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_workspace_size(L):
+    ws = lambda rows, D, B, nnz: binding.emb_bag_bwd_workspace_size(rows, D, B, nnz)
+    assert ws([100], 6, 4, 10) == 0          # D must be a power of two
+    assert ws([100], 1024, 4, 10) == 0
+    a, b = ws([100, 200], 128, 64, 1000), ws([100, 200], 128, 64, 100000)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+    assert ws([100], 128, 4, 0) > 0           # valid for an empty batch too
+
+
+def bwd(L, T=1, D=16, dtype=0, B=4, nnz=4, rows=None, ws=FAKE, wsz=None, grad=FAKE, state=None,
+        tables=None, flags=0):
+    rows = rows if rows is not None else [10] * T
+    r = i64s(*rows)
+    tables = tables if tables is not None else ptrs(*[FAKE] * T)
+    state = state if state is not None else ptrs(*[FAKE] * T)
+    if wsz is None:
+        wsz = binding.emb_bag_bwd_workspace_size(rows, D, B, nnz)
+    return L.emb_bag_bwd_adagrad(tables, state, r, T, D, dtype, FAKE, FAKE, None, B, nnz, grad,
+                                 0.01, 1e-8, ws, wsz, None, None, None, None, flags, None)
+
+
+def test_emb_bag_bwd_rejects(L):
+    assert bwd(L, D=24) == UNSUPPORTED         # not a power of two
+    assert bwd(L, D=4, dtype=1) == UNSUPPORTED  # bf16 rows below 16 bytes
+    assert bwd(L, rows=[1 << 31, 1 << 31, 5], T=3) == UNSUPPORTED  # keys beyond 32 bits
+    assert bwd(L, state=ptrs(0)) == INVALID
+    assert bwd(L, grad=0) == INVALID
+    assert bwd(L, grad=FAKE + 4) == INVALID
+    assert bwd(L, ws=0) == WORKSPACE
+    assert bwd(L, ws=FAKE + 16) == WORKSPACE    # workspace must be 256-byte aligned
+    need = binding.emb_bag_bwd_workspace_size([10], 16, 4, 4)
+    assert bwd(L, wsz=need - 1) == WORKSPACE
+    assert bwd(L, flags=2) == INVALID
+    assert bwd(L, B=0, nnz=2) == INVALID
+
+
+def test_trace_api_without_gpu(L):
+    binding.dlrm_trace_enable(True)
+    assert binding.dlrm_trace_read() == {}
+    binding.dlrm_trace_enable(False)
+    n = ctypes.c_int32(0)
+    assert L.dlrm_trace_read(-1, None, None, None, ctypes.byref(n)) == INVALID
+
+
+def test_synth_fill_rejects(L):
+    f = L.dlrm_synth_fill_table
+    assert f(None, 0, 10, 16, 0, 1, 1.0, None) == INVALID
+    assert f(FAKE, 0, 0, 16, 0, 1, 1.0, None) == INVALID
+    assert f(FAKE, 0, 10, 6, 0, 1, 1.0, None) == INVALID
+    assert f(FAKE, 2, 10, 16, 0, 1, 1.0, None) == INVALID
+    assert f(FAKE + 4, 0, 10, 16, 0, 1, 1.0, None) == INVALID
