@@ -102,8 +102,8 @@ Layout make_layout(int32_t D, int64_t nnz) {
         L.grow[i] = take(4 * n);
         L.wgt[i] = take(4 * n);
     }
-    L.counts = take(4 * 256 * static_cast<size_t>(L.nblk));
-    L.totals = take(4 * 256);
+    L.counts = take(4 * 1024 * static_cast<size_t>(L.nblk));  // up to 10-bit digits
+    L.totals = take(4 * 1024);
     L.flag = take(4);
     L.seg_count = take(4 * static_cast<size_t>(L.nblk));
     L.seg_offsets = take(8 * (n + 1));
@@ -192,21 +192,24 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
 
 // ---------------------------------------------------------------- K5 radix sort
 
+// Digits of RB bits (8..10): K = 2^RB / 256 digits per thread in the per-digit phases.
+template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__ keys, uint32_t n,
                                                     int shift, uint32_t *__restrict__ counts,
                                                     uint32_t nblk) {
-    __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
+    constexpr int NBK = 1 << RB;
+    __shared__ uint32_t h[NBK];
+    for (int d = threadIdx.x; d < NBK; d += 256) h[d] = 0;
     __syncthreads();
     const uint32_t base = blockIdx.x * kSortTile;
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const uint32_t k = base + i * 256 + threadIdx.x;
         const uint32_t key = keys[min(k, n - 1)];
-        if (k < n) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        if (k < n) atomicAdd(&h[(key >> shift) & (NBK - 1)], 1u);
     }
     __syncthreads();
-    counts[threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+    for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + blockIdx.x] = h[d];
 }
 
 // Block d: exclusive scan of counts[d][0..nblk) in place; totals[d] = row sum.
@@ -237,22 +240,37 @@ struct SortIO {
 // NP payload words travel with each key.  Each 256-thread block ranks its tile of 4096 keys
 // stably with wavefront ballots, stages the tile in LDS in sorted order, and writes it out in
 // runs of equal digits, so the global stores are contiguous.
-template <int NP>
+template <int NP, int RB>
 __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, int shift,
                                                        const uint32_t *__restrict__ counts,
                                                        uint32_t nblk,
                                                        const uint32_t *__restrict__ totals) {
-    __shared__ uint32_t gbase[256];  // global start of this block's run of digit d
-    __shared__ uint32_t lbase[256];  // start of digit d inside the block's sorted tile
-    __shared__ uint32_t wcnt[4][256];
+    constexpr int NBK = 1 << RB;
+    constexpr int K = NBK / 256;             // digits per thread in the per-digit phases
+    constexpr uint32_t MASK = NBK - 1;
+    __shared__ uint32_t gbase[NBK];  // global start of this block's run of digit d
+    __shared__ uint32_t lbase[NBK];  // start of digit d inside the block's sorted tile
+    __shared__ uint32_t wcnt[4][NBK];
     __shared__ uint32_t stage[kSortTile];
     const int tid = threadIdx.x, w = tid >> 6;
     {
-        uint32_t tot;
-        const uint32_t excl = block_exclusive_scan(totals[tid], &tot);
-        gbase[tid] = excl + counts[tid * nblk + blockIdx.x];
+        // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
+        uint32_t tv[K], sum = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
+        for (int k = 0; k < K; ++k) {
+            tv[k] = totals[tid * K + k];
+            sum += tv[k];
+        }
+        uint32_t tot;
+        uint32_t run = block_exclusive_scan(sum, &tot);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int d = tid * K + k;
+            gbase[d] = run + counts[d * nblk + blockIdx.x];
+            run += tv[k];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wcnt[q][d] = 0;
+        }
     }
     __syncthreads();
     const uint32_t tile0 = blockIdx.x * kSortTile;
@@ -269,10 +287,10 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const bool valid = base + i * kWave < n;
-        const uint32_t d = (key[i] >> shift) & 255u;
+        const uint32_t d = (key[i] >> shift) & MASK;
         uint64_t peers = __ballot(valid);
 #pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
+        for (int bit = 0; bit < RB; ++bit) {
             const bool on = (d >> bit) & 1u;
             const uint64_t m = __ballot(on);
             peers &= on ? m : ~m;
@@ -285,14 +303,26 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     }
     __syncthreads();
     {
-        const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid], c3 = wcnt[3][tid];
+        uint32_t c[K][4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[k][q] = wcnt[q][tid * K + k];
+                sum += c[k][q];
+            }
         uint32_t tot;
-        const uint32_t ls = block_exclusive_scan(c0 + c1 + c2 + c3, &tot);
-        lbase[tid] = ls;
-        wcnt[0][tid] = ls;
-        wcnt[1][tid] = ls + c0;
-        wcnt[2][tid] = ls + c0 + c1;
-        wcnt[3][tid] = ls + c0 + c1 + c2;
+        uint32_t run = block_exclusive_scan(sum, &tot);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int d = tid * K + k;
+            lbase[d] = run;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wcnt[q][d] = run;
+                run += c[k][q];
+            }
+        }
     }
     __syncthreads();
     const uint32_t nvalid = min(static_cast<uint32_t>(kSortTile), n - tile0);
@@ -300,7 +330,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         if (base + i * kWave < n) {
-            loc[i] += wcnt[w][(key[i] >> shift) & 255u];  // position in the sorted tile
+            loc[i] += wcnt[w][(key[i] >> shift) & MASK];  // position in the sorted tile
             stage[loc[i]] = key[i];
         }
     }
@@ -310,7 +340,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t q = j * 256 + tid;
         const uint32_t k = stage[min(q, nvalid - 1)];
-        const uint32_t d = (k >> shift) & 255u;
+        const uint32_t d = (k >> shift) & MASK;
         dst[j] = gbase[d] + (q - lbase[d]);
         if (q < nvalid) io.kout[dst[j]] = k;
     }
@@ -845,11 +875,17 @@ void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t 
     }
 }
 
-template <int NP>
-void launch_scatter(const SortIO &io, uint32_t n, int shift, const uint32_t *counts, uint32_t nblk,
-                    const uint32_t *totals, hipStream_t stream) {
-    DLRM_LAUNCH("radix_scatter", k_radix_scatter<NP>, dim3(nblk), dim3(256), 0, stream, io, n, shift, counts,
-                       nblk, totals);
+template <int RB>
+void launch_radix_pass(const SortIO &io, int NP, uint32_t n, int shift, uint32_t *counts,
+                       uint32_t nblk, uint32_t *totals, hipStream_t stream) {
+    DLRM_LAUNCH("radix_hist", k_radix_hist<RB>, dim3(nblk), dim3(256), 0, stream, io.kin, n, shift, counts, nblk);
+    DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(1 << RB), dim3(256), 0, stream, counts, nblk, totals);
+    if (NP == 3)
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
+    else
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
 }
 
 }  // namespace
@@ -928,10 +964,13 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     ea.nbags = static_cast<uint32_t>(T * B);
     DLRM_LAUNCH("expand", k_expand, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
-    // K5: passes over the significant bits of the largest key (sumV - 1)
+    // K5: passes over the significant bits of the largest key (sumV - 1), digits of 8..10 bits
+    // chosen for the fewest passes
     int bits = 0;
     while (bits < 32 && ((sumV - 1) >> bits) != 0) ++bits;
-    const int passes = (bits + 7) / 8;
+    const int passes = (bits + 9) / 10;
+    int rb = passes > 0 ? (bits + passes - 1) / passes : 8;
+    if (rb < 8) rb = 8;
     int cur = 0;
     uint32_t *counts = u32(L.counts), *totals = u32(L.totals);
     for (int p = 0; p < passes; ++p) {
@@ -945,10 +984,9 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
         io.pout[1] = u32(L.grow[cur ^ 1]);
         io.pin[2] = u32(L.wgt[cur]);
         io.pout[2] = u32(L.wgt[cur ^ 1]);
-        DLRM_LAUNCH("radix_hist", k_radix_hist, dim3(L.nblk), dim3(256), 0, stream, io.kin, n, 8 * p, counts, L.nblk);
-        DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(256), dim3(256), 0, stream, counts, L.nblk, totals);
-        if (NP == 3) launch_scatter<3>(io, n, 8 * p, counts, L.nblk, totals, stream);
-        else launch_scatter<2>(io, n, 8 * p, counts, L.nblk, totals, stream);
+        if (rb == 8) launch_radix_pass<8>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
+        else if (rb == 9) launch_radix_pass<9>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
+        else launch_radix_pass<10>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
         cur ^= 1;
     }
     const uint32_t *skeys = u32(L.keys[cur]);

@@ -269,9 +269,12 @@ def test_adagrad_random(D, dtype, weighted):
                 label="random")
 
 
-@pytest.mark.parametrize("rows,label", [([200], "1 pass"), ([300, 300], "2 passes"),
-                                        ([70000, 5], "3 passes"), ([(1 << 24) + 5], "4 passes"),
-                                        ([1], "0 passes")])
+@pytest.mark.parametrize("rows,label", [([200], "8-bit keys: 1 pass of 8"),
+                                        ([300, 300], "10-bit keys: 1 pass of 10"),
+                                        ([70000, 5], "17-bit keys: 2 passes of 9"),
+                                        ([(1 << 20) + 7], "21-bit keys: 3 passes of 8"),
+                                        ([(1 << 24) + 5], "25-bit keys: 3 passes of 9"),
+                                        ([1], "one row: no pass")])
 def test_adagrad_sort_passes(rows, label):
     run_adagrad(rows, 4, "f32", 1500, "multi", True, seed=len(rows) + rows[0] % 97, max_len=10,
                 random_state=True, label=label)

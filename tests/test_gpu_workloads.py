@@ -167,3 +167,32 @@ def test_workload_training_step():
     say(f"   Adagrad U={U} worst row rel err {worst:.3e}")
     del tabs, states
     torch.cuda.empty_cache()
+
+
+def test_adagrad_wide_keys():
+    """30-bit keys (2^29 + 12345 rows): three sort passes of 10-bit digits, checked on every lookup."""
+    from recommendation_model_sparse_amd.synth import Workload
+    V = (1 << 29) + 12345
+    wl = Workload(name="wide-keys", seed=777, T=1, D=4, dtype="f32", B=4096, rows=[V], init="hash",
+                  bags="geom", bag_lo=1, bag_hi=8, bag_mean=3.0, dist="uniform")
+    b = wl.batch(0, weighted=True)
+    say(f"[adagrad] wide keys V={V} nnz={b.nnz}")
+    tabs = device_tables(wl)
+    states = [torch.zeros(V, dtype=torch.float32, device=DEV)]
+    gp = (np.random.default_rng(5).standard_normal((wl.B, 1, wl.D)) * 1e-3).astype(np.float32)
+    outs = AdagradOutputs(b.nnz, DEV)
+    emb_bag_bwd_adagrad(tabs, states, to_dev(b.indices), to_dev(b.offsets), to_dev(b.weights),
+                        to_dev(gp), wl.lr, wl.eps, outputs=outs)
+    torch.cuda.synchronize()
+    sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
+    r = oracle.emb_bag_bwd_adagrad(subset_tables(wl, row_ids), [np.zeros(len(row_ids[0]), np.float32)],
+                                   sub.indices, sub.offsets, sub.weights, wl.B, gp, wl.lr, wl.eps)
+    U = int(outs.num_unique.item())
+    assert U == r.U
+    assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
+    assert np.array_equal(outs.segment_offsets.cpu().numpy()[:U + 1], r.seg_offsets)
+    assert np.array_equal(outs.unique_keys.cpu().numpy()[:U], row_ids[0][r.unique_keys])
+    got = tabs[0][torch.from_numpy(row_ids[0][r.unique_keys]).to(DEV)].cpu().numpy().astype(np.float64)
+    assert row_inf_rel(got, r.new_rows) <= 1e-4
+    del tabs, states
+    torch.cuda.empty_cache()
