@@ -26,6 +26,34 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_multihot_bf16.md")
+
+
+def measured_traffic(kernel: str, workload: str, path: str = TRAFFIC_PROFILE, root: str = ROOT):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when the summary is
+    missing, covers another workload, or the kernel's sources changed since it was taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(path) if l.startswith("traffic-json: "))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line[len("traffic-json: "):])
+    e = rec.get("kernels", {}).get(kernel)
+    if rec.get("workload") != workload or e is None:
+        return None
+    h = hashlib.sha256()
+    for f in e["sources"]:
+        h.update(f.encode())
+        h.update(b"\0")
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != e["source_sha256"]:
+        return None
+    return {"bytes": e["read_bytes"] + e["write_bytes"], "read": e["read_bytes"],
+            "write": e["write_bytes"]}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -197,6 +225,7 @@ def main():
     k1_s = call_ms["emb_bag_fwd"] / 1e3
     gathered_gbps = gathered / k1_s / 1e9
 
+    traffic = measured_traffic(dominant, "multihot-bf16-" + args.dist)
     res = {
         "metric": "samples/sec + gathered-embedding GB/s (fraction of HBM peak), 1 MI355X",
         "value": wl.B / (ms / 1e3),
@@ -224,7 +253,9 @@ def main():
         "kernel_ms_per_step": kern_ms,
         "roofline": {"bound": "hbm", "kernel": dominant,
                      "achieved": dom["GBps"] if dom else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom["frac_hbm_peak"] if dom else None, "traffic": None,
+                     "frac": dom["frac_hbm_peak"] if dom else None,
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "ms_per_launch": kern_launch_ms[dominant],
                      "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
         "kernels": kernels,

@@ -7,22 +7,24 @@
 //   K4  expand: for lookup j of bag (t, b): key_j = rowbase[t] + idx_j, and the payloads
 //       pos_j = j, grow_j = b*T + t (the row of grad_pooled it reads) and, when weighted,
 //       w_j.  One block per 256 bags; bag offsets and bag rows staged in LDS.
-//   K5  stable LSD radix sort of the keys carrying the payloads, 8-bit digits,
-//       ceil(bits(sum V - 1)/8) passes.  Per pass: per-tile digit histograms, a per-digit
-//       scan across tiles, and a scatter that ranks each key inside its tile with wavefront
-//       ballots (stable: ties keep their order).
+//   K5  stable LSD radix sort of the keys carrying the payloads.  Keys of `bits` bits take
+//       ceil(bits/10) passes of equal digits of max(8, ceil(bits/passes)) bits (25-bit keys:
+//       3 passes of 9 bits).  Per pass: per-tile digit histograms, a per-digit scan across
+//       tiles, and a scatter that ranks each key inside its tile with wavefront ballots
+//       (stable: ties keep their order) and writes the tile out in runs of equal digits.
 //   K6  unique keys and segment offsets (flag = key differs from its predecessor; a scan of
-//       the flags), written only when the caller asks for them.
+//       the flags), and for every K7 chunk the segment of its last position.  Always run: K7b
+//       reads the segment ends; the caller's output buffers receive them when given.
 //   K7  chunked segment reduction fused with the update.  The sorted sequence is cut into
-//       chunks of G positions (G = D/W lanes, W = 4 fp32 columns per lane); a lane group walks
-//       its chunk in order with U gradient rows in flight, summing w * grad_pooled rows.  A
-//       segment inside one chunk is finished on the spot: row-wise Adagrad on the table row
-//       and state prefetched with the gradient rows.  A segment that crosses chunk boundaries
-//       leaves one partial sum per chunk (slot A: the piece that began in an earlier chunk,
-//       slot B: the piece that runs past the chunk), and K7b finishes each such segment with
-//       a whole wavefront: it finds the segment's last chunk by galloping search, adds the
-//       partials in chunk order and applies the update.  Every sum has a fixed order, so the
-//       update is bitwise reproducible; no atomics.
+//       chunks of CS positions, one per lane group of G = D/W lanes (W fp32 columns per lane);
+//       a group walks its chunk in order with U gradient rows in flight, summing
+//       w * grad_pooled rows.  A segment inside one chunk is finished on the spot: row-wise
+//       Adagrad on the table row and state prefetched with the gradient rows.  A segment that
+//       crosses chunk boundaries leaves one partial sum per chunk (slot A: the piece that began
+//       in an earlier chunk, slot B: the piece that runs past the chunk) and its first chunk is
+//       queued on a worklist; K7b takes each listed segment with a whole block, reads its end
+//       from the segment offsets, adds the partials in chunk order and applies the update.
+//       Every sum has a fixed order, so the update is bitwise reproducible; no float atomics.
 #include "common.h"
 
 namespace dlrm {

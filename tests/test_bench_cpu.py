@@ -1,0 +1,60 @@
+"""bench.py host logic without a GPU: the multi-GPU refusal and the source-checked HBM traffic figure."""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def write_profile(tmp_path, src_rel, digest, workload="multihot-bf16-zipf"):
+    rec = {"workload": workload, "kernels": {"seg_reduce_adagrad": {
+        "dispatches": 3, "read_bytes": 1000, "write_bytes": 24, "sources": [src_rel], "source_sha256": digest}}}
+    p = tmp_path / "hbm.md"
+    p.write_text("# summary\n\n```\ntraffic-json: " + json.dumps(rec) + "\n```\n")
+    return str(p)
+
+
+def digest_of(rel, data):
+    h = hashlib.sha256()
+    h.update(rel.encode())
+    h.update(b"\0")
+    h.update(data)
+    return h.hexdigest()
+
+
+def test_traffic_used_only_for_unchanged_sources(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"kernel v1\n")
+    prof = write_profile(tmp_path, "k.hip", digest_of("k.hip", b"kernel v1\n"))
+    got = bench.measured_traffic("seg_reduce_adagrad", "multihot-bf16-zipf", prof, str(tmp_path))
+    assert got == {"bytes": 1024, "read": 1000, "write": 24}
+    # another workload, another kernel: no figure
+    assert bench.measured_traffic("seg_reduce_adagrad", "multihot-bf16-uniform", prof, str(tmp_path)) is None
+    assert bench.measured_traffic("pool_wave_per_bag", "multihot-bf16-zipf", prof, str(tmp_path)) is None
+    # the kernel changed since the counters were taken: no figure
+    src.write_bytes(b"kernel v2\n")
+    assert bench.measured_traffic("seg_reduce_adagrad", "multihot-bf16-zipf", prof, str(tmp_path)) is None
+    # no summary at all
+    assert bench.measured_traffic("seg_reduce_adagrad", "multihot-bf16-zipf", str(tmp_path / "none.md"),
+                                  str(tmp_path)) is None
+
+
+def test_committed_profile_is_well_formed():
+    line = next(l for l in open(bench.TRAFFIC_PROFILE) if l.startswith("traffic-json: "))
+    rec = json.loads(line[len("traffic-json: "):])
+    assert rec["workload"] == "multihot-bf16-zipf"
+    for name, e in rec["kernels"].items():
+        assert e["read_bytes"] >= 0 and e["write_bytes"] >= 0 and e["dispatches"] > 0
+        for f in e["sources"]:
+            assert os.path.exists(os.path.join(ROOT, f)), f
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
