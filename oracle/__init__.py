@@ -45,10 +45,11 @@ def lib():
         p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.oracle_emb_bag_fwd.argtypes = [i32, i32, i32, p, p, p, p, p, i64, p, p, i32]
         L.oracle_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p, i32]
+        L.oracle_emb_interact_fwd.argtypes = [i32, i32, i32, p, p, p, p, p, i64, p, p, p, i32]
         L.oracle_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p, p, i32]
         L.oracle_emb_bag_bwd_adagrad.argtypes = [i32, i32, i32, p, p, p, p, p, p, i64, i64, p,
                                                  f32, f32, p, p, p, p, p, p]
-        for f in (L.oracle_emb_bag_fwd, L.oracle_interact_fwd, L.oracle_interact_bwd,
+        for f in (L.oracle_emb_bag_fwd, L.oracle_interact_fwd, L.oracle_emb_interact_fwd, L.oracle_interact_bwd,
                   L.oracle_emb_bag_bwd_adagrad):
             f.restype = ctypes.c_int
         _lib = L
@@ -102,6 +103,28 @@ def interact_fwd(dense: np.ndarray, pooled: np.ndarray, threads: int = 0):
     mag = np.zeros((B, P + D), dtype=np.float64)
     _check(lib().oracle_interact_fwd(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out), _ptr(mag),
                                      threads), "interact_fwd")
+    return out, mag
+
+
+def emb_interact_fwd(tables: Sequence[np.ndarray], indices: np.ndarray, offsets: np.ndarray,
+                     weights: Optional[np.ndarray], B: int, dense: np.ndarray, threads: int = 0):
+    """Lookup fused with the interaction: [B, N(N-1)/2 + D] (fp64, pooled rows unrounded) and
+    its error scale.  N = T + 1."""
+    dtype, arrs, ptrs, rows = _tables(tables)
+    T, D = len(arrs), arrs[0].shape[1]
+    indices = np.ascontiguousarray(indices, dtype=np.int64)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    w = None if weights is None else np.ascontiguousarray(weights, dtype=np.float32)
+    dense = np.ascontiguousarray(dense, dtype=np.float32)
+    if dense.shape != (B, D):
+        raise ValueError("dense must be [B, D]")
+    N = T + 1
+    P = N * (N - 1) // 2
+    out = np.zeros((B, P + D), dtype=np.float64)
+    mag = np.zeros((B, P + D), dtype=np.float64)
+    _check(lib().oracle_emb_interact_fwd(T, D, dtype, ptrs, _ptr(rows), _ptr(indices), _ptr(offsets),
+                                         _ptr(w), B, _ptr(dense), _ptr(out), _ptr(mag), threads),
+           "emb_interact_fwd")
     return out, mag
 
 

@@ -172,6 +172,86 @@ int oracle_interact_fwd(const float *dense, const float *pooled, int64_t B, int3
 }
 
 /*
+ * Lookup fused with the interaction: the stages (2)-(4) of [P5] "Forward pass"
+ * applied in sequence to one sample, the pooled vectors going straight into the
+ * pairwise dots.  The value is the definition of the two stages composed; the
+ * pooled rows are kept in fp64 (no rounding between the stages).
+ *
+ *   x_0 = dense_b,  x_{t+1}[d] = sum_{j in bag(t,b)} w_j * E_t[idx_j][d]
+ *   out[b] = [ <x_i,x_j> for i < j row by row, dense_b[0..D-1] ]
+ *   abs_out[b][p] = sum_d a_i[d] * a_j[d], with a_0 = |dense_b| and
+ *                   a_{t+1}[d] = sum_j |w_j| |E_t[idx_j][d]|
+ *
+ * abs_out is the sum of the absolute values of every product w_k E_k[d] w_l E_l[d]
+ * the dot expands into; the dense part of abs_out is |dense|.
+ */
+int oracle_emb_interact_fwd(int32_t T, int32_t D, int32_t dtype, const void *const *tables,
+                            const int64_t *rows, const int64_t *indices, const int64_t *offsets,
+                            const float *weights, int64_t B, const float *dense, double *out,
+                            double *abs_out, int32_t nthreads) {
+    if (T <= 0 || D <= 0 || B < 0 || !tables || !rows || !offsets || !dense || !out)
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_ERR_ARG;
+    int rc = check_csr(T, rows, indices, offsets, B);
+    if (rc) return rc;
+    const int N = T + 1;
+    const int64_t P = (int64_t)N * (N - 1) / 2, W = P + D;
+    int nt = threads_or_default(nthreads);
+    int failed = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double *x = malloc(sizeof(double) * (size_t)N * D);
+        double *a = malloc(sizeof(double) * (size_t)N * D);
+        if (!x || !a) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t b = 0; b < B; ++b) {
+            if (!x || !a) continue;
+            for (int d = 0; d < D; ++d) {
+                x[d] = (double)dense[b * D + d];
+                a[d] = fabs(x[d]);
+            }
+            for (int t = 0; t < T; ++t) {
+                int64_t bag = (int64_t)t * B + b;
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t j = offsets[bag]; j < offsets[bag + 1]; ++j) {
+                        double w = weights ? (double)weights[j] : 1.0;
+                        double e = table_value(tables[t], dtype, indices[j], D, d);
+                        acc += w * e;
+                        mag += fabs(w) * fabs(e);
+                    }
+                    x[(int64_t)(t + 1) * D + d] = acc;
+                    a[(int64_t)(t + 1) * D + d] = mag;
+                }
+            }
+            int64_t p = 0;
+            for (int i = 0; i < N; ++i) {
+                for (int j = i + 1; j < N; ++j) {
+                    double z = 0.0, mag = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        z += x[(int64_t)i * D + d] * x[(int64_t)j * D + d];
+                        mag += a[(int64_t)i * D + d] * a[(int64_t)j * D + d];
+                    }
+                    out[b * W + p] = z;
+                    if (abs_out) abs_out[b * W + p] = mag;
+                    ++p;
+                }
+            }
+            for (int d = 0; d < D; ++d) {
+                out[b * W + P + d] = x[d];
+                if (abs_out) abs_out[b * W + P + d] = a[d];
+            }
+        }
+        free(x);
+        free(a);
+    }
+    return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/*
  * Dot-product interaction, backward.  The pages give only the forward map and
  * say training runs gradient descent on it ([P5] training sentence), so this
  * is its derivative: with g the upstream gradient of out[b],

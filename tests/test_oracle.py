@@ -187,6 +187,98 @@ def test_interact_closed_forms():
 
 # ---------------------------------------------------------------- interaction bwd
 
+# ---------------------------------------------------------------- lookup fused with the interaction
+
+def test_emb_interact_hand_example():
+    g = GOLD["emb_interact_fwd"]
+    tabs = [np.array(t, dtype=np.float32) for t in g["tables"]]
+    idx = np.array(g["indices"], dtype=np.int64)
+    off = np.array(g["offsets"], dtype=np.int64)
+    w = np.array(g["weights"], dtype=np.float32)
+    dense = np.array(g["dense"], dtype=np.float32)
+    out, _ = oracle.emb_interact_fwd(tabs, idx, off, None, 1, dense)
+    assert np.array_equal(out, np.array(g["sum"], dtype=np.float64))
+    out, mag = oracle.emb_interact_fwd(tabs, idx, off, w, 1, dense)
+    assert np.array_equal(out, np.array(g["weighted"], dtype=np.float64))
+    assert np.array_equal(mag, np.array(g["weighted_scale"], dtype=np.float64))
+
+
+def torch_emb_interact(tables, idx, off, w, B, dense):
+    """torch.nn.functional.embedding_bag per table, then torch.bmm, in fp64; value and scale."""
+    T, D = len(tables), tables[0].shape[1]
+    N = T + 1
+    xs, axs = [torch.from_numpy(dense.astype(np.float64))], [torch.from_numpy(np.abs(dense.astype(np.float64)))]
+    for t in range(T):
+        lo, hi = off[t * B], off[(t + 1) * B]
+        ti = torch.from_numpy(idx[lo:hi])
+        to = torch.from_numpy(off[t * B:(t + 1) * B] - lo)
+        tw = None if w is None else torch.from_numpy(w[lo:hi].astype(np.float64))
+        E = torch.from_numpy(as_f64(tables[t]))
+        xs.append(torch.nn.functional.embedding_bag(ti, E, to, mode="sum", per_sample_weights=tw))
+        aw = None if tw is None else tw.abs()
+        axs.append(torch.nn.functional.embedding_bag(ti, E.abs(), to, mode="sum", per_sample_weights=aw))
+    X = torch.stack(xs, 1)
+    A = torch.stack(axs, 1)
+    iu = torch.triu_indices(N, N, 1)
+    Z = torch.bmm(X, X.transpose(1, 2).contiguous())[:, iu[0], iu[1]]
+    S = torch.bmm(A, A.transpose(1, 2).contiguous())[:, iu[0], iu[1]]
+    return (torch.cat([Z, X[:, 0]], 1).numpy(), torch.cat([S, A[:, 0]], 1).numpy())
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_emb_interact_vs_torch(weighted, dtype):
+    T, V, D, B = 5, 31, 16, 19
+    tables, idx, off, w = rand_problem(21, T, V, D, B, 6, weighted, dtype)
+    dense = np.random.default_rng(22).standard_normal((B, D)).astype(np.float32)
+    out, mag = oracle.emb_interact_fwd(tables, idx, off, w, B, dense)
+    ref, rmag = torch_emb_interact(tables, idx, off, w, B, dense)
+    assert out.shape == (B, (T + 1) * T // 2 + D)
+    assert np.all(np.abs(out - ref) <= 1e-13 * mag + 1e-300)
+    assert np.allclose(mag, rmag, rtol=1e-13, atol=0)
+
+
+def test_emb_interact_against_the_two_stages():
+    """Unweighted one-hot fp32 bags pool exactly, so the fused value equals the two stages run
+    in turn; for multi-hot bags the two differ only by the fp32 rounding of the pooled rows,
+    at most (2u + u^2) * scale with u = 2^-24."""
+    T, V, D, B = 4, 40, 12, 25
+    tables, _, _, _ = rand_problem(23, T, V, D, B, 1, False)
+    rng = np.random.default_rng(24)
+    dense = rng.standard_normal((B, D)).astype(np.float32)
+    idx = rng.integers(0, V, T * B).astype(np.int64)
+    off = np.arange(T * B + 1, dtype=np.int64)
+    fused, _ = oracle.emb_interact_fwd(tables, idx, off, None, B, dense)
+    pooled, _ = oracle.emb_bag_fwd(tables, idx, off, None, B)
+    two, _ = oracle.interact_fwd(dense, pooled.astype(np.float32))
+    assert np.array_equal(fused, two)
+
+    tables, idx, off, w = rand_problem(25, T, V, D, B, 9, True)
+    fused, mag = oracle.emb_interact_fwd(tables, idx, off, w, B, dense)
+    pooled, _ = oracle.emb_bag_fwd(tables, idx, off, w, B)
+    two, _ = oracle.interact_fwd(dense, pooled.astype(np.float32))
+    u = 2.0 ** -24
+    assert np.all(np.abs(fused - two) <= (2 * u + u * u) * mag * (1 + 1e-12) + 1e-300)
+    assert np.any(fused != two)  # the rounding between the stages is really skipped
+
+
+def test_emb_interact_empty_bags_and_preconditions():
+    T, D, B = 3, 4, 2
+    tab = np.ones((5, D), dtype=np.float32)
+    dense = np.full((B, D), 2.0, dtype=np.float32)
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    out, mag = oracle.emb_interact_fwd([tab] * T, np.zeros(0, dtype=np.int64), off, None, B, dense)
+    P = (T + 1) * T // 2
+    assert np.all(out[:, :P] == 0) and np.all(mag[:, :P] == 0)
+    assert np.all(out[:, P:] == 2.0)
+    with pytest.raises(oracle.OracleError):
+        oracle.emb_interact_fwd([tab], np.array([5], dtype=np.int64), np.array([0, 1]), None, 1,
+                                np.zeros((1, D), np.float32))
+    with pytest.raises(ValueError):
+        oracle.emb_interact_fwd([tab], np.array([0], dtype=np.int64), np.array([0, 1]), None, 1,
+                                np.zeros((2, D), np.float32))
+
+
 def test_interact_bwd_hand_example():
     g = GOLD["interact_bwd"]
     gd, gp, _, _ = oracle.interact_bwd(np.array(g["grad_out"], np.float32), np.array(g["dense"], np.float32),
