@@ -82,6 +82,85 @@ def cpu_baseline(wl, batch, n_samples: int):
                       f"(pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s"}
 
 
+def time_inference(tabs, batches, steps, pooled, inter):
+    """Mean ms of emb_bag_interact_fwd and of emb_bag_fwd + dlrm_interact_fwd (HIP events)."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
+
+    def fused(b):
+        emb_bag_interact_fwd(tabs, b["idx"], b["off"], None, b["dense"], out=inter)
+
+    def two(b):
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+        dlrm_interact_fwd(b["dense"], pooled, out=inter)
+
+    res = {}
+    for name, fn in (("fused", fused), ("two_call", two)):
+        for i in range(3):
+            fn(batches[i % len(batches)])
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            fn(batches[i % len(batches)])
+        ev[1].record()
+        torch.cuda.synchronize()
+        res[name] = ev[0].elapsed_time(ev[1]) / steps
+    return res
+
+
+def inference_summary(inf, wl, nnz_avg):
+    D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
+    alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
+    f = inf["fused"] / 1e3
+    return {"fused_ms": inf["fused"], "two_call_ms": inf["two_call"],
+            "fused_samples_per_s": B / f, "two_call_samples_per_s": B / (inf["two_call"] / 1e3),
+            "speedup": inf["two_call"] / inf["fused"],
+            "fused_algorithmic_bytes": alg, "fused_GBps": alg / f / 1e9,
+            "fused_frac_hbm_peak": alg / f / 1e9 / HBM_PEAK_GBPS,
+            "gathered_GBps": nnz_avg * D * wl.elem_size / f / 1e9}
+
+
+def bench_inference_big(args, dev):
+    """Inference on one GPU's share of 8 x 50M-row bf16 tables (102.4 GB), one-hot, B=65536."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
+    from recommendation_model_sparse_amd.configs import make_config
+
+    wl = make_config(4)
+    if args.dist == "zipf":
+        wl = wl.with_(dist="zipf", alpha=1.2)
+    log(f"[bench] workload {wl.name} ({args.dist})")
+    tabs = []
+    for t, v in enumerate(wl.rows):
+        x = torch.empty((v, wl.D), dtype=torch.bfloat16, device=dev)
+        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
+        tabs.append(x)
+    batches = []
+    for i in range(args.rotate):
+        b = wl.batch(i)
+        batches.append(dict(idx=torch.from_numpy(b.indices).to(dev), off=torch.from_numpy(b.offsets).to(dev),
+                            dense=torch.from_numpy(b.dense).to(dev), nnz=b.nnz))
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    inf = time_inference(tabs, batches, args.steps, pooled, inter)
+    nnz_avg = float(np.mean([b["nnz"] for b in batches]))
+    summ = inference_summary(inf, wl, nnz_avg)
+    res = {
+        "metric": "inference samples/sec (lookup fused with the interaction), 1 MI355X",
+        "value": summ["fused_samples_per_s"], "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": 3, "ms_per_step": inf["fused"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 tables, fp32 accumulation",
+        "data": f"synthetic (seeded; counter-hash tables, {'Zipf(1.2)' if args.dist == 'zipf' else 'uniform'} rows)",
+        "config": {"workload": "one-hot inference: 8 bf16 tables of 50M x 128 (102.4 GB), B=65536, N=9",
+                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_GB": wl.table_bytes() / 1e9,
+                   "parallelism": "single GPU"},
+        "inference": summ,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +173,10 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--dist", choices=["zipf", "uniform"], default="zipf",
                     help="row distribution of the lookups (uniform: a cache-cold control)")
+    ap.add_argument("--workload", choices=["multihot", "onehot-big"], default="multihot",
+                    help="multihot: the training step (default); onehot-big: inference only "
+                         "(fused lookup + interaction against the two calls) on 8 x 50M-row "
+                         "bf16 tables, B=65536 one-hot, uniform or --dist zipf (Zipf 1.2)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
@@ -116,6 +199,8 @@ def main():
     from recommendation_model_sparse_amd.configs import make_config
 
     dev = torch.device("cuda:0")
+    if args.workload == "onehot-big":
+        return bench_inference_big(args, dev)
     wl = make_config(3)
     if args.dist == "uniform":
         wl = wl.with_(dist="uniform")
@@ -199,6 +284,9 @@ def main():
     log("[bench] per kernel (ms/step): " + ", ".join(f"{k}={v:.4f}" for k, v in
                                                      sorted(kern_ms.items(), key=lambda x: -x[1])))
 
+    # inference: the fused lookup + interaction against the two calls, same batches and tables
+    inf = time_inference(tabs, batches, args.steps, pooled, inter)
+
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     U_last = int(outs.num_unique.item())
     es = wl.elem_size
@@ -259,6 +347,7 @@ def main():
                      "ms_per_launch": kern_launch_ms[dominant],
                      "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
         "kernels": kernels,
+        "inference": inference_summary(inf, wl, nnz_avg),
     }
     if not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")

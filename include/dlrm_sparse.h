@@ -127,6 +127,26 @@ int dlrm_interact_bwd(const float *grad_out, const float *dense, const float *po
                       int32_t N, int32_t D, float *grad_dense, float *grad_pooled,
                       dlrm_stream_t stream);
 
+/*
+ * Lookup fused with the interaction, for inference ([P5] "Forward pass" stages (2)-(4) in
+ * sequence: the pooled vectors of a sample go straight into the pairwise dots and the
+ * concatenation).  Computes exactly dlrm_interact_fwd(dense, emb_bag_fwd(...)) -- the same
+ * pooling and the same matrix-core arithmetic, so the bits are identical -- without writing
+ * the pooled [B][T][D] array: each sample's N = T + 1 vectors are kept on chip.
+ *
+ *   tables, rows, T, D, dtype, indices, offsets, per_sample_weights, B, nnz: as emb_bag_fwd
+ *   dense [B][D] fp32, 16-byte aligned
+ *   out   [B][N(N-1)/2 + D] fp32: the strict upper triangle of X X^T row by row, then dense
+ *   flags: DLRM_FLAG_CHECK_INDICES as for emb_bag_fwd (the check borrows 4 bytes of out)
+ *   Limits: D % 16 == 0 and D*sizeof(elem) in {64, 128, 256, 512, 1024} bytes (fp32 D in
+ *   {16..256}, bf16 D in {32..512}); one sample's X, N*(D+4)*4 bytes, plus the bags' offsets
+ *   must fit in 64 KiB (DLRM_ERR_UNSUPPORTED otherwise; use the two calls).
+ */
+int emb_bag_interact_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                         int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                         const float *per_sample_weights, int64_t B, int64_t nnz,
+                         const float *dense, float *out, uint32_t flags, dlrm_stream_t stream);
+
 /* Bytes of device workspace emb_bag_bwd_adagrad needs for these sizes
  * (0 on invalid sizes).  rows is a host array of T row counts. */
 size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int32_t D, int64_t B,

@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     emb_bag_bwd_adagrad,
     emb_bag_bwd_workspace_size,
     emb_bag_fwd,
+    emb_bag_interact_fwd,
 )

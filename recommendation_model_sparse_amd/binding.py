@@ -40,6 +40,7 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t)
         L.emb_bag_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, u32, p]
         L.dlrm_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p]
+        L.emb_bag_interact_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, p, u32, p]
         L.dlrm_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.emb_bag_bwd_workspace_size.argtypes = [i32, p, i32, i64, i64]
         L.emb_bag_bwd_workspace_size.restype = sz
@@ -50,7 +51,7 @@ def lib() -> ctypes.CDLL:
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
         L.dlrm_trace_enable.argtypes = [ctypes.c_int]
         L.dlrm_trace_read.argtypes = [i32, p, p, p, p]
-        for f in (L.emb_bag_fwd, L.dlrm_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
+        for f in (L.emb_bag_fwd, L.dlrm_interact_fwd, L.emb_bag_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
                   L.dlrm_synth_fill_table, L.dlrm_trace_enable, L.dlrm_trace_read):
             f.restype = ctypes.c_int
         _lib = L
@@ -138,6 +139,28 @@ def dlrm_interact_fwd(dense: torch.Tensor, pooled: torch.Tensor,
         out = torch.empty((B, P + D), dtype=torch.float32, device=dense.device)
     _check(lib().dlrm_interact_fwd(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out),
                                    _stream(dense.device)), "dlrm_interact_fwd")
+    return out
+
+
+def emb_bag_interact_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: torch.Tensor,
+                         per_sample_weights: Optional[torch.Tensor], dense: torch.Tensor,
+                         out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """[B, N(N-1)/2 + D] fp32, N = T + 1: lookup fused with the interaction (C: emb_bag_interact_fwd)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    indices = _contig(indices, torch.int64, "indices")
+    offsets = _contig(offsets, torch.int64, "offsets")
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    dense = _contig(dense, torch.float32, "dense")
+    B = (offsets.numel() - 1) // T
+    if offsets.numel() != T * B + 1 or tuple(dense.shape) != (B, D):
+        raise ValueError("offsets must have T*B+1 entries and dense must be [B, D]")
+    N = T + 1
+    dev = tables[0].device
+    if out is None:
+        out = torch.empty((B, N * (N - 1) // 2 + D), dtype=torch.float32, device=dev)
+    _check(lib().emb_bag_interact_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
+                                      indices.numel(), _ptr(dense), _ptr(out), flags, _stream(dev)),
+           "emb_bag_interact_fwd")
     return out
 
 

@@ -36,6 +36,13 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));  // MFMA 16x16 accumulator fragment
+
+// Position of pair (i, j), i < j, in the row-major strict upper triangle of an N x N matrix.
+__device__ __forceinline__ int triu_pos(int i, int j, int N) {
+    return i * N - (i * (i + 1)) / 2 + (j - i - 1);
+}
+
 // Loads and stores through the global address space (pointers staged in LDS would otherwise be
 // generic/flat, and flat loads also count against the LDS wait counter).
 #define DLRM_GLOBAL __attribute__((address_space(1)))

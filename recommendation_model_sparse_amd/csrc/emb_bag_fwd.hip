@@ -17,6 +17,7 @@
 //   - fp32 accumulation in a fixed order: results are bitwise reproducible; a bag of one row
 //     returns that row exactly.
 #include "common.h"
+#include "pool.h"
 
 namespace dlrm {
 namespace {
@@ -34,48 +35,6 @@ struct PoolArgs {
     uint32_t row_bytes;
     uint32_t nblocks;  // blocks launched (a multiple of 8)
 };
-
-template <int DT>
-struct Elem;
-template <>
-struct Elem<DLRM_F32> {
-    static constexpr int kPerChunk = 4;
-};
-template <>
-struct Elem<DLRM_BF16> {
-    static constexpr int kPerChunk = 8;
-};
-
-// acc += w * (16-byte chunk widened to fp32)
-template <int DT, bool WEIGHTED>
-__device__ __forceinline__ void accumulate(float *acc, const uint4 &v, float w) {
-    if constexpr (DT == DLRM_F32) {
-        const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                            __uint_as_float(v.w)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = WEIGHTED ? fmaf(w, x[e], acc[e]) : acc[e] + x[e];
-    } else {
-        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = bf16_lo(q[e]), hi = bf16_hi(q[e]);
-            acc[2 * e] = WEIGHTED ? fmaf(w, lo, acc[2 * e]) : acc[2 * e] + lo;
-            acc[2 * e + 1] = WEIGHTED ? fmaf(w, hi, acc[2 * e + 1]) : acc[2 * e + 1] + hi;
-        }
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ void store_chunk(float *dst, const float *acc) {
-    constexpr int EPC = Elem<DT>::kPerChunk;
-#pragma unroll
-    for (int e = 0; e < EPC; e += 4)
-        *reinterpret_cast<float4 *>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-}
-
-__device__ __forceinline__ uint4 load_row_chunk(const char *tab, int64_t idx, uint32_t row_bytes) {
-    return *reinterpret_cast<const uint4 *>(tab + static_cast<uint64_t>(idx) * row_bytes);
-}
 
 // One wavefront per bag (multi-hot).  G lanes per row, NG = 64/G groups, U rows per group in flight.
 template <int DT, int G, bool WEIGHTED>

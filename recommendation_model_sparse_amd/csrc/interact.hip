@@ -22,12 +22,6 @@
 namespace dlrm {
 namespace {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int triu_pos(int i, int j, int N) {  // i < j
-    return i * N - (i * (i + 1)) / 2 + (j - i - 1);
-}
-
 __device__ __forceinline__ const float *x_row(const float *dense, const float *pooled, uint32_t b,
                                               int N, int D, int i) {
     return i == 0 ? dense + static_cast<uint64_t>(b) * D

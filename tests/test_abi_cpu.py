@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"emb_bag_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
+    assert {"emb_bag_fwd", "emb_bag_interact_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
             "emb_bag_bwd_adagrad", "dlrm_status_string", "dlrm_synth_fill_table",
             "dlrm_trace_enable", "dlrm_trace_read"} <= names
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
@@ -93,6 +93,27 @@ def test_emb_bag_fwd_rejects(L):
     assert fwd(L, B=0, nnz=3) == INVALID
     assert fwd(L, B=0, nnz=0) == OK            # nothing to do, nothing launched
     assert fwd(L, B=1 << 30, T=2, tables=ptrs(FAKE, FAKE), rows=i64s(1, 1)) == UNSUPPORTED
+
+
+def fused(L, T=2, D=32, dtype=0, rows=None, tables=None, dense=FAKE, out=FAKE, B=4, nnz=4, flags=0):
+    tables = ptrs(*[FAKE] * T) if tables is None else tables
+    rows = i64s(*([10] * T)) if rows is None else rows
+    return L.emb_bag_interact_fwd(tables, rows, T, D, dtype, FAKE, FAKE, None, B, nnz, dense, out, flags, None)
+
+
+def test_emb_bag_interact_fwd_rejects(L):
+    assert fused(L, T=0) == INVALID
+    assert fused(L, D=48) == UNSUPPORTED            # 192-byte rows: not a power-of-two chunk count
+    assert fused(L, D=8) == UNSUPPORTED             # D % 16
+    assert fused(L, D=16, dtype=1) == UNSUPPORTED   # 32-byte bf16 rows
+    assert fused(L, D=512) == UNSUPPORTED           # 2 KiB fp32 rows
+    assert fused(L, T=64, D=256) == UNSUPPORTED     # X of one sample over 64 KiB
+    assert fused(L, dense=0) == INVALID
+    assert fused(L, dense=FAKE + 4) == INVALID
+    assert fused(L, out=0) == INVALID
+    assert fused(L, flags=4) == INVALID
+    assert fused(L, B=0, nnz=1) == INVALID
+    assert fused(L, B=0, nnz=0) == OK
 
 
 def test_interact_rejects(L):

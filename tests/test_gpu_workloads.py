@@ -18,6 +18,7 @@ from recommendation_model_sparse_amd import (
     dlrm_synth_fill_table,
     emb_bag_bwd_adagrad,
     emb_bag_fwd,
+    emb_bag_interact_fwd,
     synth,
 )
 from recommendation_model_sparse_amd.configs import make_config
@@ -60,7 +61,10 @@ def check_forward(wl, batch, tabs, n_samples=256):
     dense = to_dev(batch.dense)
     pooled = emb_bag_fwd(tabs, di, do, dw)
     inter = dlrm_interact_fwd(dense, pooled)
+    fused = emb_bag_interact_fwd(tabs, di, do, dw, dense)
     torch.cuda.synchronize()
+    # the fused inference call runs the same arithmetic without the pooled round trip
+    assert torch.equal(fused.view(torch.int32), inter.view(torch.int32)), "fused != two-call path"
     S = sample_rows(wl.B, n_samples, wl.seed)
     sub_wl, sub, row_ids = batch.sample_subset(S)
     host_tabs = subset_tables(wl, row_ids)
