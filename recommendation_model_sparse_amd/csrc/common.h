@@ -31,6 +31,12 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t bid, uint32_t nblock
     return (bid % kNumXcd) * per + bid / kNumXcd;
 }
 
+// Index of this wavefront in its block, as a wave-uniform (scalar) value: the compiler cannot see
+// that threadIdx.x >> 6 is uniform, and would otherwise do per-sample address math per lane.
+__device__ __forceinline__ uint32_t wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const uint32_t lane = __lane_id();
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));

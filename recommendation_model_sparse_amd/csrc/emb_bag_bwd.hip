@@ -133,7 +133,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
 // Exclusive scan over a 256-thread block; every thread must call it.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *total) {
     __shared__ uint32_t ws[4];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = static_cast<int>(wave_id()), lane = threadIdx.x & 63;
     const uint32_t inc = wave_inclusive_scan(v);
     if (lane == 63) ws[w] = inc;
     __syncthreads();
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     __shared__ uint32_t lbase[NBK];  // start of digit d inside the block's sorted tile
     __shared__ uint32_t wcnt[4][NBK];
     __shared__ uint32_t stage[kSortTile];
-    const int tid = threadIdx.x, w = tid >> 6;
+    const int tid = threadIdx.x, w = static_cast<int>(wave_id());
     {
         // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
         uint32_t tv[K], sum = 0;
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
                                                    int64_t *__restrict__ seg_offsets,
                                                    uint32_t *__restrict__ chunk_seg, uint32_t CS) {
     __shared__ uint32_t wtot[4];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = static_cast<int>(wave_id()), lane = tid & 63;
     const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + lane;
     uint64_t masks[kSortItems];
     uint32_t wsum = 0;
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     __shared__ PosMeta meta[4][NG][CS];
     __shared__ TableLDS sl;
     stage_tables(a, sl);
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane / G, c = lane % G;
+    const int wv = static_cast<int>(wave_id()), lane = threadIdx.x & 63, grp = lane / G, c = lane % G;
     const uint32_t chunk = (blockIdx.x * 4 + wv) * NG + grp;
     if (chunk >= a.nchunk) return;  // group-uniform
     const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n), cnt = hi - lo;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     constexpr int EPC = Elem<DT>::kPerChunk;
     constexpr int U = 8;
     const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
-    const uint32_t bag = lb * 4 + (threadIdx.x >> 6);
+    const uint32_t bag = lb * 4 + wave_id();
     if (bag >= a.nbags) return;
     const int lane = threadIdx.x & 63;
     const int grp = lane / G, c = lane % G;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
     constexpr int NG = kWave / G;
     constexpr int EPC = Elem<DT>::kPerChunk;
     const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
-    const uint32_t wave = lb * 4 + (threadIdx.x >> 6);
+    const uint32_t wave = lb * 4 + wave_id();
     const int lane = threadIdx.x & 63;
     const int grp = lane / G, c = lane % G;
     const uint32_t bag0 = wave * (NG * BPG) + grp;

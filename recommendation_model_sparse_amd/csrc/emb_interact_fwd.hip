@@ -21,6 +21,7 @@
 // Multi-hot bags: while a wave gathers the rows of one bag it already has the first indices of
 // its next bag in flight, so a bag costs one memory latency rather than two.
 #include "common.h"
+#include "gram.h"
 #include "pool.h"
 
 namespace dlrm {
@@ -47,6 +48,7 @@ struct FusedArgs {
     int32_t S;          // samples per block
     int32_t BPG;        // bags per lane group and pass (group-per-bag pooling)
     uint32_t row_bytes;
+    int32_t ksplit;     // the Gram is the k-split one of gram.h (N <= 11, D in {64, 128, 256})
 };
 
 constexpr int kPad = 4;  // floats of padding per LDS row of X
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
     const int Sb = static_cast<int>(min(static_cast<uint32_t>(S), a.B - b0));
     float *X = smem;
     int64_t *offs = reinterpret_cast<int64_t *>(smem + static_cast<size_t>(S) * N * XS);
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wv = static_cast<int>(wave_id()), lane = tid & 63;
 
     // ---- stage the bags' offsets and the dense rows (row 0 of each X)
     for (int i = tid; i < T * (Sb + 1); i += 256) {
@@ -232,9 +234,31 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
     }
     __syncthreads();
 
+    const int P = a.P, W = P + D;
+    if constexpr (D == 64 || D == 128 || D == 256) {
+        if (a.ksplit) {  // small N: the k-split Gram, one sample per wave
+            constexpr int CPL = D / 64;
+            int pi, pj;
+            gram_pair(lane, pi, pj);
+            for (int s = wv; s < Sb; s += 4) {
+                const float *xs = X + static_cast<size_t>(s) * N * XS + lane * CPL;
+                float x[kGramRows][CPL];
+#pragma unroll
+                for (int i = 0; i < kGramRows; ++i)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) x[i][c] = i < N ? xs[i * XS + c] : 0.f;
+                const float z = gram_ksplit<CPL>(x);
+                if (lane < kGramPairs && pj < N) a.out[(static_cast<uint64_t>(b0) + s) * W + triu_pos(pi, pj, N)] = z;
+            }
+            for (int i = tid; i < Sb * D; i += 256) {
+                const int s = i / D, d = i - s * D;
+                a.out[(static_cast<uint64_t>(b0) + s) * W + P + d] = X[static_cast<size_t>(s) * N * XS + d];
+            }
+            return;
+        }
+    }
     // ---- Gram blocks on the matrix cores; one upper 16 x 16 block per wave and job
     const int r16 = lane & 15, q = lane >> 4;
-    const int P = a.P, W = P + D;
     for (int j = wv; j < Sb * a.NBLK; j += 4) {
         const int s = j / a.NBLK;
         int I, J;
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd_regs(FusedArgs a) {
     constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
     constexpr int TW = PL * ES / 16;  // 16-byte loads per chunk of a table row quarter (1 or 2)
     constexpr int DW = PL / 4;        // 16-byte loads per chunk of a dense row quarter (2)
-    const uint32_t b0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * M;
+    const uint32_t b0 = (blockIdx.x * 4 + wave_id()) * M;
     if (b0 >= a.B) return;
     const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
     const int N = a.N;
@@ -453,6 +477,150 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd_regs(FusedArgs a) {
     }
 }
 
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32), l);
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Short bags, small N (N <= 11, D = 64 * CPL): pooled straight into the k-split Gram of gram.h.
+// Lane l owns columns l*CPL.. of every row of X; lane t < T reads the bounds and first index of
+// bag (t, b), which the wave then takes as uniform values, so each row is one coalesced load
+// whose base is uniform.  The bag's rows are summed in order from zero, as the unfused
+// lane-group-per-bag pooling sums them, and the Gram is the unfused interaction's: the bits
+// match the two-call path.  M samples per wave go through each dependent load step together.
+template <int DT, int CPL, int M, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_emb_interact_fwd_ksplit(FusedArgs a) {
+    constexpr int D = 64 * CPL;
+    constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
+    constexpr int TMAX = kGramRows - 1;
+    const uint32_t b0 = (blockIdx.x * 4 + wave_id()) * M;
+    if (b0 >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int T = a.T, N = a.N;
+    const int64_t *idx_base = a.indices ? a.indices : a.offsets;  // nnz = 0: never read for a value
+
+    // step 1: lane t < T reads the bounds of bag (t, b) for each sample
+    int64_t j0[M], j1[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t b = min(b0 + m, a.B - 1);
+        const int t = lane < T ? lane : T - 1;
+        const uint64_t bag = static_cast<uint64_t>(t) * a.B + b;
+        j0[m] = a.offsets[bag];
+        j1[m] = a.offsets[bag + 1];
+    }
+    // step 2: first index and weight of that bag
+    int64_t idx0[M];
+    float w0[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const bool has = j0[m] < j1[m];
+        idx0[m] = idx_base[has ? j0[m] : 0];
+        if constexpr (WEIGHTED) w0[m] = a.weights[has ? j0[m] : 0];
+        if (!has) idx0[m] = 0;
+    }
+    // step 3: dense rows and the first row of every bag, all in flight together
+    float x[M][kGramRows][CPL];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t b = min(b0 + m, a.B - 1);
+        uint32_t dw[CPL];
+        gload_words<CPL>(a.dense + static_cast<uint64_t>(b) * D + lane * CPL, dw);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) x[m][0][c] = __uint_as_float(dw[c]);
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            const int tt = t < T ? t : T - 1;
+            const int64_t idx = readlane64(idx0[m], tt);
+            const char *row = a.tables[tt] + static_cast<uint64_t>(idx) * a.row_bytes + lane * CPL * ES;
+            float v[CPL];
+            if constexpr (DT == DLRM_BF16) {
+                if constexpr (CPL == 1) {
+                    v[0] = __uint_as_float(static_cast<uint32_t>(*(const DLRM_GLOBAL uint16_t *)row) << 16);
+                } else {
+                    uint32_t h[CPL / 2];
+                    gload_words<CPL / 2>(row, h);
+#pragma unroll
+                    for (int k = 0; k < CPL / 2; ++k) v[2 * k] = bf16_lo(h[k]), v[2 * k + 1] = bf16_hi(h[k]);
+                }
+            } else {
+                uint32_t h[CPL];
+                gload_words<CPL>(row, h);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) v[c] = __uint_as_float(h[c]);
+            }
+            const bool has = t < T && readlane64(j0[m], tt) < readlane64(j1[m], tt);
+            const float w = WEIGHTED ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0[m]), tt)) : 1.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float p = WEIGHTED ? fmaf(w, v[c], 0.f) : 0.f + v[c];
+                x[m][t + 1][c] = has ? p : 0.f;
+            }
+        }
+    }
+    // step 4: the remaining rows of bags with more than one lookup, in order (uniform loops)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t >= T || b0 + m >= a.B) continue;
+            const int64_t s0 = readlane64(j0[m], t), s1 = readlane64(j1[m], t);
+            const char *tab = a.tables[t] + lane * CPL * ES;
+            for (int64_t j = s0 + 1; j < s1; ++j) {
+                const char *row = tab + static_cast<uint64_t>(a.indices[j]) * a.row_bytes;
+                const float w = WEIGHTED ? a.weights[j] : 1.f;
+                float v[CPL];
+                if constexpr (DT == DLRM_BF16) {
+                    if constexpr (CPL == 1) {
+                        v[0] = __uint_as_float(static_cast<uint32_t>(*(const DLRM_GLOBAL uint16_t *)row) << 16);
+                    } else {
+                        uint32_t h[CPL / 2];
+                        gload_words<CPL / 2>(row, h);
+#pragma unroll
+                        for (int k = 0; k < CPL / 2; ++k) v[2 * k] = bf16_lo(h[k]), v[2 * k + 1] = bf16_hi(h[k]);
+                    }
+                } else {
+                    uint32_t h[CPL];
+                    gload_words<CPL>(row, h);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) v[c] = __uint_as_float(h[c]);
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    x[m][t + 1][c] = WEIGHTED ? fmaf(w, v[c], x[m][t + 1][c]) : x[m][t + 1][c] + v[c];
+            }
+        }
+    // step 5: the Gram and [triu | dense]
+    int pi, pj;
+    gram_pair(lane, pi, pj);
+    const int P = a.P;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t b = b0 + m;
+        if (b >= a.B) break;  // wave-uniform
+        const float z = gram_ksplit<CPL>(x[m]);
+        float *orow = a.out + static_cast<uint64_t>(b) * (P + D);
+        if (lane < kGramPairs && pj < N) orow[triu_pos(pi, pj, N)] = z;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) orow[P + lane * CPL + c] = x[m][0][c];
+    }
+}
+
+template <int DT>
+void dispatch_ksplit(const FusedArgs &a, int D, bool weighted, hipStream_t stream) {
+#define DLRM_KSPLIT(CPL, M)                                                                                         \
+    do {                                                                                                            \
+        const dim3 grid(static_cast<uint32_t>((a.B + 4 * (M) - 1) / (4 * (M)))), block(256);                       \
+        if (weighted) DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, CPL, M, true>), grid, block, 0, stream, a); \
+        else DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, CPL, M, false>), grid, block, 0, stream, a); \
+    } while (0)
+    if (D == 64) DLRM_KSPLIT(1, DLRM_FUSED_M);
+    else if (D == 128) DLRM_KSPLIT(2, DLRM_FUSED_M);
+    else DLRM_KSPLIT(4, 1);
+#undef DLRM_KSPLIT
+}
+
 // The register path for D = KC * NCH and NB row blocks (NB * D <= 256); M samples per wave.
 template <int DT, int NB>
 bool dispatch_regs(const FusedArgs &a, int D, bool weighted, hipStream_t stream) {
@@ -553,7 +721,13 @@ extern "C" int emb_bag_interact_fwd(const void *const *tables, const int64_t *ro
     a.row_bytes = row_bytes;
     // the same kernel choice as emb_bag_fwd: a wavefront per bag for 4+ lookups per bag on average
     const bool wpb = nnz >= 4 * static_cast<int64_t>(T) * B;
-    const bool weighted = per_sample_weights != nullptr;
+    const bool weighted = per_sample_weights != nullptr && nnz > 0;  // no lookup: nothing to weigh
+    a.ksplit = gram_ksplit_ok(N, D) ? 1 : 0;
+    if (!wpb && a.ksplit) {  // short bags, small N: pooled straight into the k-split Gram
+        if (dtype == DLRM_F32) dispatch_ksplit<DLRM_F32>(a, D, weighted, stream);
+        else dispatch_ksplit<DLRM_BF16>(a, D, weighted, stream);
+        return launch_status();
+    }
     if (!wpb && a.NB <= 2 && a.NB * D <= 256) {  // short bags, X fits in registers: no LDS, no barriers
         const bool ok = dtype == DLRM_F32
                             ? (a.NB == 1 ? dispatch_regs<DLRM_F32, 1>(a, D, weighted, stream)

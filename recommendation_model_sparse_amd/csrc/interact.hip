@@ -18,6 +18,7 @@
 // X in registers, G sits in LDS and is read with broadcast loads, and dX[i][d] = sum_j G[i][j]
 // X[j][d] is a register FMA chain.  Reads X once and writes dX once: HBM-bound.
 #include "common.h"
+#include "gram.h"
 
 namespace dlrm {
 namespace {
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void k_interact_fwd_mfma(const float *__restri
     constexpr int D = KC * NCH;
     constexpr int PL = KC / 4;  // floats per lane per chunk
     constexpr int NBLK = NB * (NB + 1) / 2;
-    const uint32_t sample = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint32_t sample = blockIdx.x * 4 + wave_id();
     if (sample >= B) return;
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, q = lane >> 4;
@@ -132,6 +133,45 @@ __global__ __launch_bounds__(256) void k_interact_fwd_valu(const float *__restri
     for (int d = threadIdx.x; d < D; d += blockDim.x) orow[P + d] = dsrc[d];
 }
 
+// Small interactions (N <= 11, D = 64 * CPL): the k-split Gram (gram.h), M samples per wave.
+// Lane l loads columns l*CPL.. of every row (each row read is one coalesced load), and every
+// load is unconditional (rows past N re-read row N-1 and are zeroed) so all are in flight at once.
+template <int CPL, int M>
+__global__ __launch_bounds__(256) void k_interact_fwd_ksplit(const float *__restrict__ dense,
+                                                             const float *__restrict__ pooled,
+                                                             float *__restrict__ out, uint32_t B,
+                                                             int N, int P) {
+    constexpr int D = 64 * CPL;
+    const uint32_t b0 = (blockIdx.x * 4 + wave_id()) * M;
+    if (b0 >= B) return;
+    const int lane = threadIdx.x & 63;
+    float x[M][kGramRows][CPL];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t b = min(b0 + m, B - 1);
+#pragma unroll
+        for (int i = 0; i < kGramRows; ++i) {
+            const int ii = i < N ? i : N - 1;
+            uint32_t w[CPL];
+            gload_words<CPL>(x_row(dense, pooled, b, N, D, ii) + lane * CPL, w);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) x[m][i][c] = i < N ? __uint_as_float(w[c]) : 0.f;
+        }
+    }
+    int pi, pj;
+    gram_pair(lane, pi, pj);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t b = b0 + m;
+        if (b >= B) break;  // wave-uniform
+        const float z = gram_ksplit<CPL>(x[m]);
+        float *orow = out + static_cast<uint64_t>(b) * (P + D);
+        if (lane < kGramPairs && pj < N) orow[triu_pos(pi, pj, N)] = z;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) orow[P + lane * CPL + c] = x[m][0][c];
+    }
+}
+
 // Backward.  NP = padded N (multiple of 4, >= N); CPL = columns per lane (1 or 2).
 template <int NP, int CPL>
 __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ grad_out,
@@ -141,7 +181,7 @@ __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ 
                                                       float *__restrict__ grad_pooled, uint32_t B,
                                                       int N, int D, int P, int slices) {
     __shared__ float Gs[4][NP][NP];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = static_cast<int>(wave_id()), lane = threadIdx.x & 63;
     const uint64_t gw = static_cast<uint64_t>(blockIdx.x) * 4 + wv;
     const uint32_t sample = static_cast<uint32_t>(gw / slices);
     const int slice = static_cast<int>(gw % slices);
@@ -260,6 +300,14 @@ extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_
     const int P = N * (N - 1) / 2;
     const uint32_t b = static_cast<uint32_t>(B);
     bool done = false;
+    if (gram_ksplit_ok(N, D)) {
+        switch (D) {
+            case 64: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<1, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+            case 128: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<2, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+            default: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<4, 1>), dim3((b + 3) / 4), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+        }
+        return launch_status();
+    }
     switch ((N + 15) / 16) {
         case 1: done = launch_fwd_mfma<1>(dense, pooled, out, b, N, D, P, stream); break;
         case 2: done = launch_fwd_mfma<2>(dense, pooled, out, b, N, D, P, stream); break;

@@ -48,7 +48,7 @@ def run_fused(tables, idx, off, w, B, dense, label, check_oracle=True):
                                      ("bf16", 32), ("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512)])
 @pytest.mark.parametrize("mode", ["onehot", "multi", "long"])
 @pytest.mark.parametrize("weighted", [False, True])
-@pytest.mark.parametrize("T", [3, 26])
+@pytest.mark.parametrize("T", [3, 10, 26])
 def test_fused_random(dtype, D, mode, weighted, T):
     rng = np.random.default_rng(zlib.crc32(f"fused-{dtype}-{D}-{mode}-{weighted}-{T}".encode()))
     B = 37  # not a multiple of the samples per block
@@ -60,6 +60,18 @@ def test_fused_random(dtype, D, mode, weighted, T):
     got = run_fused(tables, idx, off, w, B, dense, mode)
     P = (T + 1) * T // 2
     assert np.array_equal(got[:, P:], dense)
+
+
+def test_fused_empty_batch_with_weights():
+    """nnz = 0 with a weights tensor: every pooled row is zero, the weights are never read."""
+    rng = np.random.default_rng(34)
+    for T, D in [(3, 128), (10, 64), (26, 128)]:
+        tables = random_tables(rng, [7] * T, D, "bf16")
+        idx, off, _ = random_csr(rng, T, 5, [7] * T, "empty")
+        w = np.zeros(0, np.float32)
+        dense = rng.standard_normal((5, D)).astype(np.float32)
+        got = run_fused(tables, idx, off, w, 5, dense, "empty-weighted")
+        assert np.all(got[:, :(T + 1) * T // 2] == 0)
 
 
 def test_fused_short_bags_group_mode():
