@@ -49,7 +49,9 @@ def lib():
         L.oracle_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p, p, i32]
         L.oracle_emb_bag_bwd_adagrad.argtypes = [i32, i32, i32, p, p, p, p, p, p, i64, i64, p,
                                                  f32, f32, p, p, p, p, p, p]
-        for f in (L.oracle_emb_bag_fwd, L.oracle_interact_fwd, L.oracle_emb_interact_fwd, L.oracle_interact_bwd,
+        L.oracle_emb_bag_bwd_sgd.argtypes = [i32, i32, i32, p, p, p, p, p, i64, i64, p, f32,
+                                             p, p, p, p, p]
+        for f in (L.oracle_emb_bag_bwd_sgd, L.oracle_emb_bag_fwd, L.oracle_interact_fwd, L.oracle_emb_interact_fwd, L.oracle_interact_bwd,
                   L.oracle_emb_bag_bwd_adagrad):
             f.restype = ctypes.c_int
         _lib = L
@@ -192,6 +194,33 @@ def emb_bag_bwd_adagrad(tables: Sequence[np.ndarray], states: Sequence[np.ndarra
     np.cumsum(rows, out=rowbase[1:])
     return AdagradResult(uk[:U].copy(), so[:U + 1].copy(), pm[:nnz].copy(), nr[:U].copy(),
                          ns[:U].copy(), rowbase)
+
+
+def emb_bag_bwd_sgd(tables: Sequence[np.ndarray], indices: np.ndarray, offsets: np.ndarray,
+                    weights: Optional[np.ndarray], B: int, grad_pooled: np.ndarray,
+                    lr: float) -> AdagradResult:
+    """Plain SGD on the looked-up rows: E[r] - lr * G_r for each unique row (new_state is empty)."""
+    dtype, arrs, ptrs, rows = _tables(tables)
+    T, D = len(arrs), arrs[0].shape[1]
+    indices = np.ascontiguousarray(indices, dtype=np.int64)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    w = None if weights is None else np.ascontiguousarray(weights, dtype=np.float32)
+    g = np.ascontiguousarray(grad_pooled, dtype=np.float32)
+    nnz = int(indices.shape[0])
+    n1 = max(nnz, 1)
+    uk = np.zeros(n1, dtype=np.int64)
+    so = np.zeros(n1 + 1, dtype=np.int64)
+    pm = np.zeros(n1, dtype=np.int32)
+    nu = np.zeros(1, dtype=np.int64)
+    nr = np.zeros((n1, D), dtype=np.float64)
+    _check(lib().oracle_emb_bag_bwd_sgd(
+        T, D, dtype, ptrs, _ptr(rows), _ptr(indices), _ptr(offsets), _ptr(w), B, nnz, _ptr(g),
+        float(lr), _ptr(uk), _ptr(so), _ptr(pm), _ptr(nu), _ptr(nr)), "emb_bag_bwd_sgd")
+    U = int(nu[0])
+    rowbase = np.zeros(T + 1, dtype=np.int64)
+    np.cumsum(rows, out=rowbase[1:])
+    return AdagradResult(uk[:U].copy(), so[:U + 1].copy(), pm[:nnz].copy(), nr[:U].copy(),
+                         np.zeros(0), rowbase)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray, scale: np.ndarray) -> float:

@@ -335,10 +335,10 @@ static int cmp_key_pos(const void *a, const void *b) {
 }
 
 /*
- * Embedding backward with row-wise Adagrad ([P5] training sentence: training
- * uses SGD/Adagrad).  The lookup is linear in the table, so the gradient of a
- * table row is the sum, over every lookup of that row, of the lookup's weight
- * times the pooled gradient of the lookup's bag.
+ * Gradients of the looked-up rows, shared by the two update rules below ([P5]
+ * training sentence: training uses SGD/Adagrad).  The lookup is linear in the
+ * table, so the gradient of a table row is the sum, over every lookup of that
+ * row, of the lookup's weight times the pooled gradient of the lookup's bag.
  *
  * Readings (the pages say nothing more):
  *   - A row's key is rowbase[t] + idx, rowbase the exclusive prefix sum of
@@ -347,37 +347,37 @@ static int cmp_key_pos(const void *a, const void *b) {
  *     sorted position of key u and seg_offsets[U] = nnz.
  *   - G_u[d] = sum over the segment, in ascending sorted position, of
  *     w * grad_pooled[b][t][d] (fp64).
- *   - Row-wise Adagrad with one accumulator per row, updated before the step:
- *         s <- s + (1/D) sum_d G_u[d]^2
- *         E[r][d] <- E[r][d] - lr * G_u[d] / (sqrt(s) + eps)
- *     (Duchi, Hazan & Singer 2011 with the accumulator shared by the row).
  *   - Only rows that appear are updated; each appears once in the output.
  *
- * Outputs are per unique row u (row = unique_keys[u] - rowbase[t]):
- * new_rows[u][d] and new_state[u] in fp64.  The inputs are not modified.
- * Arrays are sized by nnz; only the first U entries (U+1 for seg_offsets) are
- * written.
+ * On success *G_out holds U x D fp64 gradients (caller frees), *t_out and
+ * *r_out the table and row of each unique key.
  */
-int oracle_emb_bag_bwd_adagrad(int32_t T, int32_t D, int32_t dtype, const void *const *tables,
-                               const float *const *states, const int64_t *rows,
-                               const int64_t *indices, const int64_t *offsets, const float *weights,
-                               int64_t B, int64_t nnz, const float *grad_pooled, float lr, float eps,
-                               int64_t *unique_keys, int64_t *seg_offsets, int32_t *perm,
-                               int64_t *num_unique, double *new_rows, double *new_state) {
-    if (T <= 0 || D <= 0 || B < 0 || nnz < 0 || !tables || !states || !rows || !offsets ||
-        !unique_keys || !seg_offsets || !perm || !num_unique || !new_rows || !new_state)
-        return ORACLE_ERR_ARG;
-    if (nnz > 0 && (!indices || !grad_pooled)) return ORACLE_ERR_ARG;
+typedef struct {
+    int64_t U;
+    double *G;   /* [U][D] */
+    int32_t *t;  /* [U] */
+    int64_t *r;  /* [U] */
+} row_grads;
+
+static void free_row_grads(row_grads *g) {
+    free(g->G), free(g->t), free(g->r);
+    g->G = NULL, g->t = NULL, g->r = NULL;
+}
+
+static int gather_row_grads(int32_t T, int32_t D, const int64_t *rows, const int64_t *indices,
+                            const int64_t *offsets, const float *weights, int64_t B, int64_t nnz,
+                            const float *grad_pooled, int64_t *unique_keys, int64_t *seg_offsets,
+                            int32_t *perm, int64_t *num_unique, row_grads *out) {
+    out->G = NULL, out->t = NULL, out->r = NULL, out->U = 0;
     if (offsets[(int64_t)T * B] != nnz) return ORACLE_ERR_OFFSETS;
     int rc = check_csr(T, rows, indices, offsets, B);
     if (rc) return rc;
-
+    size_t n1 = (size_t)(nnz > 0 ? nnz : 1);
     int64_t *rowbase = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T + 1));
-    int64_t *bag_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nnz > 0 ? nnz : 1));
-    key_pos *kp = (key_pos *)malloc(sizeof(key_pos) * (size_t)(nnz > 0 ? nnz : 1));
-    double *G = (double *)malloc(sizeof(double) * (size_t)D);
-    if (!rowbase || !bag_of || !kp || !G) {
-        free(rowbase), free(bag_of), free(kp), free(G);
+    int64_t *bag_of = (int64_t *)malloc(sizeof(int64_t) * n1);
+    key_pos *kp = (key_pos *)malloc(sizeof(key_pos) * n1);
+    if (!rowbase || !bag_of || !kp) {
+        free(rowbase), free(bag_of), free(kp);
         return ORACLE_ERR_NOMEM;
     }
     rowbase[0] = 0;
@@ -405,20 +405,63 @@ int oracle_emb_bag_bwd_adagrad(int32_t T, int32_t D, int32_t dtype, const void *
     seg_offsets[U] = nnz;
     *num_unique = U;
 
+    out->U = U;
+    out->G = (double *)calloc((size_t)(U > 0 ? U : 1) * (size_t)D, sizeof(double));
+    out->t = (int32_t *)malloc(sizeof(int32_t) * (size_t)(U > 0 ? U : 1));
+    out->r = (int64_t *)malloc(sizeof(int64_t) * (size_t)(U > 0 ? U : 1));
+    if (!out->G || !out->t || !out->r) {
+        free_row_grads(out);
+        free(rowbase), free(bag_of), free(kp);
+        return ORACLE_ERR_NOMEM;
+    }
     for (int64_t u = 0; u < U; ++u) {
         int64_t key = unique_keys[u];
         int t = 0;
         while (!(rowbase[t] <= key && key < rowbase[t + 1])) ++t;
-        int64_t r = key - rowbase[t];
-        for (int d = 0; d < D; ++d) G[d] = 0.0;
+        out->t[u] = t;
+        out->r[u] = key - rowbase[t];
+        double *G = out->G + u * (int64_t)D;
         for (int64_t k = seg_offsets[u]; k < seg_offsets[u + 1]; ++k) {
             int64_t j = kp[k].pos;
-            int64_t bag = bag_of[j];
-            int64_t b = bag % B;
+            int64_t b = bag_of[j] % B;
             double w = weights ? (double)weights[j] : 1.0;
-            for (int d = 0; d < D; ++d)
-                G[d] += w * (double)grad_pooled[(b * T + t) * (int64_t)D + d];
+            for (int d = 0; d < D; ++d) G[d] += w * (double)grad_pooled[(b * T + t) * (int64_t)D + d];
         }
+    }
+    free(rowbase), free(bag_of), free(kp);
+    return ORACLE_OK;
+}
+
+/*
+ * Embedding backward with row-wise Adagrad: the row gradients above, then one
+ * accumulator per row, updated before the step:
+ *         s <- s + (1/D) sum_d G_u[d]^2
+ *         E[r][d] <- E[r][d] - lr * G_u[d] / (sqrt(s) + eps)
+ * (Duchi, Hazan & Singer 2011 with the accumulator shared by the row).
+ *
+ * Outputs are per unique row u (row = unique_keys[u] - rowbase[t]):
+ * new_rows[u][d] and new_state[u] in fp64.  The inputs are not modified.
+ * Arrays are sized by nnz; only the first U entries (U+1 for seg_offsets) are
+ * written.
+ */
+int oracle_emb_bag_bwd_adagrad(int32_t T, int32_t D, int32_t dtype, const void *const *tables,
+                               const float *const *states, const int64_t *rows,
+                               const int64_t *indices, const int64_t *offsets, const float *weights,
+                               int64_t B, int64_t nnz, const float *grad_pooled, float lr, float eps,
+                               int64_t *unique_keys, int64_t *seg_offsets, int32_t *perm,
+                               int64_t *num_unique, double *new_rows, double *new_state) {
+    if (T <= 0 || D <= 0 || B < 0 || nnz < 0 || !tables || !states || !rows || !offsets ||
+        !unique_keys || !seg_offsets || !perm || !num_unique || !new_rows || !new_state)
+        return ORACLE_ERR_ARG;
+    if (nnz > 0 && (!indices || !grad_pooled)) return ORACLE_ERR_ARG;
+    row_grads g;
+    int rc = gather_row_grads(T, D, rows, indices, offsets, weights, B, nnz, grad_pooled, unique_keys,
+                              seg_offsets, perm, num_unique, &g);
+    if (rc) return rc;
+    for (int64_t u = 0; u < g.U; ++u) {
+        const double *G = g.G + u * (int64_t)D;
+        int t = g.t[u];
+        int64_t r = g.r[u];
         double m = 0.0;
         for (int d = 0; d < D; ++d) m += G[d] * G[d];
         m /= (double)D;
@@ -426,9 +469,36 @@ int oracle_emb_bag_bwd_adagrad(int32_t T, int32_t D, int32_t dtype, const void *
         new_state[u] = s;
         double denom = sqrt(s) + (double)eps;
         for (int d = 0; d < D; ++d)
-            new_rows[u * (int64_t)D + d] =
-                table_value(tables[t], dtype, r, D, d) - (double)lr * G[d] / denom;
+            new_rows[u * (int64_t)D + d] = table_value(tables[t], dtype, r, D, d) - (double)lr * G[d] / denom;
     }
-    free(rowbase), free(bag_of), free(kp), free(G);
+    free_row_grads(&g);
+    return ORACLE_OK;
+}
+
+/*
+ * Embedding backward with plain SGD ([P5] training sentence names SGD): the
+ * row gradients above, then for each unique row
+ *         E[r][d] <- E[r][d] - lr * G_u[d]
+ * Outputs as for Adagrad (no state).
+ */
+int oracle_emb_bag_bwd_sgd(int32_t T, int32_t D, int32_t dtype, const void *const *tables,
+                           const int64_t *rows, const int64_t *indices, const int64_t *offsets,
+                           const float *weights, int64_t B, int64_t nnz, const float *grad_pooled,
+                           float lr, int64_t *unique_keys, int64_t *seg_offsets, int32_t *perm,
+                           int64_t *num_unique, double *new_rows) {
+    if (T <= 0 || D <= 0 || B < 0 || nnz < 0 || !tables || !rows || !offsets || !unique_keys ||
+        !seg_offsets || !perm || !num_unique || !new_rows)
+        return ORACLE_ERR_ARG;
+    if (nnz > 0 && (!indices || !grad_pooled)) return ORACLE_ERR_ARG;
+    row_grads g;
+    int rc = gather_row_grads(T, D, rows, indices, offsets, weights, B, nnz, grad_pooled, unique_keys,
+                              seg_offsets, perm, num_unique, &g);
+    if (rc) return rc;
+    for (int64_t u = 0; u < g.U; ++u) {
+        const double *G = g.G + u * (int64_t)D;
+        for (int d = 0; d < D; ++d)
+            new_rows[u * (int64_t)D + d] = table_value(tables[g.t[u]], dtype, g.r[u], D, d) - (double)lr * G[d];
+    }
+    free_row_grads(&g);
     return ORACLE_OK;
 }

@@ -474,6 +474,68 @@ def test_adagrad_empty():
 
 # ---------------------------------------------------------------- error measure
 
+# ---------------------------------------------------------------- backward + SGD
+
+def test_sgd_hand_example():
+    g, h = GOLD["adagrad"], GOLD["sgd"]
+    tables = [np.array(t, dtype=np.float32) for t in g["tables"]]
+    idx = np.array(g["indices"], dtype=np.int64)
+    off = np.array(g["offsets"], dtype=np.int64)
+    gp = np.array(g["grad_pooled"], dtype=np.float32)
+    lr = float(np.float32(0.01))
+    assert lr == h["lr"]
+    for key, w in (("unweighted", None), ("weighted", np.array(g["weights"], dtype=np.float32))):
+        r = oracle.emb_bag_bwd_sgd(tables, idx, off, w, 2, gp, lr)
+        assert np.array_equal(r.unique_keys, g["unique_keys"])
+        assert np.array_equal(r.seg_offsets, g["seg_offsets"])
+        assert np.array_equal(r.perm, g["perm"])
+        assert np.allclose(r.new_rows, np.array(h[key]), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sgd_vs_torch_optim(weighted, dtype):
+    """Autograd through torch embedding_bag (fp64) with loss <pooled, grad_pooled>, then
+    torch.optim.SGD on the dense tables: the rows the batch touched must match."""
+    T, V, D, B = 3, 25, 6, 17
+    tables, idx, off, w = rand_problem(41, T, V, D, B, 7, weighted, dtype)
+    gp = np.random.default_rng(42).standard_normal((B, T, D)).astype(np.float32)
+    lr = float(np.float32(0.05))
+    r = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, lr)
+    params = [torch.nn.Parameter(torch.from_numpy(as_f64(t))) for t in tables]
+    opt = torch.optim.SGD(params, lr=lr)
+    loss = 0.0
+    for t in range(T):
+        lo, hi = off[t * B], off[(t + 1) * B]
+        tw = None if w is None else torch.from_numpy(w[lo:hi].astype(np.float64))
+        pooled = torch.nn.functional.embedding_bag(torch.from_numpy(idx[lo:hi]), params[t],
+                                                   torch.from_numpy(off[t * B:(t + 1) * B] - lo),
+                                                   mode="sum", per_sample_weights=tw)
+        loss = loss + (pooled * torch.from_numpy(gp[:, t, :].astype(np.float64))).sum()
+    loss.backward()
+    opt.step()
+    tt, rr = r.table_and_row()
+    for u in range(r.U):
+        ref = params[tt[u]].detach().numpy()[rr[u]]
+        assert np.allclose(r.new_rows[u], ref, rtol=1e-13, atol=1e-15)
+    # every touched row is in the output, and nothing else
+    touched = {(t, int(i)) for t in range(T) for i in idx[off[t * B]:off[(t + 1) * B]]}
+    assert touched == {(int(a), int(b)) for a, b in zip(tt, rr)}
+
+
+def test_sgd_step_scales_with_lr():
+    T, V, D, B = 2, 30, 4, 11
+    tables, idx, off, w = rand_problem(43, T, V, D, B, 5, True)
+    gp = np.random.default_rng(44).standard_normal((B, T, D)).astype(np.float32)
+    r1 = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, 0.125)
+    r2 = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, 0.25)
+    tt, rr = r1.table_and_row()
+    old = np.stack([as_f64(tables[t])[r] for t, r in zip(tt, rr)])
+    assert np.allclose(r2.new_rows - old, 2 * (r1.new_rows - old), rtol=1e-12, atol=1e-15)
+    r0 = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, 0.0)
+    assert np.array_equal(r0.new_rows, old)
+
+
 def test_rel_err():
     ref = np.array([1.0, 0.0, -2.0])
     scale = np.array([1.0, 0.0, 4.0])
