@@ -52,8 +52,15 @@ extern "C" {
 /* Same type as hipStream_t. */
 typedef struct ihipStream_t *dlrm_stream_t;
 
-/* Table element type.  bf16 values are the upper 16 bits of an fp32. */
+/* Table element type (and pooled output type of emb_bag_fwd_ex).  bf16 values are the upper
+ * 16 bits of an fp32. */
 typedef enum { DLRM_F32 = 0, DLRM_BF16 = 1 } dlrm_dtype;
+
+/* Integer type of indices and offsets (the *_ex / *_update calls). */
+typedef enum { DLRM_INDEX_I64 = 0, DLRM_INDEX_I32 = 1 } dlrm_index_type;
+
+/* Update rule of emb_bag_bwd_update. */
+typedef enum { DLRM_OPT_ADAGRAD = 0, DLRM_OPT_SGD = 1 } dlrm_optimizer;
 
 enum {
     DLRM_OK = 0,
@@ -91,6 +98,20 @@ int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32
                 int32_t dtype, const int64_t *indices, const int64_t *offsets,
                 const float *per_sample_weights, int64_t B, int64_t nnz, float *out,
                 uint32_t flags, dlrm_stream_t stream);
+
+/*
+ * emb_bag_fwd with a choice of index type and pooled output type.
+ *   indices, offsets: int64 (DLRM_INDEX_I64) or int32 (DLRM_INDEX_I32), same type for both,
+ *                     aligned to their size
+ *   out: [B][T][D] of out_dtype: DLRM_F32, or DLRM_BF16 = the fp32 pooled value rounded to
+ *        nearest even (halves the output bytes); 16-byte aligned
+ * Everything else as emb_bag_fwd, which is emb_bag_fwd_ex(..., DLRM_INDEX_I64, ..., DLRM_F32).
+ * The pooled sums are the same fp32 values for both index types.
+ */
+int emb_bag_fwd_ex(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                   int32_t dtype, const void *indices, const void *offsets, int32_t index_type,
+                   const float *per_sample_weights, int64_t B, int64_t nnz, void *out,
+                   int32_t out_dtype, uint32_t flags, dlrm_stream_t stream);
 
 /*
  * Dot-product interaction, forward ([P5] stage (3) and the interaction
@@ -191,6 +212,24 @@ int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t 
                         size_t workspace_bytes, int64_t *unique_keys_out,
                         int64_t *segment_offsets_out, int32_t *sorted_pos_out,
                         int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream);
+
+/*
+ * Embedding backward with a choice of update rule and index type ([P5] training sentence: SGD
+ * or Adagrad).  The row gradients G are emb_bag_bwd_adagrad's (same sort, segments and fixed
+ * summation order), then for each touched row:
+ *   DLRM_OPT_ADAGRAD: the row-wise Adagrad step of emb_bag_bwd_adagrad (state required);
+ *   DLRM_OPT_SGD:     E[r,d] <- E[r,d] - lr * G[d]   (state may be NULL; eps is ignored).
+ *   indices, offsets: index_type as in emb_bag_fwd_ex.
+ * Everything else as emb_bag_bwd_adagrad, which is
+ * emb_bag_bwd_update(..., DLRM_INDEX_I64, ..., DLRM_OPT_ADAGRAD, ...).
+ */
+int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
+                       int32_t D, int32_t dtype, const void *indices, const void *offsets,
+                       int32_t index_type, const float *per_sample_weights, int64_t B, int64_t nnz,
+                       const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                       void *workspace, size_t workspace_bytes, int64_t *unique_keys_out,
+                       int64_t *segment_offsets_out, int32_t *sorted_pos_out,
+                       int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream);
 
 /* Static description of a status code. */
 const char *dlrm_status_string(int status);

@@ -8,6 +8,10 @@ from .binding import (  # noqa: F401
     DLRM_BF16,
     DLRM_F32,
     DLRM_FLAG_CHECK_INDICES,
+    DLRM_INDEX_I32,
+    DLRM_INDEX_I64,
+    DLRM_OPT_ADAGRAD,
+    DLRM_OPT_SGD,
     AdagradOutputs,
     DlrmError,
     dlrm_interact_bwd,
@@ -17,7 +21,9 @@ from .binding import (  # noqa: F401
     dlrm_trace_enable,
     dlrm_trace_read,
     emb_bag_bwd_adagrad,
+    emb_bag_bwd_update,
     emb_bag_bwd_workspace_size,
     emb_bag_fwd,
+    emb_bag_fwd_ex,
     emb_bag_interact_fwd,
 )

@@ -17,6 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdlrm_sparse.so")
 
 DLRM_F32, DLRM_BF16 = 0, 1
+DLRM_INDEX_I64, DLRM_INDEX_I32 = 0, 1
+DLRM_OPT_ADAGRAD, DLRM_OPT_SGD = 0, 1
 DLRM_FLAG_CHECK_INDICES = 1
 
 _lib = None
@@ -39,6 +41,9 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
                                           ctypes.c_size_t)
         L.emb_bag_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, u32, p]
+        L.emb_bag_fwd_ex.argtypes = [p, p, i32, i32, i32, p, p, i32, p, i64, i64, p, i32, u32, p]
+        L.emb_bag_bwd_update.argtypes = [p, p, p, i32, i32, i32, p, p, i32, p, i64, i64, p, i32, f32, f32,
+                                         p, sz, p, p, p, p, u32, p]
         L.dlrm_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p]
         L.emb_bag_interact_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, p, u32, p]
         L.dlrm_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p]
@@ -51,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
         L.dlrm_trace_enable.argtypes = [ctypes.c_int]
         L.dlrm_trace_read.argtypes = [i32, p, p, p, p]
-        for f in (L.emb_bag_fwd, L.dlrm_interact_fwd, L.emb_bag_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
+        for f in (L.emb_bag_fwd, L.emb_bag_fwd_ex, L.emb_bag_bwd_update, L.dlrm_interact_fwd, L.emb_bag_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
                   L.dlrm_synth_fill_table, L.dlrm_trace_enable, L.dlrm_trace_read):
             f.restype = ctypes.c_int
         _lib = L
@@ -100,6 +105,14 @@ def _tables(tables: Sequence[torch.Tensor]):
     return T, D, code, ptrs, rows
 
 
+def _index_code(indices: torch.Tensor, offsets: torch.Tensor) -> int:
+    if indices.dtype != offsets.dtype or indices.dtype not in (torch.int64, torch.int32):
+        raise ValueError("indices and offsets must both be int64 or both int32")
+    if not (indices.is_contiguous() and offsets.is_contiguous()):
+        raise ValueError("indices and offsets must be contiguous")
+    return DLRM_INDEX_I32 if indices.dtype == torch.int32 else DLRM_INDEX_I64
+
+
 def _contig(t: Optional[torch.Tensor], dtype, name):
     if t is None:
         return None
@@ -124,6 +137,28 @@ def emb_bag_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: 
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     _check(lib().emb_bag_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
                              indices.numel(), _ptr(out), flags, _stream(dev)), "emb_bag_fwd")
+    return out
+
+
+def emb_bag_fwd_ex(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: torch.Tensor,
+                   per_sample_weights: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.float32, flags: int = 0) -> torch.Tensor:
+    """Pooled embeddings [B, T, D] in out_dtype (fp32 or bf16), int64 or int32 indices and
+    offsets (C: emb_bag_fwd_ex)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    icode = _index_code(indices, offsets)
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    ocode = {torch.float32: DLRM_F32, torch.bfloat16: DLRM_BF16}[out_dtype]
+    B = (offsets.numel() - 1) // T
+    if offsets.numel() != T * B + 1:
+        raise ValueError("offsets must have T*B+1 entries")
+    dev = tables[0].device
+    if out is None:
+        out = torch.empty((B, T, D), dtype=out_dtype, device=dev)
+    if out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous of out_dtype")
+    _check(lib().emb_bag_fwd_ex(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B,
+                                indices.numel(), _ptr(out), ocode, flags, _stream(dev)), "emb_bag_fwd_ex")
     return out
 
 
@@ -230,6 +265,42 @@ def emb_bag_bwd_adagrad(tables: Sequence[torch.Tensor], state: Sequence[torch.Te
         _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
         _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
         _stream(dev)), "emb_bag_bwd_adagrad")
+    return o
+
+
+def emb_bag_bwd_update(tables: Sequence[torch.Tensor], state: Optional[Sequence[torch.Tensor]],
+                       indices: torch.Tensor, offsets: torch.Tensor,
+                       per_sample_weights: Optional[torch.Tensor], grad_pooled: torch.Tensor,
+                       optimizer: int, lr: float, eps: float = 0.0,
+                       workspace: Optional[torch.Tensor] = None, outputs: Optional[AdagradOutputs] = None,
+                       flags: int = 0) -> Optional[AdagradOutputs]:
+    """Embedding backward with DLRM_OPT_ADAGRAD (state required) or DLRM_OPT_SGD (state may be
+    None), int64 or int32 indices and offsets (C: emb_bag_bwd_update)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    icode = _index_code(indices, offsets)
+    sptrs = None
+    if state is not None:
+        if len(state) != T:
+            raise ValueError("one state vector per table")
+        for st, t in zip(state, tables):
+            if st.dtype != torch.float32 or st.numel() != t.shape[0] or not st.is_contiguous():
+                raise ValueError("state[t] must be contiguous fp32 [V_t]")
+        sptrs = (ctypes.c_void_p * T)(*[st.data_ptr() for st in state])
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
+    B = (offsets.numel() - 1) // T
+    nnz = indices.numel()
+    dev = tables[0].device
+    need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = outputs
+    _check(lib().emb_bag_bwd_update(
+        ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
+        _ptr(grad_pooled), int(optimizer), float(lr), float(eps), _ptr(workspace), workspace.numel(),
+        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
+        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
+        _stream(dev)), "emb_bag_bwd_update")
     return o
 
 

@@ -115,8 +115,9 @@ inline int launch_status() {
 
 // Shared validation of the CSR batch description (host side, no device access).
 inline int check_batch(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
-                       int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                       int32_t dtype, const void *indices, const void *offsets, int32_t index_type,
                        const float *weights, int64_t B, int64_t nnz) {
+    const uintptr_t ib = index_type == DLRM_INDEX_I32 ? 4 : 8;
     if (T < 1 || T > kMaxTables || D < 1 || B < 0 || nnz < 0) return DLRM_ERR_INVALID_ARG;
     if (dtype != DLRM_F32 && dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
     if (D > 512 || (D * elem_size(dtype)) % 16 != 0) return DLRM_ERR_UNSUPPORTED;
@@ -124,7 +125,7 @@ inline int check_batch(const void *const *tables, const int64_t *rows, int32_t T
         return DLRM_ERR_UNSUPPORTED;
     if (!tables || !rows || !offsets) return DLRM_ERR_INVALID_ARG;
     if (nnz > 0 && !indices) return DLRM_ERR_INVALID_ARG;
-    if (!aligned(offsets, 8) || (indices && !aligned(indices, 8)) || (weights && !aligned(weights, 4)))
+    if (!aligned(offsets, ib) || (indices && !aligned(indices, ib)) || (weights && !aligned(weights, 4)))
         return DLRM_ERR_INVALID_ARG;
     for (int t = 0; t < T; ++t) {
         if (rows[t] < 1) return DLRM_ERR_INVALID_ARG;

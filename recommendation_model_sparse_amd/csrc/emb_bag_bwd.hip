@@ -29,9 +29,8 @@
 
 namespace dlrm {
 
-int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
-                        const int64_t *offsets, int64_t B, int64_t nnz, int *flag,
-                        hipStream_t stream);
+int check_csr_on_device(const int64_t *rows, int32_t T, const void *indices, const void *offsets,
+                        int32_t index_type, int64_t B, int64_t nnz, int *flag, hipStream_t stream);
 
 namespace {
 
@@ -40,9 +39,6 @@ constexpr int kSortTile = 256 * kSortItems;  // keys per sort / segment block
 
 #ifndef DLRM_K7_U
 #define DLRM_K7_U 8  // gradient rows in flight per lane group
-#endif
-#ifndef DLRM_K7_BRANCH_PREFETCH
-#define DLRM_K7_BRANCH_PREFETCH 1  // 1: load table rows only where a segment starts
 #endif
 
 
@@ -152,8 +148,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
 
 struct ExpandArgs {
     uint32_t rowbase[kMaxTables];
-    const int64_t *offsets;
-    const int64_t *indices;
+    const void *offsets;  // int64 or int32 (the kernel's IT)
+    const void *indices;
     const float *weights;
     uint32_t *keys;
     uint32_t *pos;
@@ -164,12 +160,15 @@ struct ExpandArgs {
     uint32_t nbags;
 };
 
+template <typename IT>
 __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
+    const IT *offsets = static_cast<const IT *>(a.offsets);
+    const IT *indices = static_cast<const IT *>(a.indices);
     __shared__ int64_t so[257];
     __shared__ uint32_t s_grow[256], s_base[256];
     const uint32_t g0 = blockIdx.x * 256u;
     const int nb = static_cast<int>(min(256u, a.nbags - g0));
-    for (int i = threadIdx.x; i <= nb; i += 256) so[i] = a.offsets[g0 + i];
+    for (int i = threadIdx.x; i <= nb; i += 256) so[i] = offsets[g0 + i];
     if (static_cast<int>(threadIdx.x) < nb) {
         const uint32_t bag = g0 + threadIdx.x;
         const uint32_t t = bag / a.B, b = bag - t * a.B;
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
             if (so[mid] <= j) lo = mid;
             else hi = mid;
         }
-        a.keys[j] = s_base[lo] + static_cast<uint32_t>(a.indices[j]);
+        a.keys[j] = s_base[lo] + static_cast<uint32_t>(indices[j]);
         a.pos[j] = static_cast<uint32_t>(j);
         a.grow[j] = s_grow[lo];
         if (a.weights) a.wgt[j] = __float_as_uint(a.weights[j]);
@@ -600,12 +599,24 @@ struct TabWords {
     }
 };
 
-// Row-wise Adagrad on one row (the lane's W columns): s += mean(G^2); row -= lr*G/(sqrt(s)+eps).
-// `row` points at the lane's first column of the row, `old` holds those columns as stored.
-template <int DT, int W, int G>
-__device__ __forceinline__ void adagrad_row(const AdagradArgs &a, char *row, float *state, int c,
-                                            const float *g, const uint32_t *old, float old_state) {
+// The update of one row (the lane's W columns).  Row-wise Adagrad: s += mean(G^2);
+// row -= lr*G/(sqrt(s)+eps).  SGD: row -= lr*G (no state).  `row` points at the lane's first
+// column of the row, `old` holds those columns as stored.
+template <int DT, int W, int G, int OPT>
+__device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, float *state, int c,
+                                           const float *g, const uint32_t *old, float old_state) {
     using TW = TabWords<DT, W>;
+    if constexpr (OPT == DLRM_OPT_SGD) {
+        float x[W];
+        TW::to_f32(old, x);
+#pragma unroll
+        for (int e = 0; e < W; ++e) x[e] = fmaf(-a.lr, g[e], x[e]);
+        uint32_t nw[TW::N];
+        TW::from_f32(x, nw);
+        gstore_words<TW::N>(row, nw);
+        (void)state, (void)c, (void)old_state;
+        return;
+    }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < W; ++e) ss = fmaf(g[e], g[e], ss);
@@ -633,7 +644,7 @@ struct PosMeta {
 };
 
 // Chunk of CS = G*MP sorted positions per lane group of G lanes; U gradient rows in flight.
-template <int DT, int W, int G, int MP, bool WEIGHTED, int U>
+template <int DT, int W, int G, int MP, bool WEIGHTED, int U, int OPT>
 __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     using TW = TabWords<DT, W>;
     constexpr int NG = kWave / G;
@@ -666,7 +677,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         PosMeta p;
         p.grad_row = a.grad + static_cast<uint64_t>(grow) * a.D;
         p.tab_row = sl.tab[t] + static_cast<uint64_t>(row) * a.D * ES;
-        p.state = sl.state[t] + row;
+        p.state = OPT == DLRM_OPT_ADAGRAD ? sl.state[t] + row : nullptr;
         p.w = w;
         p.pad = 0;
         if (have) pm[r] = p;
@@ -733,19 +744,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool s_u = (starts >> (r0 + u)) & 1ull;  // bits past cnt are 0
-#if DLRM_K7_BRANCH_PREFETCH
-            if (s_u) {
+            if (s_u) {  // table row and state only where a segment starts
                 gload_words<TW::N>(mu[u].tab_row + c * W * ES, tr[u]);
-                st[u] = *(const DLRM_GLOBAL float *)mu[u].state;
+                st[u] = OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)mu[u].state : 0.f;
             }
-#else
-            const void *tp = s_u ? static_cast<const void *>(mu[u].tab_row + c * W * ES)
-                                 : static_cast<const void *>(mu[u].grad_row + c * W);
-            const void *sp = s_u ? static_cast<const void *>(mu[u].state)
-                                 : static_cast<const void *>(mu[u].grad_row);
-            gload_words<TW::N>(tp, tr[u]);
-            st[u] = *(const DLRM_GLOBAL float *)sp;
-#endif
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
             if ((starts >> r) & 1ull) {
                 if (r > 0) {  // the previous piece ended inside this chunk
                     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-                    else adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+                    else update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
                 }
                 open_before = false;
                 cur_row_ptr = mu[u].tab_row + c * W * ES;
@@ -780,14 +782,14 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         // (list order is arbitrary; each entry's work is fixed, so results do not depend on it)
         if (c == 0) a.fin_list[atomicAdd(a.fin_count, 1u)] = chunk;
     } else {
-        adagrad_row<DT, W, G>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+        update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
     }
 }
 
 // Finishes the chunk-crossing segments: a grid-stride loop over the worklist K7 filled, one
 // listed chunk per block at a time.  The segment's partials are added in chunk order (slot B of
 // its first chunk, then slot A of every later chunk it covers), then the row is updated.
-template <int DT, int W, int G, int CS>
+template <int DT, int W, int G, int CS, int OPT>
 __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
     constexpr int NS = 256 / G;  // partial rows read per pass of the block
     constexpr int U = 8;
@@ -835,8 +837,9 @@ __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
             char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
             uint32_t old[TabWords<DT, W>::N];
             gload_words<TabWords<DT, W>::N>(row, old);
-            adagrad_row<DT, W, G>(a, row, sl.state[t] + r, c, acc, old,
-                                  *(const DLRM_GLOBAL float *)(sl.state[t] + r));
+            float *st = OPT == DLRM_OPT_ADAGRAD ? sl.state[t] + r : nullptr;
+            update_row<DT, W, G, OPT>(a, row, st, c, acc, old,
+                                      OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)st : 0.f);
         }
         __syncthreads();  // red[] is reused by the next item
         (void)lo;
@@ -846,34 +849,35 @@ __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
 template <int G>
 constexpr int chunk_mp() { return G >= 16 ? 64 / G : 4; }
 
-template <int DT, int W, int G>
+template <int DT, int W, int G, int OPT>
 void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
+    constexpr const char *name = OPT == DLRM_OPT_SGD ? "seg_reduce_sgd" : "seg_reduce_adagrad";
     constexpr int NG = kWave / G;
     constexpr int MP = chunk_mp<G>();
     constexpr int U = DLRM_K7_U;
     const uint32_t blocks = (a.nchunk + 4 * NG - 1) / (4 * NG);
     if (weighted)
-        DLRM_LAUNCH("seg_reduce_adagrad", (k_seg_reduce_adagrad<DT, W, G, MP, true, U>), dim3(blocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH(name, (k_seg_reduce_adagrad<DT, W, G, MP, true, U, OPT>), dim3(blocks), dim3(256), 0, stream, a);
     else
-        DLRM_LAUNCH("seg_reduce_adagrad", (k_seg_reduce_adagrad<DT, W, G, MP, false, U>), dim3(blocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH(name, (k_seg_reduce_adagrad<DT, W, G, MP, false, U, OPT>), dim3(blocks), dim3(256), 0, stream, a);
     const uint32_t fin_blocks = a.nchunk < 2048 ? a.nchunk : 2048;
-    DLRM_LAUNCH("seg_finish", (k_seg_finish<DT, W, G, G * MP>), dim3(fin_blocks), dim3(256), 0, stream, a);
+    DLRM_LAUNCH("seg_finish", (k_seg_finish<DT, W, G, G * MP, OPT>), dim3(fin_blocks), dim3(256), 0, stream, a);
 }
 
-template <int DT>
+template <int DT, int OPT>
 void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t stream) {
     if (W == 8) {
-        launch_k7<DT, 8, 64>(a, weighted, stream);
+        launch_k7<DT, 8, 64, OPT>(a, weighted, stream);
         return;
     }
     switch (G) {
-        case 1: launch_k7<DT, 4, 1>(a, weighted, stream); break;
-        case 2: launch_k7<DT, 4, 2>(a, weighted, stream); break;
-        case 4: launch_k7<DT, 4, 4>(a, weighted, stream); break;
-        case 8: launch_k7<DT, 4, 8>(a, weighted, stream); break;
-        case 16: launch_k7<DT, 4, 16>(a, weighted, stream); break;
-        case 32: launch_k7<DT, 4, 32>(a, weighted, stream); break;
-        case 64: launch_k7<DT, 4, 64>(a, weighted, stream); break;
+        case 1: launch_k7<DT, 4, 1, OPT>(a, weighted, stream); break;
+        case 2: launch_k7<DT, 4, 2, OPT>(a, weighted, stream); break;
+        case 4: launch_k7<DT, 4, 4, OPT>(a, weighted, stream); break;
+        case 8: launch_k7<DT, 4, 8, OPT>(a, weighted, stream); break;
+        case 16: launch_k7<DT, 4, 16, OPT>(a, weighted, stream); break;
+        case 32: launch_k7<DT, 4, 32, OPT>(a, weighted, stream); break;
+        case 64: launch_k7<DT, 4, 64, OPT>(a, weighted, stream); break;
     }
 }
 
@@ -901,26 +905,29 @@ extern "C" size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int
     return make_layout(D, nnz).total;
 }
 
-extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows,
-                                   int32_t T, int32_t D, int32_t dtype, const int64_t *indices,
-                                   const int64_t *offsets, const float *per_sample_weights,
-                                   int64_t B, int64_t nnz, const float *grad_pooled, float lr,
-                                   float eps, void *workspace, size_t workspace_bytes,
-                                   int64_t *unique_keys_out, int64_t *segment_offsets_out,
-                                   int32_t *sorted_pos_out, int64_t *num_unique_out,
-                                   uint32_t flags, dlrm_stream_t stream_) {
+extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *rows,
+                                  int32_t T, int32_t D, int32_t dtype, const void *indices,
+                                  const void *offsets, int32_t index_type,
+                                  const float *per_sample_weights, int64_t B, int64_t nnz,
+                                  const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                                  void *workspace, size_t workspace_bytes, int64_t *unique_keys_out,
+                                  int64_t *segment_offsets_out, int32_t *sorted_pos_out,
+                                  int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream_) {
     using namespace dlrm;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (index_type != DLRM_INDEX_I64 && index_type != DLRM_INDEX_I32) return DLRM_ERR_INVALID_ARG;
+    if (optimizer != DLRM_OPT_ADAGRAD && optimizer != DLRM_OPT_SGD) return DLRM_ERR_INVALID_ARG;
     int rc = check_batch(const_cast<const void *const *>(tables), rows, T, D, dtype, indices,
-                         offsets, per_sample_weights, B, nnz);
+                         offsets, index_type, per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     if (flags & ~DLRM_FLAG_CHECK_INDICES) return DLRM_ERR_INVALID_ARG;
     int G, W;
     if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
-    if (!state) return DLRM_ERR_INVALID_ARG;
+    const bool adagrad = optimizer == DLRM_OPT_ADAGRAD;
+    if (adagrad && !state) return DLRM_ERR_INVALID_ARG;
     uint64_t sumV = 0;
     for (int t = 0; t < T; ++t) {
-        if (!state[t] || !aligned(state[t], 4)) return DLRM_ERR_INVALID_ARG;
+        if (adagrad && (!state[t] || !aligned(state[t], 4))) return DLRM_ERR_INVALID_ARG;
         sumV += static_cast<uint64_t>(rows[t]);
     }
     if (sumV > (uint64_t(1) << 32)) return DLRM_ERR_UNSUPPORTED;
@@ -932,7 +939,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
 
     if (flags & DLRM_FLAG_CHECK_INDICES) {
-        rc = check_csr_on_device(rows, T, indices, offsets, B, nnz,
+        rc = check_csr_on_device(rows, T, indices, offsets, index_type, B, nnz,
                                  reinterpret_cast<int *>(ws + L.flag), stream);
         if (rc != DLRM_OK) return rc;
     }
@@ -964,7 +971,10 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     ea.B = static_cast<uint32_t>(B);
     ea.T = static_cast<uint32_t>(T);
     ea.nbags = static_cast<uint32_t>(T * B);
-    DLRM_LAUNCH("expand", k_expand, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
+    if (index_type == DLRM_INDEX_I32)
+        DLRM_LAUNCH("expand", k_expand<int32_t>, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
+    else
+        DLRM_LAUNCH("expand", k_expand<int64_t>, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
     // K5: passes over the significant bits of the largest key (sumV - 1), digits of 8..10 bits
     // chosen for the fewest passes
@@ -1013,7 +1023,7 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     AdagradArgs a{};
     for (int t = 0; t < T; ++t) {
         a.tables[t] = static_cast<char *>(tables[t]);
-        a.state[t] = state[t];
+        a.state[t] = adagrad ? state[t] : nullptr;
         a.rowbase[t] = ea.rowbase[t];
     }
     a.skeys = skeys;
@@ -1034,7 +1044,26 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
     a.lr = lr;
     a.eps = eps;
     a.inv_D = 1.0f / static_cast<float>(D);
-    if (dtype == DLRM_F32) dispatch_k7<DLRM_F32>(a, L.G, L.W, weighted, stream);
-    else dispatch_k7<DLRM_BF16>(a, L.G, L.W, weighted, stream);
+    if (adagrad) {
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_ADAGRAD>(a, L.G, L.W, weighted, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_ADAGRAD>(a, L.G, L.W, weighted, stream);
+    } else {
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_SGD>(a, L.G, L.W, weighted, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_SGD>(a, L.G, L.W, weighted, stream);
+    }
     return launch_status();
+}
+
+extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows,
+                                   int32_t T, int32_t D, int32_t dtype, const int64_t *indices,
+                                   const int64_t *offsets, const float *per_sample_weights,
+                                   int64_t B, int64_t nnz, const float *grad_pooled, float lr,
+                                   float eps, void *workspace, size_t workspace_bytes,
+                                   int64_t *unique_keys_out, int64_t *segment_offsets_out,
+                                   int32_t *sorted_pos_out, int64_t *num_unique_out,
+                                   uint32_t flags, dlrm_stream_t stream) {
+    return emb_bag_bwd_update(tables, state, rows, T, D, dtype, indices, offsets, DLRM_INDEX_I64,
+                              per_sample_weights, B, nnz, grad_pooled, DLRM_OPT_ADAGRAD, lr, eps,
+                              workspace, workspace_bytes, unique_keys_out, segment_offsets_out,
+                              sorted_pos_out, num_unique_out, flags, stream);
 }

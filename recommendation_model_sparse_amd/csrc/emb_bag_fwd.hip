@@ -24,10 +24,10 @@ namespace {
 
 struct PoolArgs {
     const char *tables[kMaxTables];
-    const int64_t *indices;
-    const int64_t *offsets;
+    const void *indices;  // int64 or int32 (the kernel's IT)
+    const void *offsets;  // same type as the indices
     const float *weights;
-    float *out;
+    void *out;            // fp32 or bf16 (the kernel's OT)
     uint32_t B;
     uint32_t nbags;
     int32_t T;
@@ -37,8 +37,10 @@ struct PoolArgs {
 };
 
 // One wavefront per bag (multi-hot).  G lanes per row, NG = 64/G groups, U rows per group in flight.
-template <int DT, int G, bool WEIGHTED>
+template <int DT, int G, bool WEIGHTED, typename IT, int OT>
 __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
+    const IT *indices = static_cast<const IT *>(a.indices);
+    const IT *offsets = static_cast<const IT *>(a.offsets);
     constexpr int NG = kWave / G;
     constexpr int EPC = Elem<DT>::kPerChunk;
     constexpr int U = 8;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     const int grp = lane / G, c = lane % G;
     const uint32_t t = bag / a.B, b = bag - t * a.B;
     const char *tab = a.tables[t] + c * 16;
-    const int64_t start = a.offsets[bag], end = a.offsets[bag + 1];
+    const int64_t start = offsets[bag], end = offsets[bag + 1];
 
     float acc[EPC];
 #pragma unroll
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
 
     for (int64_t base = start; base < end; base += kWave) {
         const int n = static_cast<int>(min<int64_t>(kWave, end - base));
-        const int64_t my_idx = lane < n ? a.indices[base + lane] : 0;
+        const int64_t my_idx = lane < n ? static_cast<int64_t>(indices[base + lane]) : 0;
         float my_w = 1.f;
         if constexpr (WEIGHTED) my_w = lane < n ? a.weights[base + lane] : 0.f;
         for (int r0 = 0; r0 < n; r0 += NG * U) {
@@ -81,13 +83,14 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     for (int s = G; s < kWave; s <<= 1)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], s);
-    if (grp == 0)
-        store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
+    if (grp == 0) store_pooled<DT, OT>(a.out, (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
 }
 
 // One lane group per bag (one-hot or short bags); each group owns BPG bags.
-template <int DT, int G, bool WEIGHTED, int BPG>
+template <int DT, int G, bool WEIGHTED, int BPG, typename IT, int OT>
 __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
+    const IT *indices = static_cast<const IT *>(a.indices);
+    const IT *offsets = static_cast<const IT *>(a.offsets);
     constexpr int NG = kWave / G;
     constexpr int EPC = Elem<DT>::kPerChunk;
     const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
@@ -102,8 +105,8 @@ __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
     for (int k = 0; k < BPG; ++k) {
         const uint32_t bag = bag0 + k * NG;
         const bool ok = bag < a.nbags;
-        s[k] = ok ? a.offsets[bag] : 0;
-        e[k] = ok ? a.offsets[bag + 1] : 0;
+        s[k] = ok ? static_cast<int64_t>(offsets[bag]) : 0;
+        e[k] = ok ? static_cast<int64_t>(offsets[bag + 1]) : 0;
         tab[k] = a.tables[ok ? bag / a.B : 0] + c * 16;
     }
     float acc[BPG][EPC];
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
         float w[BPG];
 #pragma unroll
         for (int k = 0; k < BPG; ++k) {
-            idx[k] = s[k] < e[k] ? a.indices[s[k]] : 0;
+            idx[k] = s[k] < e[k] ? static_cast<int64_t>(indices[s[k]]) : 0;
             w[k] = (WEIGHTED && s[k] < e[k]) ? a.weights[s[k]] : 1.f;
         }
         uint4 v[BPG];
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const bool ok = j + u < e[k];
-                const int64_t idx = ok ? a.indices[j + u] : 0;
+                const int64_t idx = ok ? static_cast<int64_t>(indices[j + u]) : 0;
                 w[u] = (WEIGHTED && ok) ? a.weights[j + u] : 1.f;
                 v[u] = ok ? load_row_chunk(tab[k], idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
             }
@@ -152,14 +155,16 @@ __global__ __launch_bounds__(256) void k_pool_group_per_bag(PoolArgs a) {
         const uint32_t bag = bag0 + k * NG;
         if (bag < a.nbags) {
             const uint32_t t = bag / a.B, b = bag - t * a.B;
-            store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc[k]);
+            store_pooled<DT, OT>(a.out, (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc[k]);
         }
     }
 }
 
 // Any row width: one thread per (bag, 16-byte chunk).
-template <int DT, bool WEIGHTED>
+template <int DT, bool WEIGHTED, typename IT, int OT>
 __global__ __launch_bounds__(256) void k_pool_generic(PoolArgs a, uint32_t chunks) {
+    const IT *indices = static_cast<const IT *>(a.indices);
+    const IT *offsets = static_cast<const IT *>(a.offsets);
     constexpr int EPC = Elem<DT>::kPerChunk;
     const uint64_t gid = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const uint64_t bag = gid / chunks;
@@ -170,19 +175,20 @@ __global__ __launch_bounds__(256) void k_pool_generic(PoolArgs a, uint32_t chunk
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    for (int64_t j = a.offsets[bag]; j < a.offsets[bag + 1]; ++j) {
+    const int64_t j1 = offsets[bag + 1];
+    for (int64_t j = offsets[bag]; j < j1; ++j) {
         const float w = WEIGHTED ? a.weights[j] : 1.f;
-        accumulate<DT, WEIGHTED>(acc, load_row_chunk(tab, a.indices[j], a.row_bytes), w);
+        accumulate<DT, WEIGHTED>(acc, load_row_chunk(tab, static_cast<int64_t>(indices[j]), a.row_bytes), w);
     }
-    store_chunk<DT>(a.out + (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
+    store_pooled<DT, OT>(a.out, (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
 }
 
 // ---------------------------------------------------------------- index / offset check
 
 struct CheckArgs {
     int64_t rows[kMaxTables];
-    const int64_t *indices;
-    const int64_t *offsets;
+    const void *indices;
+    const void *offsets;
     uint32_t B;
     uint32_t nbags;
     int64_t nnz;
@@ -191,21 +197,24 @@ struct CheckArgs {
 
 __global__ void k_set_int(int *p, int v) { *p = v; }
 
+template <typename IT>
 __global__ __launch_bounds__(256) void k_check_csr(CheckArgs a) {
+    const IT *indices = static_cast<const IT *>(a.indices);
+    const IT *offsets = static_cast<const IT *>(a.offsets);
     const uint64_t bag = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (a.nbags == 0) {
-        if (bag == 0 && (a.offsets[0] != 0 || a.nnz != 0)) *a.flag = 1;
+        if (bag == 0 && (offsets[0] != 0 || a.nnz != 0)) *a.flag = 1;
         return;
     }
     if (bag >= a.nbags) return;
-    const int64_t o0 = a.offsets[bag], o1 = a.offsets[bag + 1];
+    const int64_t o0 = offsets[bag], o1 = offsets[bag + 1];
     bool bad = o1 < o0 || o0 < 0 || o1 > a.nnz;
     if (bag == 0 && o0 != 0) bad = true;
     if (bag + 1 == a.nbags && o1 != a.nnz) bad = true;
     const int64_t V = a.rows[bag / a.B];
     const int64_t lo = max<int64_t>(o0, 0), hi = min<int64_t>(o1, a.nnz);
     for (int64_t j = lo; j < hi; ++j) {
-        const int64_t i = a.indices[j];
+        const int64_t i = indices[j];
         if (i < 0 || i >= V) bad = true;
     }
     if (bad) *a.flag = 1;
@@ -214,9 +223,8 @@ __global__ __launch_bounds__(256) void k_check_csr(CheckArgs a) {
 }  // namespace
 
 // Runs the device-side CSR check; `flag` is 4 bytes of device scratch the caller lends.
-int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
-                        const int64_t *offsets, int64_t B, int64_t nnz, int *flag,
-                        hipStream_t stream) {
+int check_csr_on_device(const int64_t *rows, int32_t T, const void *indices, const void *offsets,
+                        int32_t index_type, int64_t B, int64_t nnz, int *flag, hipStream_t stream) {
     CheckArgs c{};
     for (int t = 0; t < T; ++t) c.rows[t] = rows[t];
     c.indices = indices;
@@ -227,7 +235,10 @@ int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
     c.flag = flag;
     DLRM_LAUNCH("set_int", k_set_int, dim3(1), dim3(1), 0, stream, flag, 0);
     const uint32_t blocks = c.nbags == 0 ? 1 : (c.nbags + 255) / 256;
-    DLRM_LAUNCH("check_csr", k_check_csr, dim3(blocks), dim3(256), 0, stream, c);
+    if (index_type == DLRM_INDEX_I32)
+        DLRM_LAUNCH("check_csr", k_check_csr<int32_t>, dim3(blocks), dim3(256), 0, stream, c);
+    else
+        DLRM_LAUNCH("check_csr", k_check_csr<int64_t>, dim3(blocks), dim3(256), 0, stream, c);
     if (hipGetLastError() != hipSuccess) return DLRM_ERR_HIP;
     int host_flag = 0;
     if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
@@ -238,48 +249,63 @@ int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
 
 namespace {
 
-template <int DT, int G, bool W>
+template <int DT, int G, bool W, typename IT, int OT>
 void launch_pool(const PoolArgs &a0, bool wave_per_bag, hipStream_t stream) {
     PoolArgs a = a0;
     constexpr int NG = kWave / G;
     if (wave_per_bag) {
         a.nblocks = round_up_xcd((a.nbags + 3) / 4);
-        DLRM_LAUNCH("pool_wave_per_bag", (k_pool_wave_per_bag<DT, G, W>), dim3(a.nblocks), dim3(256), 0, stream, a);
+        DLRM_LAUNCH("pool_wave_per_bag", (k_pool_wave_per_bag<DT, G, W, IT, OT>), dim3(a.nblocks), dim3(256), 0, stream, a);
     } else {
         constexpr int BPG = G >= 64 ? 1 : (G >= 32 ? 2 : 4);
         const uint64_t per_block = 4ull * NG * BPG;
         a.nblocks = round_up_xcd((a.nbags + per_block - 1) / per_block);
-        DLRM_LAUNCH("pool_group_per_bag", (k_pool_group_per_bag<DT, G, W, BPG>), dim3(a.nblocks), dim3(256), 0,
-                           stream, a);
+        DLRM_LAUNCH("pool_group_per_bag", (k_pool_group_per_bag<DT, G, W, BPG, IT, OT>), dim3(a.nblocks), dim3(256), 0,
+                    stream, a);
     }
 }
 
-template <int DT, bool W>
+template <int DT, bool W, typename IT, int OT>
 void dispatch_g(const PoolArgs &a, uint32_t chunks, bool wave_per_bag, hipStream_t stream) {
     switch (chunks) {
-        case 4: launch_pool<DT, 4, W>(a, wave_per_bag, stream); break;
-        case 8: launch_pool<DT, 8, W>(a, wave_per_bag, stream); break;
-        case 16: launch_pool<DT, 16, W>(a, wave_per_bag, stream); break;
-        case 32: launch_pool<DT, 32, W>(a, wave_per_bag, stream); break;
-        case 64: launch_pool<DT, 64, W>(a, wave_per_bag, stream); break;
+        case 4: launch_pool<DT, 4, W, IT, OT>(a, wave_per_bag, stream); break;
+        case 8: launch_pool<DT, 8, W, IT, OT>(a, wave_per_bag, stream); break;
+        case 16: launch_pool<DT, 16, W, IT, OT>(a, wave_per_bag, stream); break;
+        case 32: launch_pool<DT, 32, W, IT, OT>(a, wave_per_bag, stream); break;
+        case 64: launch_pool<DT, 64, W, IT, OT>(a, wave_per_bag, stream); break;
         default: {
             const uint64_t threads = static_cast<uint64_t>(a.nbags) * chunks;
-            DLRM_LAUNCH("pool_generic", (k_pool_generic<DT, W>), dim3((threads + 255) / 256), dim3(256), 0,
-                               stream, a, chunks);
+            DLRM_LAUNCH("pool_generic", (k_pool_generic<DT, W, IT, OT>), dim3((threads + 255) / 256), dim3(256), 0,
+                        stream, a, chunks);
         }
+    }
+}
+
+template <typename IT, int OT>
+void dispatch_pool(const PoolArgs &a, int32_t dtype, uint32_t chunks, bool wave_per_bag, bool weighted,
+                   hipStream_t stream) {
+    if (dtype == DLRM_F32) {
+        if (weighted) dispatch_g<DLRM_F32, true, IT, OT>(a, chunks, wave_per_bag, stream);
+        else dispatch_g<DLRM_F32, false, IT, OT>(a, chunks, wave_per_bag, stream);
+    } else {
+        if (weighted) dispatch_g<DLRM_BF16, true, IT, OT>(a, chunks, wave_per_bag, stream);
+        else dispatch_g<DLRM_BF16, false, IT, OT>(a, chunks, wave_per_bag, stream);
     }
 }
 
 }  // namespace
 }  // namespace dlrm
 
-extern "C" int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
-                           int32_t dtype, const int64_t *indices, const int64_t *offsets,
-                           const float *per_sample_weights, int64_t B, int64_t nnz, float *out,
-                           uint32_t flags, dlrm_stream_t stream_) {
+extern "C" int emb_bag_fwd_ex(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                              int32_t dtype, const void *indices, const void *offsets,
+                              int32_t index_type, const float *per_sample_weights, int64_t B,
+                              int64_t nnz, void *out, int32_t out_dtype, uint32_t flags,
+                              dlrm_stream_t stream_) {
     using namespace dlrm;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-    int rc = check_batch(tables, rows, T, D, dtype, indices, offsets, per_sample_weights, B, nnz);
+    if (index_type != DLRM_INDEX_I64 && index_type != DLRM_INDEX_I32) return DLRM_ERR_INVALID_ARG;
+    if (out_dtype != DLRM_F32 && out_dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
+    int rc = check_batch(tables, rows, T, D, dtype, indices, offsets, index_type, per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     if (B > 0 && (!out || !aligned(out, 16))) return DLRM_ERR_INVALID_ARG;
     if (flags & ~DLRM_FLAG_CHECK_INDICES) return DLRM_ERR_INVALID_ARG;
@@ -289,7 +315,7 @@ extern "C" int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32
     }
     if (flags & DLRM_FLAG_CHECK_INDICES) {
         // the output buffer lends 4 bytes for the flag; it is overwritten below
-        rc = check_csr_on_device(rows, T, indices, offsets, B, nnz, reinterpret_cast<int *>(out),
+        rc = check_csr_on_device(rows, T, indices, offsets, index_type, B, nnz, reinterpret_cast<int *>(out),
                                  stream);
         if (rc != DLRM_OK) return rc;
     }
@@ -308,12 +334,20 @@ extern "C" int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32
     // multi-hot bags (4+ rows on average) get a whole wavefront each
     const bool wave_per_bag = nnz >= 4 * static_cast<int64_t>(a.nbags);
     const bool weighted = per_sample_weights != nullptr;
-    if (dtype == DLRM_F32) {
-        if (weighted) dispatch_g<DLRM_F32, true>(a, chunks, wave_per_bag, stream);
-        else dispatch_g<DLRM_F32, false>(a, chunks, wave_per_bag, stream);
+    if (index_type == DLRM_INDEX_I64) {
+        if (out_dtype == DLRM_F32) dispatch_pool<int64_t, DLRM_F32>(a, dtype, chunks, wave_per_bag, weighted, stream);
+        else dispatch_pool<int64_t, DLRM_BF16>(a, dtype, chunks, wave_per_bag, weighted, stream);
     } else {
-        if (weighted) dispatch_g<DLRM_BF16, true>(a, chunks, wave_per_bag, stream);
-        else dispatch_g<DLRM_BF16, false>(a, chunks, wave_per_bag, stream);
+        if (out_dtype == DLRM_F32) dispatch_pool<int32_t, DLRM_F32>(a, dtype, chunks, wave_per_bag, weighted, stream);
+        else dispatch_pool<int32_t, DLRM_BF16>(a, dtype, chunks, wave_per_bag, weighted, stream);
     }
     return launch_status();
+}
+
+extern "C" int emb_bag_fwd(const void *const *tables, const int64_t *rows, int32_t T, int32_t D,
+                           int32_t dtype, const int64_t *indices, const int64_t *offsets,
+                           const float *per_sample_weights, int64_t B, int64_t nnz, float *out,
+                           uint32_t flags, dlrm_stream_t stream) {
+    return emb_bag_fwd_ex(tables, rows, T, D, dtype, indices, offsets, DLRM_INDEX_I64, per_sample_weights, B,
+                          nnz, out, DLRM_F32, flags, stream);
 }

@@ -26,9 +26,8 @@
 
 namespace dlrm {
 
-int check_csr_on_device(const int64_t *rows, int32_t T, const int64_t *indices,
-                        const int64_t *offsets, int64_t B, int64_t nnz, int *flag,
-                        hipStream_t stream);
+int check_csr_on_device(const int64_t *rows, int32_t T, const void *indices, const void *offsets,
+                        int32_t index_type, int64_t B, int64_t nnz, int *flag, hipStream_t stream);
 
 namespace {
 
@@ -689,7 +688,7 @@ extern "C" int emb_bag_interact_fwd(const void *const *tables, const int64_t *ro
                                     uint32_t flags, dlrm_stream_t stream_) {
     using namespace dlrm;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-    int rc = check_batch(tables, rows, T, D, dtype, indices, offsets, per_sample_weights, B, nnz);
+    int rc = check_batch(tables, rows, T, D, dtype, indices, offsets, DLRM_INDEX_I64, per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     if (flags & ~DLRM_FLAG_CHECK_INDICES) return DLRM_ERR_INVALID_ARG;
     const int N = T + 1;
@@ -702,7 +701,7 @@ extern "C" int emb_bag_interact_fwd(const void *const *tables, const int64_t *ro
     if (!dense || !out || !aligned(dense, 16) || !aligned(out, 4)) return DLRM_ERR_INVALID_ARG;
     if (flags & DLRM_FLAG_CHECK_INDICES) {
         // the output buffer lends 4 bytes for the flag; it is overwritten below
-        rc = check_csr_on_device(rows, T, indices, offsets, B, nnz, reinterpret_cast<int *>(out), stream);
+        rc = check_csr_on_device(rows, T, indices, offsets, DLRM_INDEX_I64, B, nnz, reinterpret_cast<int *>(out), stream);
         if (rc != DLRM_OK) return rc;
     }
     FusedArgs a{};

@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"emb_bag_fwd", "emb_bag_interact_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
+    assert {"emb_bag_fwd", "emb_bag_fwd_ex", "emb_bag_bwd_update", "emb_bag_interact_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
             "emb_bag_bwd_adagrad", "dlrm_status_string", "dlrm_synth_fill_table",
             "dlrm_trace_enable", "dlrm_trace_read"} <= names
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
@@ -93,6 +93,39 @@ def test_emb_bag_fwd_rejects(L):
     assert fwd(L, B=0, nnz=3) == INVALID
     assert fwd(L, B=0, nnz=0) == OK            # nothing to do, nothing launched
     assert fwd(L, B=1 << 30, T=2, tables=ptrs(FAKE, FAKE), rows=i64s(1, 1)) == UNSUPPORTED
+
+
+def fwd_ex(L, index_type=0, out_dtype=0, idx=FAKE, off=FAKE, out=FAKE, D=16, dtype=0):
+    return L.emb_bag_fwd_ex(ptrs(FAKE), i64s(10), 1, D, dtype, idx, off, index_type, None, 4, 4, out,
+                            out_dtype, 0, None)
+
+
+def test_emb_bag_fwd_ex_rejects(L):
+    assert fwd_ex(L, index_type=2) == INVALID
+    assert fwd_ex(L, out_dtype=3) == INVALID
+    assert fwd_ex(L, index_type=0, idx=FAKE + 4) == INVALID   # int64 indices need 8-byte alignment
+    assert fwd_ex(L, index_type=1, idx=FAKE + 2) == INVALID   # int32 indices need 4-byte alignment
+    assert fwd_ex(L, index_type=1, off=FAKE + 6) == INVALID
+    assert fwd_ex(L, out=FAKE + 8) == INVALID                 # output 16-byte aligned
+    assert fwd_ex(L, D=6) == UNSUPPORTED
+
+
+def upd(L, optimizer=0, index_type=0, state=True, T=1, D=16, wsz=None, idx=FAKE):
+    rows = [10] * T
+    st = ptrs(*[FAKE] * T) if state else None
+    if wsz is None:
+        wsz = binding.emb_bag_bwd_workspace_size(rows, D, 4, 4)
+    return L.emb_bag_bwd_update(ptrs(*[FAKE] * T), st, i64s(*rows), T, D, 0, idx, FAKE, index_type, None, 4,
+                                4, FAKE, optimizer, 0.01, 1e-8, FAKE, wsz, None, None, None, None, 0, None)
+
+
+def test_emb_bag_bwd_update_rejects(L):
+    assert upd(L, optimizer=2) == INVALID
+    assert upd(L, index_type=5) == INVALID
+    assert upd(L, optimizer=0, state=False) == INVALID       # Adagrad needs its state
+    assert upd(L, optimizer=1, state=False, wsz=1) == WORKSPACE  # SGD takes no state; reaches the workspace check
+    assert upd(L, index_type=1, idx=FAKE + 2) == INVALID
+    assert upd(L, D=24) == UNSUPPORTED
 
 
 def fused(L, T=2, D=32, dtype=0, rows=None, tables=None, dense=FAKE, out=FAKE, B=4, nnz=4, flags=0):

@@ -1,0 +1,155 @@
+"""GPU parity of the path variants (needs an MI355X): int32 indices and offsets, bf16 pooled
+output (emb_bag_fwd_ex), and the SGD update (emb_bag_bwd_update).
+
+Gates: int32 runs are bit-identical to the int64 runs of the same batch (forward values, updated
+tables and states, integer outputs); the bf16 output is bit-identical to the round-to-nearest-even
+of the fp32 output and within the bf16 gate (1e-2) of the oracle; SGD rows against the oracle as
+for Adagrad (fp32: per-row infinity-norm relative error <= 1e-4; bf16: half a bf16 ulp plus that),
+integer outputs bit-exact, untouched rows unchanged, every update bitwise reproducible.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recommendation_model_sparse_amd import (
+    DLRM_OPT_ADAGRAD,
+    DLRM_OPT_SGD,
+    AdagradOutputs,
+    emb_bag_bwd_update,
+    emb_bag_fwd,
+    emb_bag_fwd_ex,
+    synth,
+)
+
+from gpu_util import (DEV, as_f64, bf16_half_ulp, random_csr, random_tables, rel_err, row_inf_rel, say,
+                      to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def i32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(a.astype(np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 16), ("f32", 128), ("f32", 24), ("bf16", 64), ("bf16", 128),
+                                     ("bf16", 512)])
+@pytest.mark.parametrize("mode", ["onehot", "multi", "long"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_fwd_index_and_output_types(dtype, D, mode, weighted):
+    rng = np.random.default_rng(zlib.crc32(f"var-{dtype}-{D}-{mode}-{weighted}".encode()))
+    T, B = 4, 41
+    rows = [int(v) for v in rng.integers(1, 400, T)]
+    tables = random_tables(rng, rows, D, dtype)
+    idx, off, w = random_csr(rng, T, B, rows, "onehot" if mode == "onehot" else "multi",
+                             150 if mode == "long" else 12, weighted)
+    say(f"[variants] fwd {dtype} D={D} {mode} weighted={weighted} nnz={len(idx)}")
+    tabs = [to_dev(t) for t in tables]
+    dw = None if w is None else to_dev(w)
+    ref64 = emb_bag_fwd(tabs, to_dev(idx), to_dev(off), dw)
+    out32 = emb_bag_fwd_ex(tabs, i32(idx), i32(off), dw)
+    bf64 = emb_bag_fwd_ex(tabs, to_dev(idx), to_dev(off), dw, out_dtype=torch.bfloat16)
+    bf32 = emb_bag_fwd_ex(tabs, i32(idx), i32(off), dw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out32.view(torch.int32), ref64.view(torch.int32)), "int32 indices change the sums"
+    f32 = ref64.cpu().numpy()
+    want = synth.f32_to_bf16_bits(f32)
+    assert np.array_equal(to_host(bf64), want), "bf16 output is not the RNE of the fp32 sums"
+    assert np.array_equal(to_host(bf32), want)
+    ref, scale = oracle.emb_bag_fwd(tables, idx, off, w, B)
+    assert rel_err(synth.bf16_bits_to_f32(to_host(bf64)), ref, scale) <= 1e-2
+
+
+def run_update(rows, D, dtype, B, lengths, weighted, seed, opt, index32, max_len=12, hot=None, lr=0.01,
+               eps=1e-8, label=""):
+    """Returns (tables, states, outputs) after one update, checked to be bitwise reproducible."""
+    rng = np.random.default_rng(seed)
+    T = len(rows)
+    tables = random_tables(rng, rows, D, dtype)
+    states = [rng.random(v).astype(np.float32) for v in rows]
+    idx, off, w = random_csr(rng, T, B, rows, lengths, max_len, weighted, hot)
+    if w is not None:
+        w[::5] = 0.0
+    gp = (rng.standard_normal((B, T, D)) * 1e-3).astype(np.float32)
+    say(f"[variants] update {label} opt={opt} int32={index32} D={D} {dtype} B={B} nnz={len(idx)} weighted={weighted}")
+    res = []
+    for rep in range(2):
+        tabs = [to_dev(t) for t in tables]
+        sts = [to_dev(s) for s in states] if opt == DLRM_OPT_ADAGRAD else None
+        outs = AdagradOutputs(len(idx), DEV)
+        di, do = (i32(idx), i32(off)) if index32 else (to_dev(idx), to_dev(off))
+        emb_bag_bwd_update(tabs, sts, di, do, None if w is None else to_dev(w), to_dev(gp), opt, lr, eps,
+                           outputs=outs)
+        torch.cuda.synchronize()
+        res.append(([to_host(t) for t in tabs], None if sts is None else [s.cpu().numpy() for s in sts], outs))
+    (ta, sa, outs), (tb, sb, _) = res
+    for x, y in zip(ta + (sa or []), tb + (sb or [])):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), "update is not bitwise reproducible"
+    return tables, states, (idx, off, w, gp), ta, sa, outs
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 4), ("f32", 32), ("f32", 128), ("f32", 512), ("bf16", 8),
+                                     ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("lengths", ["onehot", "multi"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_sgd_vs_oracle(dtype, D, lengths, weighted):
+    rows = [300, 1, 2000, 77]
+    B = 130
+    seed = zlib.crc32(f"sgd-{dtype}-{D}-{lengths}-{weighted}".encode())
+    tables, _, (idx, off, w, gp), new, _, outs = run_update(rows, D, dtype, B, lengths, weighted, seed,
+                                                            DLRM_OPT_SGD, False, label="sgd")
+    r = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, 0.01)
+    U = int(outs.num_unique.item())
+    assert U == r.U
+    assert np.array_equal(outs.unique_keys.cpu().numpy()[:U], r.unique_keys)
+    assert np.array_equal(outs.segment_offsets.cpu().numpy()[:U + 1], r.seg_offsets)
+    assert np.array_equal(outs.sorted_pos.cpu().numpy()[:len(idx)], r.perm)
+    tt, rr = r.table_and_row()
+    for t in range(len(rows)):
+        sel = tt == t
+        touched = np.zeros(rows[t], dtype=bool)
+        touched[rr[sel]] = True
+        assert np.array_equal(new[t][~touched].view(np.uint8), tables[t][~touched].view(np.uint8))
+        if not sel.any():
+            continue
+        got, ref = as_f64(new[t][rr[sel]]), r.new_rows[sel]
+        if dtype == "f32":
+            assert row_inf_rel(got, ref) <= 1e-4
+        else:
+            tol = bf16_half_ulp(ref) * 1.0001 + 1e-4 * np.max(np.abs(ref), axis=1, keepdims=True)
+            assert np.all(np.abs(got - ref) <= tol)
+
+
+def test_sgd_long_segments_and_hot_rows():
+    """Segments crossing many chunks (one hot row) go through the finisher with the SGD rule."""
+    rows = [50, 5000]
+    tables, _, (idx, off, w, gp), new, _, outs = run_update(rows, 128, "f32", 3000, "multi", True, 91,
+                                                            DLRM_OPT_SGD, False, max_len=40, hot=3,
+                                                            label="hot")
+    r = oracle.emb_bag_bwd_sgd(tables, idx, off, w, 3000, gp, 0.01)
+    tt, rr = r.table_and_row()
+    for t in range(2):
+        sel = tt == t
+        assert row_inf_rel(as_f64(new[t][rr[sel]]), r.new_rows[sel]) <= 1e-4
+
+
+@pytest.mark.parametrize("opt", [DLRM_OPT_ADAGRAD, DLRM_OPT_SGD])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_update_int32_equals_int64(opt, dtype, weighted):
+    rows = [900, 3, 40000, 1]
+    seed = zlib.crc32(f"i32-{opt}-{dtype}-{weighted}".encode())
+    a = run_update(rows, 64, dtype, 257, "multi", weighted, seed, opt, False, label="i64")
+    b = run_update(rows, 64, dtype, 257, "multi", weighted, seed, opt, True, label="i32")
+    for x, y in zip(a[3], b[3]):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    if opt == DLRM_OPT_ADAGRAD:
+        for x, y in zip(a[4], b[4]):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    oa, ob = a[5], b[5]
+    U = int(oa.num_unique.item())
+    assert U == int(ob.num_unique.item())
+    for f in ("unique_keys", "segment_offsets", "sorted_pos"):
+        assert torch.equal(getattr(oa, f)[:U], getattr(ob, f)[:U])
