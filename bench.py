@@ -109,6 +109,36 @@ def time_inference(tabs, batches, steps, pooled, inter):
     return res
 
 
+def time_variants(tabs, batches, steps, ws, outs, gpooled, wl):
+    """Mean ms (HIP events) of the path variants on the same batches: bf16 pooled output, int32
+    indices and offsets, and the SGD backward (updates the tables in place)."""
+    import torch
+    from recommendation_model_sparse_amd import DLRM_OPT_SGD, emb_bag_bwd_update, emb_bag_fwd_ex
+
+    b32 = [dict(idx=b["idx"].to(torch.int32), off=b["off"].to(torch.int32)) for b in batches]
+    pooled_bf16 = torch.empty((wl.B, wl.T, wl.D), dtype=torch.bfloat16, device=tabs[0].device)
+    runs = {
+        "fwd_bf16_out": lambda i: emb_bag_fwd_ex(tabs, batches[i]["idx"], batches[i]["off"], None, out=pooled_bf16,
+                                                 out_dtype=torch.bfloat16),
+        "fwd_int32_indices": lambda i: emb_bag_fwd_ex(tabs, b32[i]["idx"], b32[i]["off"], None),
+        "bwd_sgd": lambda i: emb_bag_bwd_update(tabs, None, batches[i]["idx"], batches[i]["off"], None, gpooled,
+                                                DLRM_OPT_SGD, wl.lr, 0.0, workspace=ws, outputs=outs),
+    }
+    res = {}
+    for name, fn in runs.items():
+        for i in range(2):
+            fn(i % len(batches))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            fn(i % len(batches))
+        ev[1].record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = ev[0].elapsed_time(ev[1]) / steps
+    return res
+
+
 def inference_summary(inf, wl, nnz_avg):
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
     alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
@@ -286,6 +316,7 @@ def main():
 
     # inference: the fused lookup + interaction against the two calls, same batches and tables
     inf = time_inference(tabs, batches, args.steps, pooled, inter)
+    variants = time_variants(tabs, batches, args.steps, ws, outs, gpooled, wl)
 
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     U_last = int(outs.num_unique.item())
@@ -348,6 +379,7 @@ def main():
                      "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
         "kernels": kernels,
         "inference": inference_summary(inf, wl, nnz_avg),
+        "variants": variants,
     }
     if not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")
