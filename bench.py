@@ -139,6 +139,49 @@ def time_variants(tabs, batches, steps, ws, outs, gpooled, wl):
     return res
 
 
+def time_full_step(tabs, states, batches, host_batches, steps, wl, max_nnz):
+    """The full single-GPU DLRM training step around the sparse path: bottom MLP 13-512-256-128,
+    the lookup, the interaction, top MLP 480-1024-1024-512-256 and the sigmoid + BCE head, the
+    backward pass, SGD on the dense layers and row-wise Adagrad on the tables (HIP events)."""
+    import torch
+    from recommendation_model_sparse_amd.dlrm_step import DlrmStep
+
+    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
+
+    dev = tabs[0].device
+    # start from the initial tables: the timed regions before this one updated them with
+    # synthetic upstream gradients, which are no training signal
+    for t, (x, v) in enumerate(zip(tabs, wl.rows)):
+        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
+    for st in states:
+        st.zero_()
+    m = DlrmStep(tabs, states, wl.B, 13, bottom=[512, 256, wl.D], top=[1024, 1024, 512, 256], lr_dense=0.01,
+                 lr_emb=wl.lr, eps=wl.eps, seed=wl.seed + 99, max_nnz=max_nnz)
+    extra = [(torch.from_numpy(hb.features(13)).to(dev), torch.from_numpy(hb.labels()).to(dev)) for hb in host_batches]
+
+    def run(i):
+        b = batches[i % len(batches)]
+        x, y = extra[i % len(extra)]
+        m.step(b["idx"], b["off"], x, y)
+
+    for i in range(2):
+        run(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    dims_b = [(16, 512), (512, 256), (256, wl.D)]
+    dims_t = [(m.Ip, 1024), (1024, 1024), (1024, 512), (512, 256), (256, 1)]
+    flops = 3 * 2 * wl.B * sum(k * n for k, n in dims_b + dims_t)  # forward + two backward GEMMs
+    return {"ms_per_step": ms, "samples_per_s": wl.B / (ms / 1e3), "dense_gemm_tflop_per_step": flops / 1e12,
+            "loss_after": float(m.head_out["loss"].item()),
+            "layers": "bottom 13(16)-512-256-128, top 480-1024-1024-512-256-1, bf16 GEMMs (hipBLASLt), fp32 accumulation"}
+
+
 def inference_summary(inf, wl, nnz_avg):
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
     alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
@@ -317,6 +360,7 @@ def main():
     # inference: the fused lookup + interaction against the two calls, same batches and tables
     inf = time_inference(tabs, batches, args.steps, pooled, inter)
     variants = time_variants(tabs, batches, args.steps, ws, outs, gpooled, wl)
+    full = time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz)
 
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     U_last = int(outs.num_unique.item())
@@ -380,6 +424,7 @@ def main():
         "kernels": kernels,
         "inference": inference_summary(inf, wl, nnz_avg),
         "variants": variants,
+        "full_step": full,
     }
     if not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")

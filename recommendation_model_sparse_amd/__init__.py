@@ -5,6 +5,15 @@ kernels for gfx950 behind a C ABI (``include/dlrm_sparse.h``).
 The functions below are thin ctypes wrappers of that ABI; see ``binding``.
 """
 from .binding import (  # noqa: F401
+    DLRM_ACT_NONE,
+    DLRM_ACT_RELU,
+    dlrm_bce_head,
+    dlrm_bce_head_workspace_size,
+    dlrm_cast_rows,
+    dlrm_linear_bwd,
+    dlrm_linear_fwd,
+    dlrm_linear_workspace_size,
+    dlrm_sgd_dense,
     DLRM_BF16,
     DLRM_F32,
     DLRM_FLAG_CHECK_INDICES,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdlrm_sparse.so")
 DLRM_F32, DLRM_BF16 = 0, 1
 DLRM_INDEX_I64, DLRM_INDEX_I32 = 0, 1
 DLRM_OPT_ADAGRAD, DLRM_OPT_SGD = 0, 1
+DLRM_ACT_NONE, DLRM_ACT_RELU = 0, 1
 DLRM_FLAG_CHECK_INDICES = 1
 
 _lib = None
@@ -51,6 +52,17 @@ def lib() -> ctypes.CDLL:
         L.emb_bag_bwd_workspace_size.restype = sz
         L.emb_bag_bwd_adagrad.argtypes = [p, p, p, i32, i32, i32, p, p, p, i64, i64, p, f32, f32,
                                           p, sz, p, p, p, p, u32, p]
+        L.dlrm_linear_workspace_size.argtypes = [i64, i32, i32]
+        L.dlrm_linear_workspace_size.restype = sz
+        L.dlrm_bce_head_workspace_size.argtypes = [i64, i32]
+        L.dlrm_bce_head_workspace_size.restype = sz
+        L.dlrm_linear_fwd.argtypes = [p, p, p, i64, i32, i32, i32, p, i32, p, sz, p]
+        L.dlrm_linear_bwd.argtypes = [p, p, i32, i32, p, p, i64, i32, i32, p, p, p, p, p, sz, p]
+        L.dlrm_bce_head.argtypes = [p, p, p, p, i64, i32, p, p, p, p, p, p, sz, p]
+        L.dlrm_sgd_dense.argtypes = [p, p, p, i64, f32, p]
+        L.dlrm_cast_rows.argtypes = [p, i32, i64, i64, i32, p, i32, i32, p]
+        for f in (L.dlrm_linear_fwd, L.dlrm_linear_bwd, L.dlrm_bce_head, L.dlrm_sgd_dense, L.dlrm_cast_rows):
+            f.restype = ctypes.c_int
         L.dlrm_status_string.argtypes = [ctypes.c_int]
         L.dlrm_status_string.restype = ctypes.c_char_p
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
@@ -311,6 +323,118 @@ def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) 
     _check(lib().dlrm_synth_fill_table(_ptr(table), _dtype_code(table), table.shape[0],
                                        table.shape[1], t, seed, float(scale),
                                        _stream(table.device)), "dlrm_synth_fill_table")
+
+
+# ---------------------------------------------------------------- dense layers (dlrm_mlp.h)
+
+_TORCH_CODE = {torch.float32: DLRM_F32, torch.bfloat16: DLRM_BF16}
+
+
+def dlrm_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().dlrm_linear_workspace_size(M, N, K))
+
+
+def dlrm_bce_head_workspace_size(M: int, K: int) -> int:
+    return int(lib().dlrm_bce_head_workspace_size(M, K))
+
+
+def _ws(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous bf16")
+    return t
+
+
+def dlrm_linear_fwd(x: torch.Tensor, W: torch.Tensor, b: torch.Tensor, act: int = DLRM_ACT_RELU,
+                    y: Optional[torch.Tensor] = None, y_dtype: torch.dtype = torch.bfloat16,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = act(x W^T + b), x [M][K] bf16, W [N][K] bf16, b [N] fp32 (C: dlrm_linear_fwd)."""
+    x, W = _bf16(x, "x"), _bf16(W, "W")
+    b = _contig(b, torch.float32, "b")
+    M, K = x.shape
+    N = W.shape[0]
+    if W.shape[1] != K or b.numel() != N:
+        raise ValueError("shapes do not match")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=x.device)
+    ws = _ws(dlrm_linear_workspace_size(M, N, K), x.device, workspace)
+    _check(lib().dlrm_linear_fwd(_ptr(x), _ptr(W), _ptr(b), M, N, K, act, _ptr(y), _TORCH_CODE[y.dtype], _ptr(ws),
+                                 ws.numel(), _stream(x.device)), "dlrm_linear_fwd")
+    return y
+
+
+def dlrm_linear_bwd(dy: torch.Tensor, y: Optional[torch.Tensor], act: int, x: torch.Tensor, W: torch.Tensor,
+                    want_dx: bool = True, dz_bf16: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                    dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """(dx or None, dW, db) of y = act(x W^T + b) given dy fp32 (C: dlrm_linear_bwd)."""
+    dy = _contig(dy, torch.float32, "dy")
+    x, W = _bf16(x, "x"), _bf16(W, "W")
+    M, K = x.shape
+    N = W.shape[0]
+    dev = x.device
+    if dz_bf16 is None:
+        dz_bf16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if want_dx and dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=dev)
+    if db is None:
+        db = torch.empty(N, dtype=torch.float32, device=dev)
+    ycode = _TORCH_CODE[y.dtype] if y is not None else DLRM_F32
+    ws = _ws(dlrm_linear_workspace_size(M, N, K), dev, workspace)
+    _check(lib().dlrm_linear_bwd(_ptr(dy), _ptr(y), ycode, act, _ptr(x), _ptr(W), M, N, K, _ptr(dz_bf16),
+                                 _ptr(dx) if want_dx else None, _ptr(dW), _ptr(db), _ptr(ws), ws.numel(),
+                                 _stream(dev)), "dlrm_linear_bwd")
+    return (dx if want_dx else None), dW, db
+
+
+def dlrm_bce_head(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, t: torch.Tensor,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """Sigmoid head + mean BCE, forward and backward: dict p, loss, dx, dw, db (C: dlrm_bce_head)."""
+    x, w = _bf16(x, "x"), _bf16(w, "w")
+    b = _contig(b, torch.float32, "b")
+    t = _contig(t, torch.float32, "t")
+    M, K = x.shape
+    dev = x.device
+    o = out if out is not None else {
+        "p": torch.empty(M, dtype=torch.float32, device=dev), "loss": torch.empty(1, dtype=torch.float32, device=dev),
+        "dx": torch.empty((M, K), dtype=torch.float32, device=dev), "dw": torch.empty(K, dtype=torch.float32, device=dev),
+        "db": torch.empty(1, dtype=torch.float32, device=dev)}
+    ws = _ws(dlrm_bce_head_workspace_size(M, K), dev, workspace)
+    _check(lib().dlrm_bce_head(_ptr(x), _ptr(w), _ptr(b), _ptr(t), M, K, _ptr(o["p"]), _ptr(o["loss"]), _ptr(o["dx"]),
+                               _ptr(o["dw"]), _ptr(o["db"]), _ptr(ws), ws.numel(), _stream(dev)), "dlrm_bce_head")
+    return o
+
+
+def dlrm_sgd_dense(w32: torch.Tensor, w16: Optional[torch.Tensor], g: torch.Tensor, lr: float) -> None:
+    """w32 -= lr * g; w16 <- bf16(w32) when given (C: dlrm_sgd_dense)."""
+    w32 = _contig(w32, torch.float32, "w32")
+    g = _contig(g, torch.float32, "g")
+    if w16 is not None and (w16.numel() != w32.numel()):
+        raise ValueError("w16 must match w32")
+    if g.numel() != w32.numel():
+        raise ValueError("g must match w32")
+    _check(lib().dlrm_sgd_dense(_ptr(w32), _ptr(w16) if w16 is not None else None, _ptr(g), w32.numel(), float(lr),
+                                _stream(w32.device)), "dlrm_sgd_dense")
+
+
+def dlrm_cast_rows(src: torch.Tensor, cols: int, dst_cols: int, dst_dtype: torch.dtype,
+                   dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dst [M][dst_cols]: the first `cols` columns of src converted, the rest zero (C: dlrm_cast_rows)."""
+    if src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a 2-D matrix with packed rows")
+    M = src.shape[0]
+    if dst is None:
+        dst = torch.empty((M, dst_cols), dtype=dst_dtype, device=src.device)
+    _check(lib().dlrm_cast_rows(_ptr(src), _TORCH_CODE[src.dtype], src.stride(0), M, cols, _ptr(dst),
+                                _TORCH_CODE[dst.dtype], dst_cols, _stream(src.device)), "dlrm_cast_rows")
+    return dst
 
 
 def dlrm_trace_enable(on: bool = True) -> None:

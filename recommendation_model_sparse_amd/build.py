@@ -55,7 +55,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + f".tmp{os.getpid()}"
-    subprocess.check_call([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    # hipBLASLt runs the plain GEMMs of the dense layers (mlp.hip)
+    subprocess.check_call([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-lhipblaslt"])
     os.replace(tmp, LIB)
     if verbose:
         sys.stderr.write(f"[build] {LIB} in {time.time() - t0:.1f}s\n")

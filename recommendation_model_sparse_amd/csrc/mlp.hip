@@ -1,0 +1,490 @@
+// Dense layers either side of the sparse path (robocikowo.com "DLRM", paragraph "Forward pass":
+// stage (1) bottom MLP, stage (4) top MLP with the sigmoid, trained on cross-entropy with
+// SGD/Adagrad).
+//
+// The GEMMs are plain library GEMMs and run in hipBLASLt (bf16 operands, fp32 accumulation,
+// bias + ReLU fused into its epilogue on the forward).  The rest is hand-written here:
+//   - ReLU backward + bf16 rounding of dz for the GEMMs + per-block partial column sums of the
+//     fp32 dz, then a fixed-order reduction to the bias gradient (deterministic, no atomics);
+//   - the one-unit sigmoid head with the mean binary cross-entropy, forward and backward in one
+//     pass: a wavefront per row, the dot product reduced across the wave, per-block partial sums of
+//     dw, db and the loss reduced in a fixed order;
+//   - SGD on fp32 master weights refreshing their bf16 copies, and a row cast / pad.
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "common.h"
+#include "dlrm_mlp.h"
+
+namespace dlrm {
+namespace {
+
+constexpr size_t kGemmScratch = size_t(32) << 20;  // hipBLASLt workspace per GEMM
+constexpr int kGradRows = 128;                      // rows per block of the bias-gradient partials
+constexpr int kHeadBlocks = 512;                    // blocks of the head (fixes its summation order)
+constexpr int kHeadMaxK = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // nearest even
+}
+
+// ---------------------------------------------------------------- ReLU backward + bias gradient
+
+// Block (bx, by): rows [bx*kGradRows, +kGradRows), columns by*256 + tid.  dz = dy * [y > 0] (or
+// dy); dz rounded to bf16; partial[bx][c] = sum of the block's fp32 dz of column c, in row order.
+template <bool RELU, int YT>
+__global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy, const void *__restrict__ y,
+                                                   int64_t M, int32_t N, uint16_t *__restrict__ dz,
+                                                   float *__restrict__ partial) {
+    const int32_t c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= N) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGradRows;
+    const int64_t r1 = min<int64_t>(r0 + kGradRows, M);
+    float s = 0.f;
+    constexpr int R = 8;  // rows whose loads are in flight together (unconditional: clamped rows)
+    for (int64_t r = r0; r < r1; r += R) {
+        float g[R], yv[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const uint64_t i = static_cast<uint64_t>(min(r + u, r1 - 1)) * N + c;
+            g[u] = dy[i];
+            if constexpr (RELU)
+                yv[u] = YT == DLRM_F32 ? static_cast<const float *>(y)[i]
+                                       : bf16_to_f32(static_cast<const uint16_t *>(y)[i]);
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if (r + u >= r1) break;
+            float gu = g[u];
+            if constexpr (RELU) gu = yv[u] > 0.f ? gu : 0.f;
+            dz[static_cast<uint64_t>(r + u) * N + c] = f32_to_bf16(gu);
+            s += gu;
+        }
+    }
+    partial[static_cast<uint64_t>(blockIdx.x) * N + c] = s;
+}
+
+// Sum over blocks of partial[blk][c] (row stride `ld`) for column c: one wavefront per column;
+// lane l adds blocks l, l+64, ... in order, then a fixed butterfly adds the 64 lane sums.
+__device__ __forceinline__ float wave_colsum(const float *__restrict__ partial, int32_t nblk, int64_t ld,
+                                             int64_t c) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    for (int32_t k = lane; k < nblk; k += kWave) s += partial[static_cast<uint64_t>(k) * ld + c];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) s += __shfl_xor(s, sh);
+    return s;
+}
+
+__global__ __launch_bounds__(256) void k_colsum(const float *__restrict__ partial, int32_t nblk, int32_t N,
+                                                float *__restrict__ out) {
+    const int32_t c = blockIdx.x * 4 + static_cast<int32_t>(wave_id());
+    if (c >= N) return;  // wave-uniform
+    const float s = wave_colsum(partial, nblk, N, c);
+    if ((threadIdx.x & 63) == 0) out[c] = s;
+}
+
+// ---------------------------------------------------------------- sigmoid head + BCE
+
+constexpr int kHeadCPL = kHeadMaxK / kWave;  // columns per lane (at most)
+
+// Layout of the head's partials: [kHeadBlocks][K + 2] (dw columns, then db, then loss).
+__global__ __launch_bounds__(256) void k_bce_head(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                  const float *__restrict__ b, const float *__restrict__ t,
+                                                  int64_t M, int32_t K, float *__restrict__ p,
+                                                  float *__restrict__ dx, float *__restrict__ partial) {
+    __shared__ float red[4][kHeadMaxK + 2];
+    const int lane = threadIdx.x & 63, wv = static_cast<int>(wave_id());
+    const float bias = b[0];
+    const float invM = 1.0f / static_cast<float>(M);
+    float wl[kHeadCPL], dwl[kHeadCPL];
+#pragma unroll
+    for (int i = 0; i < kHeadCPL; ++i) {
+        const int c = lane + i * kWave;
+        wl[i] = c < K ? bf16_to_f32(w[c]) : 0.f;
+        dwl[i] = 0.f;
+    }
+    float dbl = 0.f, lossl = 0.f;
+    const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+    for (int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + wv; m < M; m += nw) {  // wave-uniform
+        const uint16_t *xr = x + static_cast<uint64_t>(m) * K;
+        float xv[kHeadCPL];
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < kHeadCPL; ++i) {
+            const int c = lane + i * kWave;
+            xv[i] = c < K ? bf16_to_f32(xr[c]) : 0.f;
+            z = fmaf(xv[i], wl[i], z);
+        }
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) z += __shfl_xor(z, sh);  // every lane: the same bits
+        z += bias;
+        const float tm = t[m];
+        const float pm = 1.0f / (1.0f + expf(-z));
+        const float loss = fmaxf(z, 0.f) - z * tm + log1pf(expf(-fabsf(z)));
+        const float dz = (pm - tm) * invM;
+        if (lane == 0) p[m] = pm;
+        float *dxr = dx + static_cast<uint64_t>(m) * K;
+#pragma unroll
+        for (int i = 0; i < kHeadCPL; ++i) {
+            const int c = lane + i * kWave;
+            if (c < K) dxr[c] = dz * wl[i];
+            dwl[i] = fmaf(dz, xv[i], dwl[i]);
+        }
+        dbl += dz;
+        lossl += loss;
+    }
+    // combine the block's 4 waves in order, then write the block's partials
+#pragma unroll
+    for (int i = 0; i < kHeadCPL; ++i) {
+        const int c = lane + i * kWave;
+        if (c < K) red[wv][c] = dwl[i];
+    }
+    if (lane == 0) {
+        red[wv][K] = dbl;
+        red[wv][K + 1] = lossl;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < K + 2; c += 256) {
+        const float s = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+        partial[static_cast<uint64_t>(blockIdx.x) * (K + 2) + c] = s;
+    }
+}
+
+// dw[c], db, loss = sums over the blocks' partials (loss divided by M); one wavefront per column.
+__global__ __launch_bounds__(256) void k_bce_final(const float *__restrict__ partial, int32_t nblk, int32_t K,
+                                                   int64_t M, float *__restrict__ dw, float *__restrict__ db,
+                                                   float *__restrict__ loss) {
+    const int32_t c = blockIdx.x * 4 + static_cast<int32_t>(wave_id());
+    if (c >= K + 2) return;  // wave-uniform
+    const float s = wave_colsum(partial, nblk, K + 2, c);
+    if ((threadIdx.x & 63) != 0) return;
+    if (c < K) dw[c] = s;
+    else if (c == K) db[0] = s;
+    else loss[0] = s / static_cast<float>(M);
+}
+
+// ---------------------------------------------------------------- SGD and row casts
+
+__global__ __launch_bounds__(256) void k_sgd_dense(float *__restrict__ w32, uint16_t *__restrict__ w16,
+                                                   const float *__restrict__ g, int64_t n, float lr) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float v = fmaf(-lr, g[i], w32[i]);
+    w32[i] = v;
+    if (w16) w16[i] = f32_to_bf16(v);
+}
+
+template <int ST, int DT>
+__global__ __launch_bounds__(256) void k_cast_rows(const void *__restrict__ src, int64_t src_ld, int64_t M,
+                                                   int32_t cols, void *__restrict__ dst, int32_t dst_cols) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M * dst_cols) return;
+    const int64_t m = i / dst_cols;
+    const int32_t c = static_cast<int32_t>(i - m * dst_cols);
+    float v = 0.f;
+    if (c < cols) {
+        const uint64_t s = static_cast<uint64_t>(m) * src_ld + c;
+        v = ST == DLRM_F32 ? static_cast<const float *>(src)[s] : bf16_to_f32(static_cast<const uint16_t *>(src)[s]);
+    }
+    if constexpr (DT == DLRM_F32) static_cast<float *>(dst)[i] = v;
+    else static_cast<uint16_t *>(dst)[i] = f32_to_bf16(v);
+}
+
+// ---------------------------------------------------------------- hipBLASLt
+
+std::mutex g_lt_mutex;
+hipblasLtHandle_t g_lt_handle[64] = {};
+
+using AlgoKey = std::tuple<int, int, int, int64_t, int64_t, int64_t, int, int>;
+std::map<AlgoKey, hipblasLtMatmulAlgo_t> g_algo_cache;
+
+hipblasLtHandle_t lt_handle(int dev) {
+    std::lock_guard<std::mutex> lock(g_lt_mutex);
+    if (!g_lt_handle[dev] && hipblasLtCreate(&g_lt_handle[dev]) != HIPBLAS_STATUS_SUCCESS) g_lt_handle[dev] = nullptr;
+    return g_lt_handle[dev];
+}
+
+// Column-major D[m][n] (ld m) = op(A) op(B) (+ bias[m], ReLU); A, B bf16, fp32 accumulation.
+// With batch > 1: `batch` such products, operand s at A + s*sA, B + s*sB, D + s*sD (elements).
+int lt_gemm(hipStream_t stream, bool transA, bool transB, int64_t m, int64_t n, int64_t k, const void *A,
+            int64_t lda, const void *B, int64_t ldb, void *D, hipDataType dtype, const float *bias, bool relu,
+            void *ws, size_t ws_bytes, int32_t batch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sD = 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DLRM_ERR_HIP;
+    hipblasLtHandle_t h = lt_handle(dev);
+    if (!h) return DLRM_ERR_HIP;
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    int rc = DLRM_ERR_HIP;
+    const hipblasOperation_t opA = transA ? HIPBLAS_OP_T : HIPBLAS_OP_N, opB = transB ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+    const hipblasLtEpilogue_t epi = bias ? (relu ? HIPBLASLT_EPILOGUE_RELU_BIAS : HIPBLASLT_EPILOGUE_BIAS)
+                                         : (relu ? HIPBLASLT_EPILOGUE_RELU : HIPBLASLT_EPILOGUE_DEFAULT);
+    const hipDataType bias_type = HIP_R_32F;
+    const float alpha = 1.f, beta = 0.f;
+    do {
+        if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opA, sizeof(opA)) != HIPBLAS_STATUS_SUCCESS) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opB, sizeof(opB)) != HIPBLAS_STATUS_SUCCESS) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof(epi)) != HIPBLAS_STATUS_SUCCESS) break;
+        if (bias) {
+            if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) != HIPBLAS_STATUS_SUCCESS) break;
+            if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type, sizeof(bias_type)) != HIPBLAS_STATUS_SUCCESS) break;
+        }
+        if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, transA ? k : m, transA ? m : k, lda) != HIPBLAS_STATUS_SUCCESS) break;
+        if (hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, transB ? n : k, transB ? k : n, ldb) != HIPBLAS_STATUS_SUCCESS) break;
+        if (hipblasLtMatrixLayoutCreate(&ld, dtype, m, n, m) != HIPBLAS_STATUS_SUCCESS) break;
+        if (batch > 1) {
+            bool ok = true;
+            const hipblasLtMatrixLayout_t lays[3] = {la, lb, ld};
+            const int64_t strides[3] = {sA, sB, sD};
+            for (int q = 0; q < 3 && ok; ++q)
+                ok = hipblasLtMatrixLayoutSetAttribute(lays[q], HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &batch,
+                                                       sizeof(batch)) == HIPBLAS_STATUS_SUCCESS &&
+                     hipblasLtMatrixLayoutSetAttribute(lays[q], HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET,
+                                                       &strides[q], sizeof(strides[q])) == HIPBLAS_STATUS_SUCCESS;
+            if (!ok) break;
+        }
+        const AlgoKey key{dev, (transA ? 1 : 0) | (transB ? 2 : 0), static_cast<int>(epi), m, n, k, static_cast<int>(dtype), batch};
+        hipblasLtMatmulAlgo_t algo;
+        bool have = false;
+        {
+            std::lock_guard<std::mutex> lock(g_lt_mutex);
+            auto it = g_algo_cache.find(key);
+            if (it != g_algo_cache.end()) algo = it->second, have = true;
+        }
+        if (!have) {
+            if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) break;
+            const uint64_t max_ws = ws_bytes;
+            if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &max_ws,
+                                                      sizeof(max_ws)) != HIPBLAS_STATUS_SUCCESS) break;
+            constexpr int kCand = 8;
+            hipblasLtMatmulHeuristicResult_t res[kCand];
+            int found = 0;
+            if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, kCand, res, &found) !=
+                    HIPBLAS_STATUS_SUCCESS ||
+                found < 1) {
+                rc = DLRM_ERR_UNSUPPORTED;
+                break;
+            }
+            // first call for this shape: time every candidate on the caller's stream, keep the fastest
+            int best = 0;
+            if (found > 1) {
+                hipEvent_t e0, e1;
+                if (hipEventCreate(&e0) != hipSuccess) break;
+                if (hipEventCreate(&e1) != hipSuccess) {
+                    (void)hipEventDestroy(e0);
+                    break;
+                }
+                float best_ms = 1e30f;
+                for (int c = 0; c < found; ++c) {
+                    if (hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &res[c].algo, ws, ws_bytes,
+                                        stream) != HIPBLAS_STATUS_SUCCESS)
+                        continue;
+                    (void)hipEventRecord(e0, stream);
+                    bool ok = true;
+                    for (int r = 0; r < 3 && ok; ++r)
+                        ok = hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &res[c].algo, ws,
+                                             ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+                    (void)hipEventRecord(e1, stream);
+                    float ms = 0.f;
+                    if (ok && hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+                        ms < best_ms)
+                        best_ms = ms, best = c;
+                }
+                (void)hipEventDestroy(e0);
+                (void)hipEventDestroy(e1);
+            }
+            algo = res[best].algo;
+            std::lock_guard<std::mutex> lock(g_lt_mutex);
+            g_algo_cache[key] = algo;
+        }
+        if (hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &algo, ws, ws_bytes, stream) !=
+            HIPBLAS_STATUS_SUCCESS)
+            break;
+        rc = DLRM_OK;
+    } while (false);
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (ld) hipblasLtMatrixLayoutDestroy(ld);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (desc) hipblasLtMatmulDescDestroy(desc);
+    return rc;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Slices of the batch dimension for the weight-gradient GEMM (its K dimension is M): enough
+// output tiles for the chip when N x K is small, and a fixed split for a given M.
+constexpr int kMaxSplit = 8;
+constexpr int64_t kSplitRows = 2048;
+int dw_split(int64_t M) {
+    int s = 1;
+    while (s < kMaxSplit && M % (2 * s) == 0 && M / (2 * s) >= kSplitRows) s *= 2;
+    return s;
+}
+
+// out[i] = sum over s of part[s][i], slices in order.
+__global__ __launch_bounds__(256) void k_sum_slices(const float *__restrict__ part, int32_t S, int64_t n,
+                                                    float *__restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = part[i];
+    for (int32_t q = 1; q < S; ++q) s += part[static_cast<uint64_t>(q) * n + i];
+    out[i] = s;
+}
+
+bool layer_dims_ok(int64_t M, int32_t N, int32_t K) {
+    return M >= 1 && M < (int64_t(1) << 31) && N >= 1 && K >= 1 && N <= 65536 && K <= 65536 && N % 8 == 0 &&
+           K % 8 == 0;
+}
+
+}  // namespace
+}  // namespace dlrm
+
+using namespace dlrm;
+
+// Workspace: [GEMM scratch][bias-gradient partials][split-K partials of dW].
+inline size_t partials_bytes(int64_t M, int32_t N) {
+    return align_up(static_cast<size_t>((M + kGradRows - 1) / kGradRows) * static_cast<size_t>(N) * 4, 256);
+}
+
+extern "C" size_t dlrm_linear_workspace_size(int64_t M, int32_t N, int32_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    const int S = dw_split(M);
+    return kGemmScratch + partials_bytes(M, N) +
+           (S > 1 ? align_up(static_cast<size_t>(S) * N * static_cast<size_t>(K) * 4, 256) : 0);
+}
+
+extern "C" int dlrm_linear_fwd(const uint16_t *x, const uint16_t *W, const float *b, int64_t M, int32_t N,
+                               int32_t K, int32_t act, void *y, int32_t y_dtype, void *workspace,
+                               size_t workspace_bytes, dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!layer_dims_ok(M, N, K)) return M >= 1 && N >= 1 && K >= 1 ? DLRM_ERR_UNSUPPORTED : DLRM_ERR_INVALID_ARG;
+    if (act != DLRM_ACT_NONE && act != DLRM_ACT_RELU) return DLRM_ERR_INVALID_ARG;
+    if (y_dtype != DLRM_F32 && y_dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
+    if (!x || !W || !b || !y || !aligned(x, 16) || !aligned(W, 16) || !aligned(b, 4) || !aligned(y, 16))
+        return DLRM_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < dlrm_linear_workspace_size(M, N, K))
+        return DLRM_ERR_WORKSPACE;
+    // row-major y[M][N] = x[M][K] W[N][K]^T  <=>  column-major y^T (N x M) = W^T x^T
+    int rc = lt_gemm(stream, true, false, N, M, K, W, K, x, K, y, y_dtype == DLRM_F32 ? HIP_R_32F : HIP_R_16BF, b,
+                     act == DLRM_ACT_RELU, workspace, kGemmScratch);
+    if (rc != DLRM_OK) return rc;
+    return launch_status();
+}
+
+extern "C" int dlrm_linear_bwd(const float *dy, const void *y, int32_t y_dtype, int32_t act, const uint16_t *x,
+                               const uint16_t *W, int64_t M, int32_t N, int32_t K, uint16_t *dz_bf16, float *dx,
+                               float *dW, float *db, void *workspace, size_t workspace_bytes,
+                               dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!layer_dims_ok(M, N, K)) return M >= 1 && N >= 1 && K >= 1 ? DLRM_ERR_UNSUPPORTED : DLRM_ERR_INVALID_ARG;
+    if (act != DLRM_ACT_NONE && act != DLRM_ACT_RELU) return DLRM_ERR_INVALID_ARG;
+    if (y_dtype != DLRM_F32 && y_dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
+    if (!dy || !x || !W || !dz_bf16 || !dW || !db || (act == DLRM_ACT_RELU && !y)) return DLRM_ERR_INVALID_ARG;
+    if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(W, 16) || !aligned(dz_bf16, 16) || !aligned(dW, 16) ||
+        !aligned(db, 4) || (dx && !aligned(dx, 16)) || (y && !aligned(y, 16)))
+        return DLRM_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < dlrm_linear_workspace_size(M, N, K))
+        return DLRM_ERR_WORKSPACE;
+    float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + kGemmScratch);
+    const int32_t nblk = static_cast<int32_t>((M + kGradRows - 1) / kGradRows);
+    const dim3 grid(nblk, (N + 255) / 256);
+    if (act == DLRM_ACT_RELU) {
+        if (y_dtype == DLRM_F32)
+            DLRM_LAUNCH("relu_grad", (k_relu_grad<true, DLRM_F32>), grid, dim3(256), 0, stream, dy, y, M, N, dz_bf16, partial);
+        else
+            DLRM_LAUNCH("relu_grad", (k_relu_grad<true, DLRM_BF16>), grid, dim3(256), 0, stream, dy, y, M, N, dz_bf16, partial);
+    } else {
+        DLRM_LAUNCH("relu_grad", (k_relu_grad<false, DLRM_F32>), grid, dim3(256), 0, stream, dy, y, M, N, dz_bf16, partial);
+    }
+    DLRM_LAUNCH("colsum", k_colsum, dim3((N + 3) / 4), dim3(256), 0, stream, partial, nblk, N, db);
+    if (hipGetLastError() != hipSuccess) return DLRM_ERR_HIP;
+    int rc;
+    if (dx) {
+        // row-major dx[M][K] = dz[M][N] W[N][K]  <=>  column-major dx^T (K x M) = W^T(K x N, stored as W) dz^T
+        rc = lt_gemm(stream, false, false, K, M, N, W, K, dz_bf16, N, dx, HIP_R_32F, nullptr, false, workspace,
+                     kGemmScratch);
+        if (rc != DLRM_OK) return rc;
+    }
+    // row-major dW[N][K] = dz^T x  <=>  column-major dW^T (K x N) = x^T(K x M, stored as x) dz (M x N);
+    // split over S slices of the rows (a strided batch), then the slices summed in order
+    const int S = dw_split(M);
+    if (S == 1) {
+        rc = lt_gemm(stream, false, true, K, N, M, x, K, dz_bf16, N, dW, HIP_R_32F, nullptr, false, workspace,
+                     kGemmScratch);
+    } else {
+        const int64_t Ms = M / S;
+        float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kGemmScratch + partials_bytes(M, N));
+        rc = lt_gemm(stream, false, true, K, N, Ms, x, K, dz_bf16, N, part, HIP_R_32F, nullptr, false, workspace,
+                     kGemmScratch, S, Ms * K, Ms * N, static_cast<int64_t>(K) * N);
+        if (rc == DLRM_OK) {
+            const int64_t n = static_cast<int64_t>(K) * N;
+            DLRM_LAUNCH("sum_slices", k_sum_slices, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream,
+                        part, S, n, dW);
+        }
+    }
+    if (rc != DLRM_OK) return rc;
+    return launch_status();
+}
+
+extern "C" size_t dlrm_bce_head_workspace_size(int64_t M, int32_t K) {
+    if (M < 1 || K < 1 || K > kHeadMaxK) return 0;
+    return align_up(static_cast<size_t>(kHeadBlocks) * (K + 2) * 4, 256);
+}
+
+extern "C" int dlrm_bce_head(const uint16_t *x, const uint16_t *w, const float *b, const float *t, int64_t M,
+                             int32_t K, float *p, float *loss, float *dx, float *dw, float *db, void *workspace,
+                             size_t workspace_bytes, dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (M < 1 || K < 1) return DLRM_ERR_INVALID_ARG;
+    if (K > kHeadMaxK || K % 8 != 0 || M >= (int64_t(1) << 31)) return DLRM_ERR_UNSUPPORTED;
+    if (!x || !w || !b || !t || !p || !loss || !dx || !dw || !db) return DLRM_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16)) return DLRM_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < dlrm_bce_head_workspace_size(M, K))
+        return DLRM_ERR_WORKSPACE;
+    float *partial = static_cast<float *>(workspace);
+    DLRM_LAUNCH("bce_head", k_bce_head, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    DLRM_LAUNCH("bce_final", k_bce_final, dim3((K + 2 + 3) / 4), dim3(256), 0, stream, partial, kHeadBlocks, K, M,
+                dw, db, loss);
+    return launch_status();
+}
+
+extern "C" int dlrm_sgd_dense(float *w32, uint16_t *w16, const float *g, int64_t n, float lr,
+                              dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (n < 0) return DLRM_ERR_INVALID_ARG;
+    if (n == 0) return DLRM_OK;
+    if (!w32 || !g) return DLRM_ERR_INVALID_ARG;
+    DLRM_LAUNCH("sgd_dense", k_sgd_dense, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, w32, w16, g,
+                n, lr);
+    return launch_status();
+}
+
+extern "C" int dlrm_cast_rows(const void *src, int32_t src_dtype, int64_t src_ld, int64_t M, int32_t cols, void *dst,
+                              int32_t dst_dtype, int32_t dst_cols, dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if ((src_dtype != DLRM_F32 && src_dtype != DLRM_BF16) || (dst_dtype != DLRM_F32 && dst_dtype != DLRM_BF16))
+        return DLRM_ERR_INVALID_ARG;
+    if (M < 0 || cols < 0 || dst_cols < cols || src_ld < cols) return DLRM_ERR_INVALID_ARG;
+    const int64_t total = M * dst_cols;
+    if (total == 0) return DLRM_OK;
+    if (!src || !dst || total >= (int64_t(1) << 40)) return DLRM_ERR_INVALID_ARG;
+    const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
+    if (src_dtype == DLRM_F32 && dst_dtype == DLRM_BF16)
+        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_F32, DLRM_BF16>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
+    else if (src_dtype == DLRM_F32)
+        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_F32, DLRM_F32>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
+    else if (dst_dtype == DLRM_BF16)
+        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_BF16, DLRM_BF16>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
+    else
+        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_BF16, DLRM_F32>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
+    return launch_status();
+}

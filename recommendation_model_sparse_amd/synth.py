@@ -31,6 +31,7 @@ import numpy as np
 
 # stream ids inside one workload seed
 S_INDICES, S_LENGTHS, S_WEIGHTS, S_DENSE, S_GRADS, S_TABLES = 0, 1, 2, 3, 4, 5
+S_FEATURES, S_LABELS = 6, 7  # raw dense features and 0/1 clicks of the full training step
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -282,6 +283,14 @@ class Batch:
         wl = self.wl
         g = rng_for(wl.seed, S_GRADS, 1000 + self.i).standard_normal((wl.B, wl.T, wl.D))
         return (g * wl.grad_std).astype(np.float32)
+
+    def features(self, n: int = 13) -> np.ndarray:
+        """Raw dense features of the full training step, N(0, 1), float32 [B, n]."""
+        return rng_for(self.wl.seed, S_FEATURES, self.i).standard_normal((self.wl.B, n)).astype(np.float32)
+
+    def labels(self, rate: float = 0.25) -> np.ndarray:
+        """0/1 clicks of the full training step, Bernoulli(rate), float32 [B]."""
+        return (rng_for(self.wl.seed, S_LABELS, self.i).random(self.wl.B) < rate).astype(np.float32)
 
     def bag_lengths(self) -> np.ndarray:
         return np.diff(self.offsets)

@@ -219,3 +219,38 @@ def test_synth_fill_rejects(L):
     assert f(FAKE, 0, 10, 6, 0, 1, 1.0, None) == INVALID
     assert f(FAKE, 2, 10, 16, 0, 1, 1.0, None) == INVALID
     assert f(FAKE + 4, 0, 10, 16, 0, 1, 1.0, None) == INVALID
+
+
+def test_dense_layer_calls_reject(L):
+    ws = binding.dlrm_linear_workspace_size(64, 32, 16)
+    assert ws > (32 << 20) and binding.dlrm_linear_workspace_size(0, 32, 16) == 0
+    # the weight gradient of a 16384-row batch is split in 8 slices of 2048 rows
+    assert binding.dlrm_linear_workspace_size(16384, 1024, 1024) >= 8 * 1024 * 1024 * 4
+    f = lambda M=64, N=32, K=16, act=1, yt=1, y=FAKE, wsz=ws: L.dlrm_linear_fwd(FAKE, FAKE, FAKE, M, N, K, act, y, yt,
+                                                                                FAKE, wsz, None)
+    assert f(N=12) == UNSUPPORTED       # rows of 16 bytes: N, K multiples of 8
+    assert f(K=20) == UNSUPPORTED
+    assert f(M=0) == INVALID
+    assert f(act=3) == INVALID
+    assert f(yt=2) == INVALID
+    assert f(y=0) == INVALID
+    assert f(y=FAKE + 8) == INVALID
+    assert f(wsz=ws - 1) == WORKSPACE
+    bw = lambda dy=FAKE, y=FAKE, act=1, dz=FAKE, wsz=ws: L.dlrm_linear_bwd(dy, y, 1, act, FAKE, FAKE, 64, 32, 16, dz,
+                                                                           None, FAKE, FAKE, FAKE, wsz, None)
+    assert bw(dy=0) == INVALID
+    assert bw(y=None, act=1) == INVALID   # ReLU needs the forward output
+    assert bw(dz=0) == INVALID
+    assert bw(wsz=100) == WORKSPACE
+    hws = binding.dlrm_bce_head_workspace_size(64, 256)
+    h = lambda K=256, wsz=hws, x=FAKE: L.dlrm_bce_head(x, FAKE, FAKE, FAKE, 64, K, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                       wsz, None)
+    assert h(K=2048) == UNSUPPORTED
+    assert h(K=12) == UNSUPPORTED
+    assert h(x=0) == INVALID
+    assert h(wsz=hws - 1) == WORKSPACE
+    assert L.dlrm_sgd_dense(FAKE, None, FAKE, -1, 0.1, None) == INVALID
+    assert L.dlrm_sgd_dense(None, None, None, 0, 0.1, None) == OK
+    assert L.dlrm_cast_rows(FAKE, 0, 16, 4, 17, FAKE, 1, 16, None) == INVALID   # cols > dst_cols
+    assert L.dlrm_cast_rows(FAKE, 0, 8, 4, 13, FAKE, 1, 16, None) == INVALID    # cols > src_ld
+    assert L.dlrm_cast_rows(FAKE, 3, 16, 4, 13, FAKE, 1, 16, None) == INVALID
