@@ -231,6 +231,40 @@ int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *
                        int64_t *segment_offsets_out, int32_t *sorted_pos_out,
                        int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream);
 
+/*
+ * The embedding backward in two halves, so that the first can run while the gradient it does
+ * not need is still being computed (emb_bag_bwd_update is emb_bag_bwd_plan followed by
+ * emb_bag_bwd_apply on one stream, with the same results bit for bit).
+ *
+ * emb_bag_bwd_plan: everything that reads only the batch -- the keys, their stable sort (with
+ * the lookup positions, grad rows and weights as payloads), the unique keys and segments --
+ * left in `workspace` for emb_bag_bwd_apply.  It reads no table, state or gradient.
+ *   Arguments as emb_bag_bwd_update (same limits, same optional integer outputs, same flags);
+ *   the workspace is sized by emb_bag_bwd_workspace_size for the same rows, D, B, nnz.
+ *
+ * emb_bag_bwd_apply: the per-segment gradient sums and the update of emb_bag_bwd_update, from
+ * a workspace that a completed emb_bag_bwd_plan with the same rows, D, B and nnz filled
+ * (ordering the two across streams is the caller's: an event, or one stream).
+ *   weighted: nonzero iff the plan was given per-sample weights
+ *   segment_offsets: the plan's segment_offsets_out if it had one, else NULL (the copy in the
+ *     workspace is used)
+ *   tables, state, dtype, grad_pooled, optimizer, lr, eps: as emb_bag_bwd_update
+ * The plan is left unchanged, so it can be applied again (to other tables or another
+ * gradient of the same batch); applications of one workspace must not overlap in time.
+ */
+int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const void *indices,
+                     const void *offsets, int32_t index_type, const float *per_sample_weights,
+                     int64_t B, int64_t nnz, void *workspace, size_t workspace_bytes,
+                     int64_t *unique_keys_out, int64_t *segment_offsets_out,
+                     int32_t *sorted_pos_out, int64_t *num_unique_out, uint32_t flags,
+                     dlrm_stream_t stream);
+
+int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
+                      int32_t D, int32_t dtype, int64_t B, int64_t nnz, int32_t weighted,
+                      const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                      void *workspace, size_t workspace_bytes, const int64_t *segment_offsets,
+                      dlrm_stream_t stream);
+
 /* Static description of a status code. */
 const char *dlrm_status_string(int status);
 

@@ -31,6 +31,8 @@ from .binding import (  # noqa: F401
     dlrm_trace_read,
     emb_bag_bwd_adagrad,
     emb_bag_bwd_update,
+    emb_bag_bwd_plan,
+    emb_bag_bwd_apply,
     emb_bag_bwd_workspace_size,
     emb_bag_fwd,
     emb_bag_fwd_ex,

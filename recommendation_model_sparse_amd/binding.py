@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.emb_bag_fwd_ex.argtypes = [p, p, i32, i32, i32, p, p, i32, p, i64, i64, p, i32, u32, p]
         L.emb_bag_bwd_update.argtypes = [p, p, p, i32, i32, i32, p, p, i32, p, i64, i64, p, i32, f32, f32,
                                          p, sz, p, p, p, p, u32, p]
+        L.emb_bag_bwd_plan.argtypes = [p, i32, i32, p, p, i32, p, i64, i64, p, sz, p, p, p, p, u32, p]
+        L.emb_bag_bwd_apply.argtypes = [p, p, p, i32, i32, i32, i64, i64, i32, p, i32, f32, f32, p, sz, p, p]
         L.dlrm_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p]
         L.emb_bag_interact_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, p, u32, p]
         L.dlrm_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p]
@@ -314,6 +316,48 @@ def emb_bag_bwd_update(tables: Sequence[torch.Tensor], state: Optional[Sequence[
         _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
         _stream(dev)), "emb_bag_bwd_update")
     return o
+
+
+def emb_bag_bwd_plan(rows: Sequence[int], D: int, indices: torch.Tensor, offsets: torch.Tensor,
+                     per_sample_weights: Optional[torch.Tensor], workspace: torch.Tensor,
+                     outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
+    """The batch-only half of the embedding backward (C: emb_bag_bwd_plan), on the current stream
+    of the indices' device; `rows` are the tables' row counts."""
+    T = len(rows)
+    r = (ctypes.c_int64 * T)(*rows)
+    icode = _index_code(indices, offsets)
+    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
+    B = (offsets.numel() - 1) // T
+    nnz = indices.numel()
+    o = outputs
+    _check(lib().emb_bag_bwd_plan(
+        r, T, D, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz, _ptr(workspace), workspace.numel(),
+        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
+        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
+        _stream(indices.device)), "emb_bag_bwd_plan")
+    return o
+
+
+def emb_bag_bwd_apply(tables: Sequence[torch.Tensor], state: Optional[Sequence[torch.Tensor]], B: int, nnz: int,
+                      weighted: bool, grad_pooled: torch.Tensor, optimizer: int, lr: float, eps: float,
+                      workspace: torch.Tensor, outputs: Optional[AdagradOutputs] = None) -> None:
+    """The update half of the embedding backward from a planned workspace (C: emb_bag_bwd_apply);
+    `outputs` is the plan's, when it was given one (its segment offsets are read)."""
+    T, D, code, ptrs, rows = _tables(tables)
+    sptrs = None
+    if state is not None:
+        if len(state) != T:
+            raise ValueError("one state vector per table")
+        for st, t in zip(state, tables):
+            if st.dtype != torch.float32 or st.numel() != t.shape[0] or not st.is_contiguous():
+                raise ValueError("state[t] must be contiguous fp32 [V_t]")
+        sptrs = (ctypes.c_void_p * T)(*[st.data_ptr() for st in state])
+    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
+    _check(lib().emb_bag_bwd_apply(
+        ptrs, sptrs, rows, T, D, code, int(B), int(nnz), 1 if weighted else 0, _ptr(grad_pooled), int(optimizer),
+        float(lr), float(eps), _ptr(workspace), workspace.numel(),
+        _ptr(outputs.segment_offsets) if outputs is not None else None, _stream(tables[0].device)),
+        "emb_bag_bwd_apply")
 
 
 def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) -> None:

@@ -905,49 +905,83 @@ extern "C" size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int
     return make_layout(D, nnz).total;
 }
 
-extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *rows,
-                                  int32_t T, int32_t D, int32_t dtype, const void *indices,
-                                  const void *offsets, int32_t index_type,
-                                  const float *per_sample_weights, int64_t B, int64_t nnz,
-                                  const float *grad_pooled, int32_t optimizer, float lr, float eps,
-                                  void *workspace, size_t workspace_bytes, int64_t *unique_keys_out,
-                                  int64_t *segment_offsets_out, int32_t *sorted_pos_out,
-                                  int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream_) {
+namespace dlrm {
+namespace {
+
+__global__ void k_zero_u32(uint32_t *p) { *p = 0; }
+
+// What a plan leaves in the workspace and where: fixed by (rows, D, nnz, weighted).
+struct PlanShape {
+    Layout L;
+    uint64_t sumV;
+    int passes;
+    int rb;
+    int cur;  // ping-pong half holding the sorted keys and payloads
+};
+
+int plan_shape(const int64_t *rows, int32_t T, int32_t D, int64_t nnz, PlanShape *ps) {
+    uint64_t sumV = 0;
+    for (int t = 0; t < T; ++t) sumV += static_cast<uint64_t>(rows[t]);
+    if (sumV > (uint64_t(1) << 32)) return DLRM_ERR_UNSUPPORTED;
+    ps->L = make_layout(D, nnz);
+    ps->sumV = sumV;
+    // passes over the significant bits of the largest key (sumV - 1), digits of 8..10 bits chosen
+    // for the fewest passes
+    int bits = 0;
+    while (bits < 32 && ((sumV - 1) >> bits) != 0) ++bits;
+    ps->passes = (bits + 9) / 10;
+    ps->rb = ps->passes > 0 ? (bits + ps->passes - 1) / ps->passes : 8;
+    if (ps->rb < 8) ps->rb = 8;
+    ps->cur = ps->passes & 1;
+    return DLRM_OK;
+}
+
+int check_rows(const int64_t *rows, int32_t T) {
+    if (T < 1 || T > kMaxTables || !rows) return DLRM_ERR_INVALID_ARG;
+    for (int t = 0; t < T; ++t)
+        if (rows[t] < 1) return DLRM_ERR_INVALID_ARG;
+    return DLRM_OK;
+}
+
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const void *indices,
+                                const void *offsets, int32_t index_type, const float *per_sample_weights,
+                                int64_t B, int64_t nnz, void *workspace, size_t workspace_bytes,
+                                int64_t *unique_keys_out, int64_t *segment_offsets_out, int32_t *sorted_pos_out,
+                                int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream_) {
     using namespace dlrm;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     if (index_type != DLRM_INDEX_I64 && index_type != DLRM_INDEX_I32) return DLRM_ERR_INVALID_ARG;
-    if (optimizer != DLRM_OPT_ADAGRAD && optimizer != DLRM_OPT_SGD) return DLRM_ERR_INVALID_ARG;
-    int rc = check_batch(const_cast<const void *const *>(tables), rows, T, D, dtype, indices,
-                         offsets, index_type, per_sample_weights, B, nnz);
+    int rc = check_rows(rows, T);
+    if (rc != DLRM_OK) return rc;
+    // the batch checks of the forward, with placeholder (never read) table pointers
+    const void *fake_tables[kMaxTables];
+    for (int t = 0; t < T; ++t) fake_tables[t] = reinterpret_cast<const void *>(uintptr_t(256));
+    rc = check_batch(fake_tables, rows, T, D, DLRM_F32, indices, offsets, index_type, per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     if (flags & ~DLRM_FLAG_CHECK_INDICES) return DLRM_ERR_INVALID_ARG;
     int G, W;
-    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
-    const bool adagrad = optimizer == DLRM_OPT_ADAGRAD;
-    if (adagrad && !state) return DLRM_ERR_INVALID_ARG;
-    uint64_t sumV = 0;
-    for (int t = 0; t < T; ++t) {
-        if (adagrad && (!state[t] || !aligned(state[t], 4))) return DLRM_ERR_INVALID_ARG;
-        sumV += static_cast<uint64_t>(rows[t]);
-    }
-    if (sumV > (uint64_t(1) << 32)) return DLRM_ERR_UNSUPPORTED;
-    if (nnz > 0 && (!grad_pooled || !aligned(grad_pooled, 16))) return DLRM_ERR_INVALID_ARG;
+    if (!bwd_geometry(D, &G, &W)) return DLRM_ERR_UNSUPPORTED;
     if (B == 0 && nnz != 0) return DLRM_ERR_INVALID_ARG;
-    const Layout L = make_layout(D, nnz);
+    PlanShape ps;
+    rc = plan_shape(rows, T, D, nnz, &ps);
+    if (rc != DLRM_OK) return rc;
+    const Layout &L = ps.L;
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)) return DLRM_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
     auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
 
     if (flags & DLRM_FLAG_CHECK_INDICES) {
-        rc = check_csr_on_device(rows, T, indices, offsets, index_type, B, nnz,
-                                 reinterpret_cast<int *>(ws + L.flag), stream);
+        rc = check_csr_on_device(rows, T, indices, offsets, index_type, B, nnz, reinterpret_cast<int *>(ws + L.flag),
+                                 stream);
         if (rc != DLRM_OK) return rc;
     }
-    const bool want_seg = unique_keys_out || segment_offsets_out || num_unique_out;
     if (nnz == 0) {
-        if (want_seg)
+        if (unique_keys_out || segment_offsets_out || num_unique_out)
             DLRM_LAUNCH("empty_outputs", k_empty_outputs, dim3(1), dim3(1), 0, stream, num_unique_out,
-                               segment_offsets_out);
+                        segment_offsets_out);
         return launch_status();
     }
     const uint32_t n = static_cast<uint32_t>(nnz);
@@ -976,17 +1010,11 @@ extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, cons
     else
         DLRM_LAUNCH("expand", k_expand<int64_t>, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
-    // K5: passes over the significant bits of the largest key (sumV - 1), digits of 8..10 bits
-    // chosen for the fewest passes
-    int bits = 0;
-    while (bits < 32 && ((sumV - 1) >> bits) != 0) ++bits;
-    const int passes = (bits + 9) / 10;
-    int rb = passes > 0 ? (bits + passes - 1) / passes : 8;
-    if (rb < 8) rb = 8;
+    // K5
     int cur = 0;
     uint32_t *counts = u32(L.counts), *totals = u32(L.totals);
-    for (int p = 0; p < passes; ++p) {
-        const bool last = p + 1 == passes;
+    for (int p = 0; p < ps.passes; ++p) {
+        const bool last = p + 1 == ps.passes;
         SortIO io{};
         io.kin = u32(L.keys[cur]);
         io.kout = u32(L.keys[cur ^ 1]);
@@ -996,47 +1024,80 @@ extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, cons
         io.pout[1] = u32(L.grow[cur ^ 1]);
         io.pin[2] = u32(L.wgt[cur]);
         io.pout[2] = u32(L.wgt[cur ^ 1]);
-        if (rb == 8) launch_radix_pass<8>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
-        else if (rb == 9) launch_radix_pass<9>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
-        else launch_radix_pass<10>(io, NP, n, rb * p, counts, L.nblk, totals, stream);
+        if (ps.rb == 8) launch_radix_pass<8>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
+        else if (ps.rb == 9) launch_radix_pass<9>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
+        else launch_radix_pass<10>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
         cur ^= 1;
     }
     const uint32_t *skeys = u32(L.keys[cur]);
-    if (sorted_pos_out && passes == 0) {
-        if (hipMemcpyAsync(sorted_pos_out, u32(L.pos[0]), sizeof(uint32_t) * n,
-                           hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    if (sorted_pos_out && ps.passes == 0) {
+        if (hipMemcpyAsync(sorted_pos_out, u32(L.pos[0]), sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, stream) !=
+            hipSuccess)
             return DLRM_ERR_HIP;
     }
 
-    // K6 (always: K7's finisher reads the segment offsets)
+    // K6 (always: the update's finisher reads the segment offsets)
     uint32_t *seg_count = u32(L.seg_count);
-    int64_t *seg_offsets = segment_offsets_out ? segment_offsets_out
-                                               : reinterpret_cast<int64_t *>(ws + L.seg_offsets);
-    uint32_t *chunk_seg = u32(L.chunk_seg);
+    int64_t *seg_offsets = segment_offsets_out ? segment_offsets_out : reinterpret_cast<int64_t *>(ws + L.seg_offsets);
     DLRM_LAUNCH("seg_count", k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
-    DLRM_LAUNCH("seg_scan", k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n,
-                       num_unique_out, seg_offsets, u32(L.fin_count));
-    DLRM_LAUNCH("seg_write", k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count,
-                       unique_keys_out, seg_offsets, chunk_seg, static_cast<uint32_t>(L.CS));
+    DLRM_LAUNCH("seg_scan", k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n, num_unique_out,
+                seg_offsets, u32(L.fin_count));
+    DLRM_LAUNCH("seg_write", k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count, unique_keys_out,
+                seg_offsets, u32(L.chunk_seg), static_cast<uint32_t>(L.CS));
+    return launch_status();
+}
 
-    // K7
+extern "C" int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
+                                 int32_t D, int32_t dtype, int64_t B, int64_t nnz, int32_t weighted,
+                                 const float *grad_pooled, int32_t optimizer, float lr, float eps, void *workspace,
+                                 size_t workspace_bytes, const int64_t *segment_offsets, dlrm_stream_t stream_) {
+    using namespace dlrm;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (optimizer != DLRM_OPT_ADAGRAD && optimizer != DLRM_OPT_SGD) return DLRM_ERR_INVALID_ARG;
+    int rc = check_rows(rows, T);
+    if (rc != DLRM_OK) return rc;
+    if (!tables || D < 1 || B < 0 || nnz < 0) return DLRM_ERR_INVALID_ARG;
+    if (dtype != DLRM_F32 && dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
+    int G, W;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    if (nnz >= (int64_t(1) << 31) || static_cast<int64_t>(T) * B >= (int64_t(1) << 31)) return DLRM_ERR_UNSUPPORTED;
+    const bool adagrad = optimizer == DLRM_OPT_ADAGRAD;
+    if (adagrad && !state) return DLRM_ERR_INVALID_ARG;
+    for (int t = 0; t < T; ++t) {
+        if (!tables[t] || !aligned(tables[t], 16)) return DLRM_ERR_INVALID_ARG;
+        if (adagrad && (!state[t] || !aligned(state[t], 4))) return DLRM_ERR_INVALID_ARG;
+    }
+    if (nnz > 0 && (!grad_pooled || !aligned(grad_pooled, 16))) return DLRM_ERR_INVALID_ARG;
+    PlanShape ps;
+    rc = plan_shape(rows, T, D, nnz, &ps);
+    if (rc != DLRM_OK) return rc;
+    const Layout &L = ps.L;
+    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)) return DLRM_ERR_WORKSPACE;
+    if (nnz == 0) return DLRM_OK;
+    char *ws = static_cast<char *>(workspace);
+    auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
+
+    // the finisher worklist of this update starts empty (so a plan may be applied more than once)
+    DLRM_LAUNCH("zero_u32", k_zero_u32, dim3(1), dim3(1), 0, stream, u32(L.fin_count));
     AdagradArgs a{};
+    uint64_t acc_rows = 0;
     for (int t = 0; t < T; ++t) {
         a.tables[t] = static_cast<char *>(tables[t]);
         a.state[t] = adagrad ? state[t] : nullptr;
-        a.rowbase[t] = ea.rowbase[t];
+        a.rowbase[t] = static_cast<uint32_t>(acc_rows);
+        acc_rows += static_cast<uint64_t>(rows[t]);
     }
-    a.skeys = skeys;
-    a.sgrow = u32(L.grow[cur]);
-    a.swgt = reinterpret_cast<const float *>(u32(L.wgt[cur]));
+    a.skeys = u32(L.keys[ps.cur]);
+    a.sgrow = u32(L.grow[ps.cur]);
+    a.swgt = reinterpret_cast<const float *>(u32(L.wgt[ps.cur]));
     a.grad = grad_pooled;
-    a.seg_offsets = seg_offsets;
-    a.chunk_seg = chunk_seg;
+    a.seg_offsets = segment_offsets ? segment_offsets : reinterpret_cast<const int64_t *>(ws + L.seg_offsets);
+    a.chunk_seg = u32(L.chunk_seg);
     a.fin_count = u32(L.fin_count);
     a.fin_list = u32(L.fin_list);
     a.part_a = reinterpret_cast<float *>(ws + L.part_a);
     a.part_b = reinterpret_cast<float *>(ws + L.part_b);
-    a.n = n;
+    a.n = static_cast<uint32_t>(nnz);
     a.nchunk = L.nchunk;
     a.T = T;
     a.D = D;
@@ -1044,14 +1105,46 @@ extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, cons
     a.lr = lr;
     a.eps = eps;
     a.inv_D = 1.0f / static_cast<float>(D);
+    const bool w = weighted != 0;
     if (adagrad) {
-        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_ADAGRAD>(a, L.G, L.W, weighted, stream);
-        else dispatch_k7<DLRM_BF16, DLRM_OPT_ADAGRAD>(a, L.G, L.W, weighted, stream);
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, stream);
     } else {
-        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_SGD>(a, L.G, L.W, weighted, stream);
-        else dispatch_k7<DLRM_BF16, DLRM_OPT_SGD>(a, L.G, L.W, weighted, stream);
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_SGD>(a, L.G, L.W, w, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_SGD>(a, L.G, L.W, w, stream);
     }
     return launch_status();
+}
+
+extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *rows,
+                                  int32_t T, int32_t D, int32_t dtype, const void *indices,
+                                  const void *offsets, int32_t index_type,
+                                  const float *per_sample_weights, int64_t B, int64_t nnz,
+                                  const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                                  void *workspace, size_t workspace_bytes, int64_t *unique_keys_out,
+                                  int64_t *segment_offsets_out, int32_t *sorted_pos_out,
+                                  int64_t *num_unique_out, uint32_t flags, dlrm_stream_t stream) {
+    using namespace dlrm;
+    // the update's own checks first, so that an invalid call enqueues nothing
+    if (optimizer != DLRM_OPT_ADAGRAD && optimizer != DLRM_OPT_SGD) return DLRM_ERR_INVALID_ARG;
+    int rc = check_batch(const_cast<const void *const *>(tables), rows, T, D, dtype, indices, offsets, index_type,
+                         per_sample_weights, B, nnz);
+    if (rc != DLRM_OK) return rc;
+    int G, W;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    if (optimizer == DLRM_OPT_ADAGRAD) {
+        if (!state) return DLRM_ERR_INVALID_ARG;
+        for (int t = 0; t < T; ++t)
+            if (!state[t] || !aligned(state[t], 4)) return DLRM_ERR_INVALID_ARG;
+    }
+    if (nnz > 0 && (!grad_pooled || !aligned(grad_pooled, 16))) return DLRM_ERR_INVALID_ARG;
+    rc = emb_bag_bwd_plan(rows, T, D, indices, offsets, index_type, per_sample_weights, B, nnz, workspace,
+                          workspace_bytes, unique_keys_out, segment_offsets_out, sorted_pos_out, num_unique_out,
+                          flags, stream);
+    if (rc != DLRM_OK) return rc;
+    return emb_bag_bwd_apply(tables, state, rows, T, D, dtype, B, nnz, per_sample_weights != nullptr ? 1 : 0,
+                             grad_pooled, optimizer, lr, eps, workspace, workspace_bytes, segment_offsets_out,
+                             stream);
 }
 
 extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows,

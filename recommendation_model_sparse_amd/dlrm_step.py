@@ -54,8 +54,11 @@ class DlrmStep:
 
     def __init__(self, tables: Sequence[torch.Tensor], states: Sequence[torch.Tensor], B: int, n_dense: int,
                  bottom: Sequence[int], top: Sequence[int], lr_dense: float, lr_emb: float, eps: float,
-                 seed: int, max_nnz: int):
+                 seed: int, max_nnz: int, overlap: bool = True):
         self.tables, self.states = list(tables), list(states)
+        # overlap: the batch-only half of the embedding backward (key sort and segments) runs on a
+        # second stream while the top MLP and interaction backward run on the caller's stream
+        self.overlap = overlap
         dev = self.tables[0].device
         self.dev = dev
         self.B, self.T, self.D = B, len(tables), tables[0].shape[1]
@@ -102,7 +105,10 @@ class DlrmStep:
                          "dx": torch.empty((B, top[-1]), **f32), "dw": torch.empty(top[-1], **f32),
                          "db": torch.empty(1, **f32)}
         rows = [t.shape[0] for t in self.tables]
+        self.rows = rows
         self.emb_ws = torch.empty(L.emb_bag_bwd_workspace_size(rows, self.D, B, max_nnz), dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)  # default priority
+        self.plan_done = torch.cuda.Event()
 
     def _mat(self, flat: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
         return flat[:rows * cols].view(rows, cols)
@@ -128,6 +134,13 @@ class DlrmStep:
 
     def backward_and_update(self, idx: torch.Tensor, off: torch.Tensor, outputs=None):
         B = self.B
+        if self.overlap:
+            main = torch.cuda.current_stream(self.dev)
+            # after everything already on the caller's stream (the previous update read the workspace)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                L.emb_bag_bwd_plan(self.rows, self.D, idx, off, None, self.emb_ws, outputs=outputs)
+                self.plan_done.record(self.side)
         # head: its own gradients came with the forward
         dy = self.head_out["dx"]
         ins = [self.t0] + self.ht[:-1]
@@ -142,8 +155,13 @@ class DlrmStep:
             dy = dx
         L.dlrm_cast_rows(dy, self.I, self.I, torch.float32, dst=self.dinter)  # drop the pad column
         L.dlrm_interact_bwd(self.dinter, self.hb[-1], self.pooled, grad_dense=self.gdense, grad_pooled=self.gpooled)
-        L.emb_bag_bwd_adagrad(self.tables, self.states, idx, off, None, self.gpooled, self.lr_emb, self.eps,
-                              workspace=self.emb_ws, outputs=outputs)
+        if self.overlap:
+            main.wait_event(self.plan_done)
+            L.emb_bag_bwd_apply(self.tables, self.states, B, idx.numel(), False, self.gpooled, L.DLRM_OPT_ADAGRAD,
+                                self.lr_emb, self.eps, self.emb_ws, outputs=outputs)
+        else:
+            L.emb_bag_bwd_adagrad(self.tables, self.states, idx, off, None, self.gpooled, self.lr_emb, self.eps,
+                                  workspace=self.emb_ws, outputs=outputs)
         dy = self.gdense
         ins = [self.x0] + self.hb[:-1]
         for i in range(len(self.bottom) - 1, -1, -1):

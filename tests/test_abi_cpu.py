@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"emb_bag_fwd", "emb_bag_fwd_ex", "emb_bag_bwd_update", "emb_bag_interact_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
+    assert {"emb_bag_fwd", "emb_bag_fwd_ex", "emb_bag_bwd_update", "emb_bag_bwd_plan", "emb_bag_bwd_apply", "emb_bag_interact_fwd", "dlrm_interact_fwd", "dlrm_interact_bwd", "emb_bag_bwd_workspace_size",
             "emb_bag_bwd_adagrad", "dlrm_status_string", "dlrm_synth_fill_table",
             "dlrm_trace_enable", "dlrm_trace_read"} <= names
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
@@ -126,6 +126,46 @@ def test_emb_bag_bwd_update_rejects(L):
     assert upd(L, optimizer=1, state=False, wsz=1) == WORKSPACE  # SGD takes no state; reaches the workspace check
     assert upd(L, index_type=1, idx=FAKE + 2) == INVALID
     assert upd(L, D=24) == UNSUPPORTED
+
+
+def plan(L, T=1, D=16, index_type=0, wsz=None, flags=0, rows=None, idx=FAKE):
+    rows = [10] * T if rows is None else rows
+    if wsz is None:
+        wsz = binding.emb_bag_bwd_workspace_size(rows, D, 4, 4)
+    return L.emb_bag_bwd_plan(i64s(*rows), T, D, idx, FAKE, index_type, None, 4, 4, FAKE, wsz, None, None,
+                              None, None, flags, None)
+
+
+def test_emb_bag_bwd_plan_rejects(L):
+    assert plan(L, index_type=5) == INVALID
+    assert plan(L, T=0, rows=[]) == INVALID
+    assert plan(L, D=24) == UNSUPPORTED
+    assert plan(L, flags=4) == INVALID
+    assert plan(L, wsz=1) == WORKSPACE
+    assert plan(L, index_type=1, idx=FAKE + 2) == INVALID
+    assert plan(L, T=2, rows=[2 ** 31, 2 ** 31 + 1], wsz=1 << 20) == UNSUPPORTED  # keys over 32 bits
+
+
+def apply(L, optimizer=0, state=True, T=1, D=16, dtype=0, grad=FAKE, wsz=None, tables=None):
+    rows = [10] * T
+    st = ptrs(*[FAKE] * T) if state else None
+    if wsz is None:
+        wsz = binding.emb_bag_bwd_workspace_size(rows, D, 4, 4)
+    tabs = ptrs(*[FAKE] * T) if tables is None else tables
+    return L.emb_bag_bwd_apply(tabs, st, i64s(*rows), T, D, dtype, 4, 4, 0, grad, optimizer, 0.01, 1e-8, FAKE,
+                               wsz, None, None)
+
+
+def test_emb_bag_bwd_apply_rejects(L):
+    assert apply(L, optimizer=2) == INVALID
+    assert apply(L, state=False) == INVALID                 # Adagrad needs its state
+    assert apply(L, optimizer=1, state=False, wsz=1) == WORKSPACE
+    assert apply(L, D=24) == UNSUPPORTED
+    assert apply(L, D=4, dtype=1) == UNSUPPORTED            # bf16 rows under 16 bytes
+    assert apply(L, dtype=3) == INVALID
+    assert apply(L, grad=FAKE + 4) == INVALID               # grad_pooled 16-byte aligned
+    assert apply(L, tables=ptrs(FAKE + 8)) == INVALID
+    assert apply(L, wsz=1) == WORKSPACE
 
 
 def fused(L, T=2, D=32, dtype=0, rows=None, tables=None, dense=FAKE, out=FAKE, B=4, nnz=4, flags=0):

@@ -27,7 +27,8 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return synth.bf16_bits_to_f32(h).astype(np.float64) if t.dtype == torch.bfloat16 else h.astype(np.float64)
 
 
-def test_full_training_step():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_full_training_step(overlap):
     wl = Workload(name="step", seed=4242, T=8, D=64, dtype="bf16", B=512,
                   rows=[1000, 50000, 3000, 7, 20000, 900, 12345, 64], init="hash", bags="geom",
                   bag_lo=1, bag_hi=20, bag_mean=5.0, dist="zipf", alpha=1.05)
@@ -35,9 +36,9 @@ def test_full_training_step():
     feats, labels = b.features(13), b.labels()
     tabs = device_tables(wl)
     states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
-    say(f"[step] T={wl.T} D={wl.D} B={wl.B} nnz={b.nnz}")
+    say(f"[step] T={wl.T} D={wl.D} B={wl.B} nnz={b.nnz} overlap={overlap}")
     m = DlrmStep(tabs, states, wl.B, 13, bottom=[64, 64], top=[128, 64], lr_dense=0.05, lr_emb=0.01,
-                 eps=1e-8, seed=7, max_nnz=b.nnz)
+                 eps=1e-8, seed=7, max_nnz=b.nnz, overlap=overlap)
     before = {id(l): (f64(l.W16), l.b.cpu().numpy().astype(np.float64), l.W32.cpu().numpy().copy(),
                       l.b.cpu().numpy().copy()) for l in m.bottom + m.top + [m.head]}
     idx, off = to_dev(b.indices), to_dev(b.offsets)
