@@ -409,13 +409,19 @@ def main():
     # algorithmic bytes per launch of the main kernels
     alg = {
         "pool_wave_per_bag": gathered + nnz_avg * 8 + (T * B + 1) * 8 + B * T * D * 4,
-        "seg_reduce_adagrad": nnz_avg * (4 * D + 8) + U_last * (2 * D * es + 8),
+        # sorted key + grad-row index per lookup, each pooled-gradient row once (the kernel reads
+        # it once per lookup: the re-reads are served by L2 / Infinity Cache or count in traffic),
+        # each touched table row read and written, its state read and written
+        "seg_reduce_adagrad": nnz_avg * 8 + B * T * D * 4 + U_last * (2 * D * es + 8),
         "interact_fwd_mfma": B * (N * D * 4 + (P + D) * 4),
         "interact_bwd": B * ((P + D) * 4 + 2 * N * D * 4),
         "radix_scatter": nnz_avg * 3 * 4 * 2,
         "radix_hist": nnz_avg * 4,
         "expand": nnz_avg * (8 + 4 * 3) + (T * B + 1) * 8,
     }
+    # what the kernels load including re-reads (one gradient row per lookup in the backward)
+    requested = {"seg_reduce_adagrad": nnz_avg * (4 * D + 8) + U_last * (2 * D * es + 8),
+                 "pool_wave_per_bag": alg["pool_wave_per_bag"]}
     kernels = {}
     for k, b_alg in alg.items():
         if k in kern_launch_ms:
@@ -462,6 +468,7 @@ def main():
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      "ms_per_launch": kern_launch_ms[dominant],
+                     "requested_bytes_per_launch": requested.get(dominant),
                      "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
         "kernels": kernels,
         "inference": inference_summary(inf, wl, nnz_avg),

@@ -719,6 +719,18 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     }
     bool open_before = !(starts & 1ull);  // the first piece began in an earlier chunk
     const bool runs_past = hi < a.n && a.skeys[hi] == a.skeys[hi - 1];
+    // A segment that begins in one chunk and ends inside the next (before that chunk's last
+    // position) belongs wholly to the chunk where it begins: that group reads on into the next
+    // chunk and updates the row; the next chunk's group skips the segment's head.  Only longer
+    // segments are cut into per-chunk partials for the finisher.
+    uint32_t r_begin = 0;
+    if (open_before) {
+        const uint32_t s0 = static_cast<uint32_t>(a.seg_offsets[a.chunk_seg[chunk - 1]]);
+        if (s0 + CS >= lo) {  // began in the previous chunk, which finishes it
+            r_begin = static_cast<uint32_t>(__builtin_ctzll(starts));
+            open_before = false;
+        }
+    }
 
     float acc[W];
 #pragma unroll
@@ -738,7 +750,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         uint32_t gr[U][W], tr[U][TW::N];
         float st[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) mu[u] = pm[min(r0 + u, cnt - 1)];
+        for (int u = 0; u < U; ++u) mu[u] = pm[min(max(r0 + u, r_begin), cnt - 1)];
 #pragma unroll
         for (int u = 0; u < U; ++u) gload_words<W>(mu[u].grad_row + c * W, gr[u]);
 #pragma unroll
@@ -753,8 +765,9 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         for (int u = 0; u < U; ++u) {
             const uint32_t r = r0 + u;
             if (r >= cnt) break;
+            if (r < r_begin) continue;
             if ((starts >> r) & 1ull) {
-                if (r > 0) {  // the previous piece ended inside this chunk
+                if (r > r_begin) {  // the previous piece ended inside this chunk
                     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
                     else update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
                 }
@@ -775,8 +788,53 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         }
     }
     // the last piece of the chunk
+    uint32_t seg_end = 0;  // end of the last segment, when it runs past the chunk
+    if (!open_before && runs_past) seg_end = static_cast<uint32_t>(a.seg_offsets[a.chunk_seg[chunk] + 1]);
+    const bool carry_on = runs_past && seg_end < min(hi + CS, a.n);
     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    else if (runs_past) {
+    else if (carry_on) {
+        // read on to the segment's end in the next chunk (fewer than CS positions), then update
+        const uint32_t m = seg_end - hi;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // every lane is done with this chunk's metadata
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+            const uint32_t r = c + k * G;
+            const uint32_t kk = hi + min(r, m - 1);
+            PosMeta p;
+            p.grad_row = a.grad + static_cast<uint64_t>(a.sgrow[kk]) * a.D;
+            p.tab_row = nullptr;
+            p.state = nullptr;
+            p.w = WEIGHTED ? a.swgt[kk] : 1.f;
+            p.pad = 0;
+            if (r < m) pm[r] = p;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (uint32_t r0 = 0; r0 < m; r0 += U) {
+            uint32_t gr[U][W];
+            float wu[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const PosMeta &p = pm[min(r0 + u, m - 1)];
+                gload_words<W>(p.grad_row + c * W, gr[u]);
+                wu[u] = p.w;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (r0 + u < m) {
+#pragma unroll
+                    for (int e = 0; e < W; ++e) {
+                        const float g = __uint_as_float(gr[u][e]);
+                        acc[e] = WEIGHTED ? fmaf(wu[u], g, acc[e]) : acc[e] + g;
+                    }
+                }
+            }
+        }
+        update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+    } else if (runs_past) {
         store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
         // the segment starting here crosses into later chunks: queue it for the finisher
         // (list order is arbitrary; each entry's work is fixed, so results do not depend on it)
