@@ -659,6 +659,15 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
     if (chunk >= a.nchunk) return;  // group-uniform
     const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n), cnt = hi - lo;
     PosMeta *pm = meta[wv][grp];
+    // Keys that place the chunk's first and last segments against the neighbouring chunks, read
+    // now (unconditionally, clamped in bounds) and used later: the key just before the previous
+    // chunk, the chunk's first and last keys, the next position's key and the next chunk's last.
+    const uint32_t e_next = min(hi + CS, a.n);  // end of the next chunk
+    const uint32_t key_pp = a.skeys[chunk >= 2 ? lo - CS - 1 : 0];
+    const uint32_t key_lo = a.skeys[lo];
+    const uint32_t key_last = a.skeys[hi - 1];
+    const uint32_t key_hi = a.skeys[min(hi, a.n - 1)];
+    const uint32_t key_e = a.skeys[e_next - 1];
 
     // build the chunk's metadata: lane c owns positions lo + c + m*G
     uint64_t starts = 0;  // bit r: position lo + r opens a segment
@@ -718,97 +727,103 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         return;
     }
     bool open_before = !(starts & 1ull);  // the first piece began in an earlier chunk
-    const bool runs_past = hi < a.n && a.skeys[hi] == a.skeys[hi - 1];
+    const bool runs_past = hi < a.n && key_hi == key_last;
     // A segment that begins in one chunk and ends inside the next (before that chunk's last
     // position) belongs wholly to the chunk where it begins: that group reads on into the next
     // chunk and updates the row; the next chunk's group skips the segment's head.  Only longer
-    // segments are cut into per-chunk partials for the finisher.
+    // segments are cut into per-chunk partials for the finisher.  Keys are sorted, so the open
+    // segment began inside the previous chunk iff the position before that chunk holds another
+    // key, and the last segment ends inside the next chunk iff that chunk's last key differs.
     uint32_t r_begin = 0;
-    if (open_before) {
-        const uint32_t s0 = static_cast<uint32_t>(a.seg_offsets[a.chunk_seg[chunk - 1]]);
-        if (s0 + CS >= lo) {  // began in the previous chunk, which finishes it
-            r_begin = static_cast<uint32_t>(__builtin_ctzll(starts));
-            open_before = false;
-        }
+    if (open_before && (chunk < 2 || key_pp != key_lo)) {  // the previous chunk finishes it
+        r_begin = static_cast<uint32_t>(__builtin_ctzll(starts));
+        open_before = false;
     }
 
     float acc[W];
 #pragma unroll
     for (int e = 0; e < W; ++e) acc[e] = 0.f;
-    char *cur_row_ptr = nullptr;
-    float *cur_state = nullptr;
+    // the open segment: where it starts in the chunk (its table row and state pointers are
+    // read back from the chunk's metadata when it is flushed), and its row and state as loaded
+    uint32_t cur_r = 0;
     uint32_t cur_row[TW::N];
     float cur_s = 0.f;
 #pragma unroll
     for (int e = 0; e < TW::N; ++e) cur_row[e] = 0u;
+    auto flush = [&](uint32_t rs) {
+        const PosMeta &p = pm[rs];
+        update_row<DT, W, G, OPT>(a, p.tab_row + c * W * ES, p.state, c, acc, cur_row, cur_s);
+    };
 
     for (uint32_t r0 = 0; r0 < cnt; r0 += U) {
-        // Every load below is unconditional (positions past the chunk re-read its last one,
-        // positions that open no segment re-read their own gradient row in place of a table
-        // row), so no branch separates the loads and all of them are in flight together.
-        PosMeta mu[U];
+        // Every load below is unconditional (positions outside [r_begin, cnt) re-read a position
+        // inside it), and every loaded value is consumed by a select rather than under a branch,
+        // so the compiler neither sinks a load into a branch nor splits the batch: all of them
+        // are in flight together, issued in the order they are used.
         uint32_t gr[U][W], tr[U][TW::N];
-        float st[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) mu[u] = pm[min(max(r0 + u, r_begin), cnt - 1)];
-#pragma unroll
-        for (int u = 0; u < U; ++u) gload_words<W>(mu[u].grad_row + c * W, gr[u]);
+        float st[U], wu[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool s_u = (starts >> (r0 + u)) & 1ull;  // bits past cnt are 0
-            if (s_u) {  // table row and state only where a segment starts
-                gload_words<TW::N>(mu[u].tab_row + c * W * ES, tr[u]);
-                st[u] = OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)mu[u].state : 0.f;
-            }
+            const PosMeta &p = pm[min(max(r0 + u, r_begin), cnt - 1)];
+            gload_words<W>(p.grad_row + c * W, gr[u]);
+            // the table row and state of the position's key: used where a segment starts, and
+            // loaded at every position (the row of the segment already being read: a cache hit)
+            gload_words<TW::N>(p.tab_row + c * W * ES, tr[u]);
+            st[u] = OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)p.state : 0.f;
+            wu[u] = WEIGHTED ? p.w : 1.f;
+            __builtin_amdgcn_sched_barrier(0);  // issue in use order: position u's loads arrive first
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t r = r0 + u;
-            if (r >= cnt) break;
-            if (r < r_begin) continue;
-            if ((starts >> r) & 1ull) {
+            const bool valid = r < cnt && r >= r_begin;
+            const bool s_u = valid && ((starts >> (r & 63u)) & 1ull);
+            if (s_u) {
                 if (r > r_begin) {  // the previous piece ended inside this chunk
                     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-                    else update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+                    else flush(cur_r);
                 }
-                open_before = false;
-                cur_row_ptr = mu[u].tab_row + c * W * ES;
-                cur_state = mu[u].state;
-                cur_s = st[u];
-#pragma unroll
-                for (int e = 0; e < TW::N; ++e) cur_row[e] = tr[u][e];
 #pragma unroll
                 for (int e = 0; e < W; ++e) acc[e] = 0.f;
             }
+            open_before = open_before && !s_u;
+            cur_r = s_u ? r : cur_r;
+            cur_s = s_u ? st[u] : cur_s;
+#pragma unroll
+            for (int e = 0; e < TW::N; ++e) cur_row[e] = s_u ? tr[u][e] : cur_row[e];
 #pragma unroll
             for (int e = 0; e < W; ++e) {
-                const float g = __uint_as_float(gr[u][e]);
-                acc[e] = WEIGHTED ? fmaf(mu[u].w, g, acc[e]) : acc[e] + g;
+                const float g = valid ? __uint_as_float(gr[u][e]) : 0.f;
+                acc[e] = WEIGHTED ? fmaf(valid ? wu[u] : 0.f, g, acc[e]) : acc[e] + g;
             }
         }
     }
     // the last piece of the chunk
-    uint32_t seg_end = 0;  // end of the last segment, when it runs past the chunk
-    if (!open_before && runs_past) seg_end = static_cast<uint32_t>(a.seg_offsets[a.chunk_seg[chunk] + 1]);
-    const bool carry_on = runs_past && seg_end < min(hi + CS, a.n);
+    const bool carry_on = runs_past && key_e != key_last;
     if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
     else if (carry_on) {
         // read on to the segment's end in the next chunk (fewer than CS positions), then update
-        const uint32_t m = seg_end - hi;
+        const uint32_t span = e_next - hi;  // positions of the next chunk
+        char *row_ptr = pm[cur_r].tab_row + c * W * ES;
+        float *st_ptr = pm[cur_r].state;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();  // every lane is done with this chunk's metadata
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint32_t m = 0;  // positions of the segment in the next chunk: its keys equal key_last
 #pragma unroll
         for (int k = 0; k < MP; ++k) {
             const uint32_t r = c + k * G;
-            const uint32_t kk = hi + min(r, m - 1);
+            const uint32_t kk = hi + min(r, span - 1);
+            const bool same = r < span && a.skeys[kk] == key_last;
             PosMeta p;
             p.grad_row = a.grad + static_cast<uint64_t>(a.sgrow[kk]) * a.D;
             p.tab_row = nullptr;
             p.state = nullptr;
             p.w = WEIGHTED ? a.swgt[kk] : 1.f;
             p.pad = 0;
-            if (r < m) pm[r] = p;
+            if (same) pm[r] = p;
+            const uint64_t bal = __ballot(same);
+            m += static_cast<uint32_t>(__popcll((bal >> (grp * G)) & (G == 64 ? ~0ull : ((1ull << G) - 1))));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -833,14 +848,14 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
                 }
             }
         }
-        update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+        update_row<DT, W, G, OPT>(a, row_ptr, st_ptr, c, acc, cur_row, cur_s);
     } else if (runs_past) {
         store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
         // the segment starting here crosses into later chunks: queue it for the finisher
         // (list order is arbitrary; each entry's work is fixed, so results do not depend on it)
         if (c == 0) a.fin_list[atomicAdd(a.fin_count, 1u)] = chunk;
     } else {
-        update_row<DT, W, G, OPT>(a, cur_row_ptr, cur_state, c, acc, cur_row, cur_s);
+        flush(cur_r);
     }
 }
 
