@@ -648,10 +648,10 @@ __device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, floa
 // Per sorted position, staged in LDS by the lane that owns it and read back as broadcasts.
 struct PosMeta {
     const float *grad_row;  // grad_pooled row of the position
-    char *tab_row;          // table row it updates (only where a segment starts)
-    float *state;           // that row's accumulator (only where a segment starts)
+    char *tab_row;          // table row of the position's key (used where a segment starts)
+    float *state;           // that row's accumulator (used where a segment starts)
     float w;
-    uint32_t pad;
+    float s_old;            // the accumulator's value before the update (Adagrad)
 };
 
 // Chunk of CS = G*MP sorted positions per lane group of G lanes; U gradient rows in flight.
@@ -699,7 +699,9 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         p.tab_row = sl.tab[t] + static_cast<uint64_t>(row) * a.D * ES;
         p.state = OPT == DLRM_OPT_ADAGRAD ? sl.state[t] + row : nullptr;
         p.w = w;
-        p.pad = 0;
+        // read here, one lane per position, rather than by the whole group in the main loop (the
+        // owning group is the only writer of this row's state, and it writes after this read)
+        p.s_old = OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)p.state : 0.f;
         if (have) pm[r] = p;
         const uint64_t bal = __ballot(st);
         starts |= ((bal >> (grp * G)) & (G == 64 ? ~0ull : ((1ull << G) - 1))) << (m * G);
@@ -777,10 +779,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
         for (int u = 0; u < U; ++u) {
             const PosMeta &p = pm[min(max(r0 + u, r_begin), cnt - 1)];
             gload_words<W>(p.grad_row + c * W, gr[u]);
-            // the table row and state of the position's key: used where a segment starts, and
-            // loaded at every position (the row of the segment already being read: a cache hit)
+            // the table row of the position's key: used where a segment starts, and loaded at
+            // every position (the row of the segment already being read: a cache hit)
             gload_words<TW::N>(p.tab_row + c * W * ES, tr[u]);
-            st[u] = OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)p.state : 0.f;
+            st[u] = p.s_old;
             wu[u] = WEIGHTED ? p.w : 1.f;
             __builtin_amdgcn_sched_barrier(0);  // issue in use order: position u's loads arrive first
         }
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
             p.tab_row = nullptr;
             p.state = nullptr;
             p.w = WEIGHTED ? a.swgt[kk] : 1.f;
-            p.pad = 0;
+            p.s_old = 0.f;
             if (same) pm[r] = p;
             const uint64_t bal = __ballot(same);
             m += static_cast<uint32_t>(__popcll((bal >> (grp * G)) & (G == 64 ? ~0ull : ((1ull << G) - 1))));
