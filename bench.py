@@ -5,14 +5,15 @@ workload (26 tables, D=128, B=16384, bag lengths truncated-geometric on
 [1,100] with mean 20, Zipf(1.05) rows):
     emb_bag_fwd -> dlrm_interact_fwd -> dlrm_interact_bwd -> emb_bag_bwd_adagrad
 (sort / unique / segment-reduce / row-wise Adagrad in place on the bf16
-tables, all integer outputs requested).  By default the batch-only half of the
-embedding backward (emb_bag_bwd_plan: keys, sort, segments) runs on a second
-stream beside the lookup and the interaction, and emb_bag_bwd_apply follows the
-interaction backward (--one-stream: every call in order on one stream; the
-results are the same bits either way).  Inputs are resident in HBM before the
-timed region; R pre-generated batches rotate.  Prints one JSON line.
+tables, all integer outputs requested), every call in order on one stream.  The
+step is also timed with the batch-only half of the embedding backward
+(emb_bag_bwd_plan: keys, sort, segments) on a second stream beside the lookup
+and the interaction, emb_bag_bwd_apply following the interaction backward (the
+results are the same bits); --overlap-plan makes that form the headline.
+Inputs are resident in HBM before the timed region; R pre-generated batches
+rotate.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu] [--one-stream]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu] [--overlap-plan]
 """
 from __future__ import annotations
 
@@ -252,8 +253,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-samples", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="time the step with every call on one stream (no plan/apply overlap)")
+    ap.add_argument("--overlap-plan", action="store_true",
+                    help="headline the step form with the backward's sort on a second stream")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     ap.add_argument("--dist", choices=["zipf", "uniform"], default="zipf",
@@ -369,10 +370,10 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: the step as configured; the other form timed beside it for the record
-    headline = step if args.one_stream else step_overlap
+    headline = step_overlap if args.overlap_plan else step
     ms = timed(headline)
-    ms_other = timed(step_overlap if args.one_stream else step)
-    ms_one, ms_ovl = (ms, ms_other) if args.one_stream else (ms_other, ms)
+    ms_other = timed(step if args.overlap_plan else step_overlap)
+    ms_ovl, ms_one = (ms, ms_other) if args.overlap_plan else (ms_other, ms)
     log(f"[bench] ms/step: one stream {ms_one:.4f}, plan overlapped {ms_ovl:.4f}")
 
     # per-call HIP event times on the launching stream, over a second identical region
@@ -442,7 +443,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
-        "step_form": "one stream" if args.one_stream else "plan on a second stream",
+        "step_form": "plan on a second stream" if args.overlap_plan else "one stream",
         "ms_per_step_one_stream": ms_one,
         "ms_per_step_plan_overlapped": ms_ovl,
         "higher_is_better": True,
