@@ -59,7 +59,10 @@ bool trace_on() { return g_on.load(std::memory_order_relaxed); }
 void trace_begin(hipStream_t s) {
     std::lock_guard<std::mutex> lk(g_mu);
     t_open = take_event();
-    if (t_open) hipEventRecord(t_open, s);
+    if (t_open && hipEventRecord(t_open, s) != hipSuccess) {  // no record for this launch
+        g_free.push_back(t_open);
+        t_open = nullptr;
+    }
 }
 
 void trace_end(const char *name, hipStream_t s) {
@@ -71,7 +74,12 @@ void trace_end(const char *name, hipStream_t s) {
         t_open = nullptr;
         return;
     }
-    hipEventRecord(stop, s);
+    if (hipEventRecord(stop, s) != hipSuccess) {
+        g_free.push_back(t_open);
+        g_free.push_back(stop);
+        t_open = nullptr;
+        return;
+    }
     g_pending.push_back(Pending{name, t_open, stop});
     t_open = nullptr;
 }
