@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
             else hi = mid;
         }
         a.keys[j] = s_base[lo] + static_cast<uint32_t>(indices[j]);
-        a.pos[j] = static_cast<uint32_t>(j);
+        if (a.pos) a.pos[j] = static_cast<uint32_t>(j);  // only when the sorted positions are an output
         a.grow[j] = s_grow[lo];
         if (a.weights) a.wgt[j] = __float_as_uint(a.weights[j]);
     }
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_radix_scan(uint32_t *__restrict__ count
 struct SortIO {
     const uint32_t *kin;
     uint32_t *kout;
-    const uint32_t *pin[3];  // payload words in (position, grad row, weight)
+    const uint32_t *pin[3];  // payload words in: grad row, then weight and position when present
     uint32_t *pout[3];
 };
 
@@ -975,8 +975,11 @@ void launch_radix_pass(const SortIO &io, int NP, uint32_t n, int shift, uint32_t
     if (NP == 3)
         DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
                     counts, nblk, totals);
-    else
+    else if (NP == 2)
         DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
+    else
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
                     counts, nblk, totals);
 }
 
@@ -1072,7 +1075,6 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
     }
     const uint32_t n = static_cast<uint32_t>(nnz);
     const bool weighted = per_sample_weights != nullptr;
-    const int NP = weighted ? 3 : 2;  // payloads: position, grad row, (weight)
 
     // K4
     ExpandArgs ea{};
@@ -1085,7 +1087,7 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
     ea.indices = indices;
     ea.weights = per_sample_weights;
     ea.keys = u32(L.keys[0]);
-    ea.pos = u32(L.pos[0]);
+    ea.pos = sorted_pos_out ? u32(L.pos[0]) : nullptr;
     ea.grow = u32(L.grow[0]);
     ea.wgt = u32(L.wgt[0]);
     ea.B = static_cast<uint32_t>(B);
@@ -1104,12 +1106,20 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
         SortIO io{};
         io.kin = u32(L.keys[cur]);
         io.kout = u32(L.keys[cur ^ 1]);
-        io.pin[0] = u32(L.pos[cur]);
-        io.pout[0] = (last && sorted_pos_out) ? reinterpret_cast<uint32_t *>(sorted_pos_out) : u32(L.pos[cur ^ 1]);
-        io.pin[1] = u32(L.grow[cur]);
-        io.pout[1] = u32(L.grow[cur ^ 1]);
-        io.pin[2] = u32(L.wgt[cur]);
-        io.pout[2] = u32(L.wgt[cur ^ 1]);
+        // payloads: the grad row, the weight (weighted), the position (only when the sorted
+        // positions are an output: the update does not need them)
+        int q = 0;
+        io.pin[q] = u32(L.grow[cur]);
+        io.pout[q++] = u32(L.grow[cur ^ 1]);
+        if (weighted) {
+            io.pin[q] = u32(L.wgt[cur]);
+            io.pout[q++] = u32(L.wgt[cur ^ 1]);
+        }
+        if (sorted_pos_out) {
+            io.pin[q] = u32(L.pos[cur]);
+            io.pout[q++] = last ? reinterpret_cast<uint32_t *>(sorted_pos_out) : u32(L.pos[cur ^ 1]);
+        }
+        const int NP = q;
         if (ps.rb == 8) launch_radix_pass<8>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
         else if (ps.rb == 9) launch_radix_pass<9>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
         else launch_radix_pass<10>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);

@@ -4,8 +4,9 @@ emb_bag_bwd_apply (segment sums and the update), needs an MI355X.
 Gates: plan + apply gives the bits of emb_bag_bwd_update (tables, states and the integer outputs),
 on one stream and with the plan on a second stream ordered by an event; one plan applied twice
 (to two copies of the tables, with and without the plan's segment-offset output) gives the same
-bits both times, also when hot rows send segments through the finisher; an empty batch leaves
-the tables untouched.  emb_bag_bwd_update itself is checked against the oracle elsewhere; one
+bits both times, also when hot rows send segments through the finisher; without the integer
+outputs (the sort then carries no position payload) the update gives the same bits; an empty batch
+leaves the tables untouched.  emb_bag_bwd_update itself is checked against the oracle elsewhere; one
 case here is checked against the oracle directly too (Adagrad rows: per-row relative error
 <= 1e-4 for fp32).
 """
@@ -144,6 +145,24 @@ def test_one_plan_applied_twice(opt, hot):
         got.append(snapshot(tabs, sts))
     for g in got:
         same(g, (want[0], want[1], None))
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_update_without_outputs(weighted, dtype):
+    """Without the integer outputs the sort carries no position payload; the update is the same."""
+    rows = [700, 2, 30000, 90]
+    B = 211
+    tables, states, idx, off, w, gp = case(zlib.crc32(f"noout-{weighted}-{dtype}".encode()), rows, 64, dtype, B,
+                                           weighted)
+    say(f"[plan/apply] no outputs weighted={weighted} {dtype} nnz={len(idx)}")
+    want = run_update(tables, states, idx, off, w, gp, DLRM_OPT_ADAGRAD)
+    tabs = [to_dev(t) for t in tables]
+    sts = [to_dev(s) for s in states]
+    emb_bag_bwd_update(tabs, sts, to_dev(idx), to_dev(off), None if w is None else to_dev(w), to_dev(gp),
+                       DLRM_OPT_ADAGRAD, 0.01, 1e-8)
+    torch.cuda.synchronize()
+    same(snapshot(tabs, sts), (want[0], want[1], None))
 
 
 def test_plan_apply_vs_oracle():
