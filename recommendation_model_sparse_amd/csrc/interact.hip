@@ -55,6 +55,13 @@ __global__ __launch_bounds__(256) void k_interact_fwd_mfma(const float *__restri
     floatx4 acc[NBLK];
 #pragma unroll
     for (int k = 0; k < NBLK; ++k) acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // the dense vector for the concatenated tail, loaded with the operands (a load at the end
+    // would add a round trip to every sample)
+    constexpr int DPL = (D + kWave - 1) / kWave;
+    const float *dsrc = dense + static_cast<uint64_t>(sample) * D;
+    float dv[DPL];
+#pragma unroll
+    for (int s = 0; s < DPL; ++s) dv[s] = dsrc[min(lane + s * kWave, D - 1)];
 
 #pragma unroll
     for (int c0 = 0; c0 < NCH; c0 += CHG) {
@@ -97,8 +104,9 @@ __global__ __launch_bounds__(256) void k_interact_fwd_mfma(const float *__restri
                 const int gi = I * 16 + q * 4 + v, gj = J * 16 + r16;
                 if (gi < gj && gj < N) orow[triu_pos(gi, gj, N)] = acc[k][v];
             }
-    const float *dsrc = dense + static_cast<uint64_t>(sample) * D;
-    for (int d = lane; d < D; d += kWave) orow[P + d] = dsrc[d];
+#pragma unroll
+    for (int s = 0; s < DPL; ++s)
+        if (lane + s * kWave < D) orow[P + lane + s * kWave] = dv[s];
 }
 
 // Any D % 4 == 0: one block per sample, one thread per pair, fp32 FMA chain over d.
@@ -189,17 +197,13 @@ __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ 
     const uint32_t sb = valid ? sample : 0;
     const float *g = grad_out + static_cast<uint64_t>(sb) * (P + D);
 
-    // G: symmetric, zero diagonal, zero padding
-    for (int e = lane; e < NP * NP; e += kWave) {
-        const int i = e / NP, j = e % NP;
-        float v = 0.f;
-        if (valid && i < N && j < N && i != j) v = g[i < j ? triu_pos(i, j, N) : triu_pos(j, i, N)];
-        Gs[wv][i][j] = v;
-    }
-    __syncthreads();
-
+    // this lane's columns of X and of the dense part of the upstream gradient are loaded first,
+    // so that their round trip overlaps the one of the G loads below
     const int d0 = slice * (kWave * CPL) + lane * CPL;
     const bool dv = valid && d0 < D;
+    float gt[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) gt[c] = dv ? g[P + d0 + c] : 0.f;
     float x[NP][CPL];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
@@ -217,6 +221,25 @@ __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ 
             for (int c = 0; c < CPL; ++c) x[j][c] = 0.f;
         }
     }
+    // G: symmetric, zero diagonal, zero padding.  All of a lane's entries are loaded before any
+    // is stored (every load unconditional: entries off the triangle re-read entry 0 and are
+    // zeroed), so they make one round trip rather than one per entry.
+    constexpr int NE = (NP * NP + kWave - 1) / kWave;
+    float gv_[NE];
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int e = lane + k * kWave, i = e / NP, j = e % NP;
+        const bool on = valid && e < NP * NP && i < N && j < N && i != j;
+        const float v = g[on ? (i < j ? triu_pos(i, j, N) : triu_pos(j, i, N)) : 0];
+        gv_[k] = on ? v : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int e = lane + k * kWave;
+        if (e < NP * NP) Gs[wv][e / NP][e % NP] = gv_[k];
+    }
+    __syncthreads();
+
     if (!dv) return;
     for (int i = 0; i < N; ++i) {
         float acc[CPL];
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ 
         float *dst;
         if (i == 0) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[c] += g[P + d0 + c];
+            for (int c = 0; c < CPL; ++c) acc[c] += gt[c];
             dst = grad_dense + static_cast<uint64_t>(sb) * D + d0;
         } else {
             dst = grad_pooled + (static_cast<uint64_t>(sb) * (N - 1) + (i - 1)) * D + d0;
