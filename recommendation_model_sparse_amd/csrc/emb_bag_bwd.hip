@@ -220,12 +220,14 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
     for (int d = threadIdx.x; d < NBK; d += 256) h[d] = 0;
     __syncthreads();
     const uint32_t base = blockIdx.x * kSortTile;
+    // all of a thread's keys are loaded (unconditionally) before the first atomic: interleaved,
+    // the compiler waits for each load in turn
+    uint32_t key[kSortItems];
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
-        const uint32_t k = base + i * 256 + threadIdx.x;
-        const uint32_t key = keys[min(k, n - 1)];
-        if (k < n) atomicAdd(&h[(key >> shift) & (NBK - 1)], 1u);
-    }
+    for (int i = 0; i < kSortItems; ++i) key[i] = keys[min(base + i * 256 + threadIdx.x, n - 1)];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i)
+        if (base + i * 256 + threadIdx.x < n) atomicAdd(&h[(key[i] >> shift) & (NBK - 1)], 1u);
     __syncthreads();
     for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + blockIdx.x] = h[d];
 }
@@ -374,16 +376,33 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
 
 // ---------------------------------------------------------------- K6 unique + segments
 
-__device__ __forceinline__ bool seg_flag(const uint32_t *keys, uint32_t k, uint32_t n) {
-    return k < n && (k == 0 || keys[k] != keys[k - 1]);
+// Segment-start flags of the positions base + i*stride (i < kSortItems), with their keys.  All
+// keys are loaded (unconditionally, clamped in bounds) before the first compare, so they make one
+// round trip together.
+__device__ __forceinline__ void seg_flags(const uint32_t *keys, uint32_t base, uint32_t stride, uint32_t n,
+                                          bool *flag, uint32_t *kv) {
+    uint32_t prev[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const uint32_t kk = min(base + i * stride, n - 1);
+        kv[i] = keys[kk];
+        prev[i] = keys[kk > 0 ? kk - 1 : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const uint32_t k = base + i * stride;
+        flag[i] = k < n && (k == 0 || kv[i] != prev[i]);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_seg_count(const uint32_t *__restrict__ keys, uint32_t n,
                                                    uint32_t *__restrict__ bcount) {
+    bool flag[kSortItems];
+    uint32_t kv[kSortItems];
+    seg_flags(keys, blockIdx.x * kSortTile + threadIdx.x, 256, n, flag, kv);
     uint32_t c = 0;
-    const uint32_t base = blockIdx.x * kSortTile;
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i) c += seg_flag(keys, base + i * 256 + threadIdx.x, n);
+    for (int i = 0; i < kSortItems; ++i) c += flag[i] ? 1u : 0u;
     uint32_t tot;
     block_exclusive_scan(c, &tot);
     if (threadIdx.x == 0) bcount[blockIdx.x] = tot;
@@ -422,11 +441,14 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
     __shared__ uint32_t wtot[4];
     const int tid = threadIdx.x, w = static_cast<int>(wave_id()), lane = tid & 63;
     const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + lane;
+    bool flags[kSortItems];
+    uint32_t kv[kSortItems];
+    seg_flags(keys, base, kWave, n, flags, kv);
     uint64_t masks[kSortItems];
     uint32_t wsum = 0;
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
-        masks[i] = __ballot(seg_flag(keys, base + i * kWave, n));
+        masks[i] = __ballot(flags[i]);
         wsum += __popcll(masks[i]);
     }
     if (lane == 0) wtot[w] = wsum;
@@ -440,7 +462,7 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
         const bool flag = (masks[i] >> lane) & 1ull;
         const uint32_t seg_incl = run + __popcll(masks[i] & lt) + (flag ? 1u : 0u);  // flags in [0, k]
         if (flag) {
-            if (unique_keys) unique_keys[seg_incl - 1] = keys[k];
+            if (unique_keys) unique_keys[seg_incl - 1] = kv[i];
             seg_offsets[seg_incl - 1] = k;
         }
         if (k < n && ((k + 1) % CS == 0 || k + 1 == n)) chunk_seg[k / CS] = seg_incl - 1;
