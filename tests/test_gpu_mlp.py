@@ -5,7 +5,7 @@ Error measure: |gpu - oracle| / scale with scale the sum of the absolute values 
   - fp32 GEMM outputs: gamma_K = K * 2^-24 (recursive summation bound; K <= 1024 -> 6.1e-5);
   - bf16 outputs and the GEMMs that take the bf16-rounded dz: 2^-9 (one rounding) + gamma_K,
     held to 2^-8;
-  - fixed-order fp32 column sums over M rows in blocks of 128: (128 + M/128) * 2^-24 -> 1e-4.
+  - fixed-order fp32 column sums over M rows in blocks of 32: (32 + M/32) * 2^-24 -> 1e-4.
 The ReLU mask is a decision taken in floating point, so the oracle takes it from the GPU's own
 forward output (y > 0); everything else the oracle computes from the same bf16 / fp32 inputs.
 """
