@@ -272,28 +272,14 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     __shared__ uint32_t lbase[NBK];  // start of digit d inside the block's sorted tile
     __shared__ uint32_t wcnt[4][NBK];
     __shared__ uint32_t stage[kSortTile];
+    // tiles are spread over the XCDs in contiguous ranges: the runs that neighbouring tiles write
+    // for one digit are adjacent in the output, and meet in one L2 before they are written back
+    const uint32_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    if (tile >= nblk) return;  // block-uniform, before any barrier
     const int tid = threadIdx.x, w = static_cast<int>(wave_id());
-    {
-        // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
-        uint32_t tv[K], sum = 0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            tv[k] = totals[tid * K + k];
-            sum += tv[k];
-        }
-        uint32_t tot;
-        uint32_t run = block_exclusive_scan(sum, &tot);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int d = tid * K + k;
-            gbase[d] = run + counts[d * nblk + blockIdx.x];
-            run += tv[k];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) wcnt[q][d] = 0;
-        }
-    }
-    __syncthreads();
-    const uint32_t tile0 = blockIdx.x * kSortTile;
+    // the tile's keys and payloads are loaded first: their round trip then overlaps the one of the
+    // digit totals and counts below (in order, before the barriers the prologue needs)
+    const uint32_t tile0 = tile * kSortTile;
     const uint32_t base = tile0 + w * (kSortTile / 4) + (tid & 63);
     uint32_t key[kSortItems], loc[kSortItems], pay[NP][kSortItems];
 #pragma unroll
@@ -303,6 +289,27 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
 #pragma unroll
         for (int q = 0; q < NP; ++q) pay[q][i] = io.pin[q][k];
     }
+    {
+        // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
+        uint32_t tv[K], cv[K], sum = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            tv[k] = totals[tid * K + k];
+            cv[k] = counts[(tid * K + k) * nblk + tile];
+            sum += tv[k];
+        }
+        uint32_t tot;
+        uint32_t run = block_exclusive_scan(sum, &tot);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int d = tid * K + k;
+            gbase[d] = run + cv[k];
+            run += tv[k];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wcnt[q][d] = 0;
+        }
+    }
+    __syncthreads();
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
@@ -994,15 +1001,16 @@ void launch_radix_pass(const SortIO &io, int NP, uint32_t n, int shift, uint32_t
                        uint32_t nblk, uint32_t *totals, hipStream_t stream) {
     DLRM_LAUNCH("radix_hist", k_radix_hist<RB>, dim3(nblk), dim3(256), 0, stream, io.kin, n, shift, counts, nblk);
     DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(1 << RB), dim3(256), 0, stream, counts, nblk, totals);
+    const dim3 sgrid(round_up_xcd(nblk));
     if (NP == 3)
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
-                    counts, nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
+                    nblk, totals);
     else if (NP == 2)
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
-                    counts, nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
+                    nblk, totals);
     else
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB>), dim3(nblk), dim3(256), 0, stream, io, n, shift,
-                    counts, nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
+                    nblk, totals);
 }
 
 }  // namespace
