@@ -217,9 +217,13 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
                                                     uint32_t nblk) {
     constexpr int NBK = 1 << RB;
     __shared__ uint32_t h[NBK];
+    // the scatter's tile mapping: each XCD counts (and later scatters) one contiguous range of
+    // tiles, so its count writes for a digit share lines in its own L2
+    const uint32_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    if (tile >= nblk) return;  // block-uniform, before any barrier
     for (int d = threadIdx.x; d < NBK; d += 256) h[d] = 0;
     __syncthreads();
-    const uint32_t base = blockIdx.x * kSortTile;
+    const uint32_t base = tile * kSortTile;
     // all of a thread's keys are loaded (unconditionally) before the first atomic: interleaved,
     // the compiler waits for each load in turn
     uint32_t key[kSortItems];
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
     for (int i = 0; i < kSortItems; ++i)
         if (base + i * 256 + threadIdx.x < n) atomicAdd(&h[(key[i] >> shift) & (NBK - 1)], 1u);
     __syncthreads();
-    for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + blockIdx.x] = h[d];
+    for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + tile] = h[d];
 }
 
 // Block d: exclusive scan of counts[d][0..nblk) in place; totals[d] = row sum.
@@ -999,7 +1003,8 @@ void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t 
 template <int RB>
 void launch_radix_pass(const SortIO &io, int NP, uint32_t n, int shift, uint32_t *counts,
                        uint32_t nblk, uint32_t *totals, hipStream_t stream) {
-    DLRM_LAUNCH("radix_hist", k_radix_hist<RB>, dim3(nblk), dim3(256), 0, stream, io.kin, n, shift, counts, nblk);
+    DLRM_LAUNCH("radix_hist", k_radix_hist<RB>, dim3(round_up_xcd(nblk)), dim3(256), 0, stream, io.kin, n, shift,
+                counts, nblk);
     DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(1 << RB), dim3(256), 0, stream, counts, nblk, totals);
     const dim3 sgrid(round_up_xcd(nblk));
     if (NP == 3)
