@@ -6,10 +6,11 @@
 // Design for gfx950:
 //   - A row is D*s bytes = G chunks of 16 bytes; a lane group of G lanes covers one row with
 //     one 16-byte load per lane (global_load_dwordx4), so every row read is fully coalesced.
-//   - Multi-hot bags: one wavefront per bag.  The wave loads up to 64 of the bag's indices
-//     with one coalesced load, broadcasts them with cross-lane permutes, and its 64/G lane
-//     groups each issue U row loads before the first use, so 64/G*U rows of the bag are in
-//     flight at once.  Group partial sums are combined in a fixed butterfly.
+//   - Multi-hot bags: one wavefront per bag at a time (4 consecutive bags per wave, in turn).
+//     The wave loads up to 64 of the bag's indices with one coalesced load, broadcasts them
+//     with cross-lane permutes, and its 64/G lane groups each issue U row loads before the
+//     first use, so 64/G*U rows of the bag are in flight at once.  Group partial sums are
+//     combined in a fixed butterfly.
 //   - One-hot / short bags: each lane group owns BPG bags and issues the first row of all of
 //     them before accumulating.
 //   - Blocks are remapped so each XCD walks a contiguous range of bags; bags are table-major,
@@ -21,6 +22,10 @@
 
 namespace dlrm {
 namespace {
+
+// Bags per wavefront in the multi-hot lookup: a wave walks 4 consecutive bags (of one table,
+// mostly) in turn, which measured 4% faster than one bag per wave (fewer, longer waves).
+constexpr int kPoolBagsPerWave = 4;
 
 struct PoolArgs {
     const char *tables[kMaxTables];
@@ -36,7 +41,8 @@ struct PoolArgs {
     uint32_t nblocks;  // blocks launched (a multiple of 8)
 };
 
-// One wavefront per bag (multi-hot).  G lanes per row, NG = 64/G groups, U rows per group in flight.
+// One wavefront per bag at a time (multi-hot), kPoolBagsPerWave bags per wave.  G lanes per row,
+// NG = 64/G groups, U rows per group in flight.
 template <int DT, int G, bool WEIGHTED, typename IT, int OT>
 __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     const IT *indices = static_cast<const IT *>(a.indices);
@@ -45,45 +51,45 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     constexpr int EPC = Elem<DT>::kPerChunk;
     constexpr int U = 8;
     const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
-    const uint32_t bag = lb * 4 + wave_id();
-    if (bag >= a.nbags) return;
+    const uint32_t bag0 = (lb * 4 + wave_id()) * kPoolBagsPerWave;
     const int lane = threadIdx.x & 63;
     const int grp = lane / G, c = lane % G;
-    const uint32_t t = bag / a.B, b = bag - t * a.B;
-    const char *tab = a.tables[t] + c * 16;
-    const int64_t start = offsets[bag], end = offsets[bag + 1];
+    for (uint32_t bag = bag0; bag < min(bag0 + kPoolBagsPerWave, a.nbags); ++bag) {  // wave-uniform
+        const uint32_t t = bag / a.B, b = bag - t * a.B;
+        const char *tab = a.tables[t] + c * 16;
+        const int64_t start = offsets[bag], end = offsets[bag + 1];
 
-    float acc[EPC];
+        float acc[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-
-    for (int64_t base = start; base < end; base += kWave) {
-        const int n = static_cast<int>(min<int64_t>(kWave, end - base));
-        const int64_t my_idx = lane < n ? static_cast<int64_t>(indices[base + lane]) : 0;
-        float my_w = 1.f;
-        if constexpr (WEIGHTED) my_w = lane < n ? a.weights[base + lane] : 0.f;
-        for (int r0 = 0; r0 < n; r0 += NG * U) {
-            uint4 v[U];
-            float w[U];
+        for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+        for (int64_t base = start; base < end; base += kWave) {
+            const int n = static_cast<int>(min<int64_t>(kWave, end - base));
+            const int64_t my_idx = lane < n ? static_cast<int64_t>(indices[base + lane]) : 0;
+            float my_w = 1.f;
+            if constexpr (WEIGHTED) my_w = lane < n ? a.weights[base + lane] : 0.f;
+            for (int r0 = 0; r0 < n; r0 += NG * U) {
+                uint4 v[U];
+                float w[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = r0 + u * NG + grp;
-                const int src = r < n ? r : 0;
-                const int64_t idx = __shfl(my_idx, src);
-                w[u] = WEIGHTED ? __shfl(my_w, src) : 1.f;
-                v[u] = r < n ? load_row_chunk(tab, idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < U; ++u) {
+                    const int r = r0 + u * NG + grp;
+                    const int src = r < n ? r : 0;
+                    const int64_t idx = __shfl(my_idx, src);
+                    w[u] = WEIGHTED ? __shfl(my_w, src) : 1.f;
+                    v[u] = r < n ? load_row_chunk(tab, idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (r0 + u * NG + grp < n) accumulate<DT, WEIGHTED>(acc, v[u], w[u]);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (r0 + u * NG + grp < n) accumulate<DT, WEIGHTED>(acc, v[u], w[u]);
         }
+        // combine the NG group partials (fixed butterfly: every group ends with identical bits)
+#pragma unroll
+        for (int s = G; s < kWave; s <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], s);
+        if (grp == 0) store_pooled<DT, OT>(a.out, (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
     }
-    // combine the NG group partials (fixed butterfly: every group ends with identical bits)
-#pragma unroll
-    for (int s = G; s < kWave; s <<= 1)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], s);
-    if (grp == 0) store_pooled<DT, OT>(a.out, (static_cast<uint64_t>(b) * a.T + t) * a.D + c * EPC, acc);
 }
 
 // One lane group per bag (one-hot or short bags); each group owns BPG bags.
@@ -254,7 +260,7 @@ void launch_pool(const PoolArgs &a0, bool wave_per_bag, hipStream_t stream) {
     PoolArgs a = a0;
     constexpr int NG = kWave / G;
     if (wave_per_bag) {
-        a.nblocks = round_up_xcd((a.nbags + 3) / 4);
+        a.nblocks = round_up_xcd((a.nbags + 4 * kPoolBagsPerWave - 1) / (4 * kPoolBagsPerWave));
         DLRM_LAUNCH("pool_wave_per_bag", (k_pool_wave_per_bag<DT, G, W, IT, OT>), dim3(a.nblocks), dim3(256), 0, stream, a);
     } else {
         constexpr int BPG = G >= 64 ? 1 : (G >= 32 ? 2 : 4);
