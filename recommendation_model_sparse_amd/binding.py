@@ -36,7 +36,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+                               "`python -m recommendation_model_sparse_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         p, i32, i64, u32, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                           ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
