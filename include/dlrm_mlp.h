@@ -89,6 +89,15 @@ int dlrm_sgd_dense(float *w32, uint16_t *w16, const float *g, int64_t n, float l
                    dlrm_stream_t stream);
 
 /*
+ * The SGD of dlrm_sgd_dense on `count` parameters at once (one launch, the same arithmetic and
+ * bits): for each i, w32[i][e] -= lr * g[i][e] for e < n[i], and the bf16 copy w16[i] refreshed
+ * when w16 is not NULL and w16[i] is not NULL.  w32, w16, g, n are host arrays of count device
+ * pointers / sizes; 0 <= count <= 64; n[i] >= 0.  The parameters must not overlap.
+ */
+int dlrm_sgd_dense_multi(int32_t count, float *const *w32, uint16_t *const *w16, const float *const *g,
+                         const int64_t *n, float lr, dlrm_stream_t stream);
+
+/*
  * Row copy with a type change and zero padding, to give a matrix the 16-byte rows the GEMMs need
  * (13 dense features -> 16, the 479-wide interaction output -> 480) or to drop the padding again:
  *   dst[m][c] = src[m][c] for c < cols,  0 for cols <= c < dst_cols

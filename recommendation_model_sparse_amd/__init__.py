@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     dlrm_linear_fwd,
     dlrm_linear_workspace_size,
     dlrm_sgd_dense,
+    dlrm_sgd_dense_multi,
     DLRM_BF16,
     DLRM_F32,
     DLRM_FLAG_CHECK_INDICES,

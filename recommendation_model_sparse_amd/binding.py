@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.dlrm_linear_bwd.argtypes = [p, p, i32, i32, p, p, i64, i32, i32, p, p, p, p, p, sz, p]
         L.dlrm_bce_head.argtypes = [p, p, p, p, i64, i32, p, p, p, p, p, p, sz, p]
         L.dlrm_sgd_dense.argtypes = [p, p, p, i64, f32, p]
+        L.dlrm_sgd_dense_multi.argtypes = [i32, p, p, p, p, f32, p]
         L.dlrm_cast_rows.argtypes = [p, i32, i64, i64, i32, p, i32, i32, p]
         for f in (L.dlrm_linear_fwd, L.dlrm_linear_bwd, L.dlrm_bce_head, L.dlrm_sgd_dense, L.dlrm_cast_rows):
             f.restype = ctypes.c_int
@@ -466,6 +467,29 @@ def dlrm_sgd_dense(w32: torch.Tensor, w16: Optional[torch.Tensor], g: torch.Tens
         raise ValueError("g must match w32")
     _check(lib().dlrm_sgd_dense(_ptr(w32), _ptr(w16) if w16 is not None else None, _ptr(g), w32.numel(), float(lr),
                                 _stream(w32.device)), "dlrm_sgd_dense")
+
+
+def dlrm_sgd_dense_multi(params: Sequence, lr: float) -> None:
+    """For each (w32, w16 or None, g): w32 -= lr * g and w16 <- bf16(w32), in one launch
+    (C: dlrm_sgd_dense_multi)."""
+    count = len(params)
+    w32s, w16s, gs, ns = [], [], [], []
+    for w32, w16, g in params:
+        if w32.dtype != torch.float32 or not w32.is_contiguous():
+            raise ValueError("w32 must be contiguous fp32")
+        if g.dtype != torch.float32 or not g.is_contiguous() or g.numel() != w32.numel():
+            raise ValueError("g must be contiguous fp32 of w32's size")
+        if w16 is not None and (w16.numel() != w32.numel() or not w16.is_contiguous()):
+            raise ValueError("w16 must match w32")
+        w32s.append(w32.data_ptr())
+        w16s.append(w16.data_ptr() if w16 is not None else None)
+        gs.append(g.data_ptr())
+        ns.append(w32.numel())
+    if count == 0:
+        return
+    vp = ctypes.c_void_p * count
+    _check(lib().dlrm_sgd_dense_multi(count, vp(*w32s), vp(*w16s), vp(*gs), (ctypes.c_int64 * count)(*ns), float(lr),
+                                      _stream(params[0][0].device)), "dlrm_sgd_dense_multi")
 
 
 def dlrm_cast_rows(src: torch.Tensor, cols: int, dst_cols: int, dst_dtype: torch.dtype,

@@ -195,6 +195,38 @@ __global__ __launch_bounds__(256) void k_sgd_dense(float *__restrict__ w32, uint
     if (w16) w16[i] = f32_to_bf16(v);
 }
 
+// Many SGD updates in one launch: tensor i owns blocks [boff[i], boff[i+1]), each block 1024
+// consecutive elements (4 per thread, 256 apart), the same arithmetic as k_sgd_dense.
+constexpr int kSgdMaxTensors = 64;
+constexpr int kSgdPerBlock = 1024;
+struct SgdMulti {
+    float *w32[kSgdMaxTensors];
+    uint16_t *w16[kSgdMaxTensors];
+    const float *g[kSgdMaxTensors];
+    int64_t n[kSgdMaxTensors];
+    uint32_t boff[kSgdMaxTensors + 1];
+    int32_t count;
+    float lr;
+};
+
+__global__ __launch_bounds__(256) void k_sgd_dense_multi(SgdMulti a) {
+    int i = 0;  // the tensor of this block (uniform scan over at most 64 entries)
+    while (i + 1 < a.count && blockIdx.x >= a.boff[i + 1]) ++i;
+    const int64_t base = static_cast<int64_t>(blockIdx.x - a.boff[i]) * kSgdPerBlock + threadIdx.x;
+    float *w32 = a.w32[i];
+    uint16_t *w16 = a.w16[i];
+    const float *g = a.g[i];
+#pragma unroll
+    for (int k = 0; k < kSgdPerBlock / 256; ++k) {
+        const int64_t e = base + k * 256;
+        if (e < a.n[i]) {
+            const float v = fmaf(-a.lr, g[e], w32[e]);
+            w32[e] = v;
+            if (w16) w16[e] = f32_to_bf16(v);
+        }
+    }
+}
+
 template <int ST, int DT>
 __global__ __launch_bounds__(256) void k_cast_rows(const void *__restrict__ src, int64_t src_ld, int64_t M,
                                                    int32_t cols, void *__restrict__ dst, int32_t dst_cols) {
@@ -480,6 +512,32 @@ extern "C" int dlrm_sgd_dense(float *w32, uint16_t *w16, const float *g, int64_t
     if (!w32 || !g) return DLRM_ERR_INVALID_ARG;
     DLRM_LAUNCH("sgd_dense", k_sgd_dense, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, w32, w16, g,
                 n, lr);
+    return launch_status();
+}
+
+extern "C" int dlrm_sgd_dense_multi(int32_t count, float *const *w32, uint16_t *const *w16, const float *const *g,
+                                    const int64_t *n, float lr, dlrm_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (count < 0 || count > kSgdMaxTensors) return DLRM_ERR_INVALID_ARG;
+    if (count == 0) return DLRM_OK;
+    if (!w32 || !g || !n) return DLRM_ERR_INVALID_ARG;
+    SgdMulti a{};
+    uint64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        if (n[i] < 0 || (n[i] > 0 && (!w32[i] || !g[i]))) return DLRM_ERR_INVALID_ARG;
+        a.w32[i] = w32[i];
+        a.w16[i] = w16 ? w16[i] : nullptr;
+        a.g[i] = g[i];
+        a.n[i] = n[i];
+        a.boff[i] = static_cast<uint32_t>(blocks);
+        blocks += (static_cast<uint64_t>(n[i]) + kSgdPerBlock - 1) / kSgdPerBlock;
+        if (blocks >= (uint64_t(1) << 31)) return DLRM_ERR_UNSUPPORTED;
+    }
+    a.boff[count] = static_cast<uint32_t>(blocks);
+    a.count = count;
+    a.lr = lr;
+    if (blocks == 0) return DLRM_OK;
+    DLRM_LAUNCH("sgd_dense_multi", k_sgd_dense_multi, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a);
     return launch_status();
 }
 

@@ -172,13 +172,13 @@ class DlrmStep:
                               dz_bf16=self._mat(self.dz, B, layer.W16.shape[0]), dx=dx, dW=layer.dW, db=layer.db,
                               workspace=self.ws)
             dy = dx
-        # SGD on every dense parameter
+        # SGD on every dense parameter, in one launch
+        params = []
         for layer in self.bottom + self.top:
-            L.dlrm_sgd_dense(layer.W32, layer.W16, layer.dW, self.lr_dense)
-            L.dlrm_sgd_dense(layer.b, None, layer.db, self.lr_dense)
+            params += [(layer.W32, layer.W16, layer.dW), (layer.b, None, layer.db)]
         h = self.head
-        L.dlrm_sgd_dense(h.W32.view(-1), h.W16.view(-1), self.head_out["dw"], self.lr_dense)
-        L.dlrm_sgd_dense(h.b, None, self.head_out["db"], self.lr_dense)
+        params += [(h.W32.view(-1), h.W16.view(-1), self.head_out["dw"]), (h.b, None, self.head_out["db"])]
+        L.dlrm_sgd_dense_multi(params, self.lr_dense)
 
     def step(self, idx, off, dense_x, labels, outputs=None):
         out = self.forward(idx, off, dense_x, labels)

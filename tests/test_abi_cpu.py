@@ -207,6 +207,17 @@ def test_interact_rejects(L):
     assert b(FAKE, FAKE, FAKE, 4, 5, 6, FAKE, FAKE, None) == UNSUPPORTED
 
 
+def test_sgd_dense_multi_rejects(L):
+    f = L.dlrm_sgd_dense_multi
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    assert f(65, arr(FAKE), None, arr(FAKE), i64s(1), 0.1, None) == INVALID   # more than 64 parameters
+    assert f(-1, None, None, None, None, 0.1, None) == INVALID
+    assert f(0, None, None, None, None, 0.1, None) == OK                      # nothing to do
+    assert f(1, None, None, arr(FAKE), i64s(1), 0.1, None) == INVALID
+    assert f(1, arr(FAKE), None, arr(FAKE), i64s(-1), 0.1, None) == INVALID
+    assert f(1, arr(0), None, arr(FAKE), i64s(4), 0.1, None) == INVALID       # null parameter
+
+
 def test_workspace_size(L):
     ws = lambda rows, D, B, nnz: binding.emb_bag_bwd_workspace_size(rows, D, B, nnz)
     assert ws([100], 6, 4, 10) == 0          # D must be a power of two

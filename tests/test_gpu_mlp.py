@@ -24,6 +24,7 @@ from recommendation_model_sparse_amd import (
     dlrm_linear_bwd,
     dlrm_linear_fwd,
     dlrm_sgd_dense,
+    dlrm_sgd_dense_multi,
     synth,
 )
 
@@ -140,3 +141,28 @@ def test_sgd_dense_and_cast_rows():
     big = to_dev(np.pad(a, ((0, 0), (0, 1))))
     crop = dlrm_cast_rows(big, 479, 479, torch.float32)
     assert np.array_equal(crop.cpu().numpy(), a)
+
+
+def test_sgd_dense_multi_equals_single():
+    """One launch over many parameters (sizes 0, 1, ragged, several blocks) gives the bits of the
+    per-parameter call."""
+    rng = np.random.default_rng(5)
+    sizes = [1, 0, 1023, 1024, 1025, 70000, 13, 4096 * 3 + 7]
+    single, multi = [], []
+    for k, n in enumerate(sizes):
+        w = rng.standard_normal(n).astype(np.float32)
+        g = rng.standard_normal(n).astype(np.float32)
+        with16 = k % 2 == 0
+        for lst in (single, multi):
+            w32 = to_dev(w)
+            w16 = torch.empty(n, dtype=torch.bfloat16, device=DEV) if with16 else None
+            lst.append((w32, w16, to_dev(g)))
+    say("[mlp] sgd dense multi")
+    for w32, w16, g in single:
+        dlrm_sgd_dense(w32, w16, g, 0.03)
+    dlrm_sgd_dense_multi(multi, 0.03)
+    torch.cuda.synchronize()
+    for (a32, a16, _), (b32, b16, _) in zip(single, multi):
+        assert torch.equal(a32.view(torch.int32), b32.view(torch.int32))
+        if a16 is not None:
+            assert torch.equal(a16.view(torch.int16), b16.view(torch.int16))
