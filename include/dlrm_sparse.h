@@ -65,7 +65,7 @@ typedef enum { DLRM_OPT_ADAGRAD = 0, DLRM_OPT_SGD = 1 } dlrm_optimizer;
 enum {
     DLRM_OK = 0,
     DLRM_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment          */
-    DLRM_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits          */
+    DLRM_ERR_UNSUPPORTED = -2, /* valid but outside the library's limits         */
     DLRM_ERR_HIP = -3,         /* a HIP launch or runtime call failed            */
     DLRM_ERR_INDEX_RANGE = -4, /* CHECK_INDICES found a bad index or offset      */
     DLRM_ERR_WORKSPACE = -5    /* workspace missing or smaller than required     */
