@@ -6,8 +6,9 @@ Error measure: |gpu - oracle| / scale with scale the sum of the absolute values 
   - bf16 outputs and the GEMMs that take the bf16-rounded dz: 2^-9 (one rounding) + gamma_K,
     held to 2^-8;
   - fixed-order fp32 column sums over M rows in blocks of 32: (32 + M/32) * 2^-24 -> 1e-4.
-The ReLU mask is a decision taken in floating point, so the oracle takes it from the GPU's own
-forward output (y > 0); everything else the oracle computes from the same bf16 / fp32 inputs.
+The ReLU mask is a decision taken in floating point, so both sides take it from one forward output
+(y > 0) that the backward receives as an input: the oracle's own forward, rounded to the layer's
+output type.  Every oracle input is generated on the host.
 """
 import zlib
 
@@ -70,12 +71,18 @@ def test_linear_fwd_bwd(M, K, N, act, ydt):
     say(f"   fwd max rel err {err:.3e} (gate {gate:.2e})")
     assert err <= gate
 
-    # backward, with the ReLU mask taken from the GPU's own output
+    # backward: the forward output it takes (the ReLU mask) is the oracle's, rounded as the layer
+    # stores it, on both sides
+    if ydt == torch.bfloat16:
+        y_in_d, y_in = bf16_pair(ref)
+    else:
+        y_in = ref.astype(np.float32)
+        y_in_d, y_in = to_dev(y_in), y_in.astype(np.float64)
     dy = rng.standard_normal((M, N)).astype(np.float32)
     for want_dx in (True, False):
-        dx_d, dW_d, db_d = dlrm_linear_bwd(to_dev(dy), y_d, act, x_d, W_d, want_dx=want_dx)
+        dx_d, dW_d, db_d = dlrm_linear_bwd(to_dev(dy), y_in_d, act, x_d, W_d, want_dx=want_dx)
         torch.cuda.synchronize()
-        mask_src = y if act == DLRM_ACT_RELU else np.ones_like(y)
+        mask_src = y_in if act == DLRM_ACT_RELU else np.ones_like(y_in)
         rdx, rdW, rdb, sdx, sdW, sdb = mlp.linear_bwd(dy, mask_src, x, W, act == DLRM_ACT_RELU)
         e_dW = rel_err(dW_d.cpu().numpy(), rdW, sdW)
         e_db = rel_err(db_d.cpu().numpy(), rdb, sdb)

@@ -5,6 +5,10 @@ benchmark times.  The oracle checks sampled batch rows one by one: the sampled
 bags are restricted to the table rows they touch (a monotone renumbering, so
 pooling, sort order and segments are unchanged), and those rows are
 regenerated on the host from the same counter hash the device fill wrote.
+Every oracle input is generated on the host: a call that consumes another
+call's output (the interaction, its backward, the update) is checked on
+host-made inputs of the same shape, the oracle's own upstream results or
+seeded arrays, not on the GPU's.
 """
 import numpy as np
 import pytest
@@ -24,7 +28,7 @@ from recommendation_model_sparse_amd import (
 from recommendation_model_sparse_amd.configs import make_config
 from recommendation_model_sparse_amd.synth import subset_tables
 
-from gpu_util import DEV, as_f64, device_tables, rel_err, row_inf_rel, say, to_dev, to_host
+from gpu_util import DEV, as_f64, bf16_half_ulp, device_tables, rel_err, row_inf_rel, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -75,9 +79,11 @@ def check_forward(wl, batch, tabs, n_samples=256):
     assert err <= POOL_TOL[wl.dtype]
     if wl.bags == "onehot":
         assert np.array_equal(got, ref.astype(np.float32))
-    # interaction on the GPU's own pooled rows
-    iref, iscale = oracle.interact_fwd(batch.dense[S], got)
-    igot = inter[torch.from_numpy(S).to(DEV)].cpu().numpy()
+    # the interaction at full size on a seeded host-made pooled input
+    pz = (np.random.default_rng(wl.seed + 17).standard_normal((wl.B, wl.T, wl.D)) * 0.1).astype(np.float32)
+    inter_z = dlrm_interact_fwd(dense, to_dev(pz))
+    iref, iscale = oracle.interact_fwd(batch.dense[S], pz[S])
+    igot = inter_z[torch.from_numpy(S).to(DEV)].cpu().numpy()
     ierr = rel_err(igot, iref, iscale)
     say(f"   interaction max rel err {ierr:.3e}")
     assert ierr <= 1e-5
@@ -117,29 +123,30 @@ def test_workload_training_step():
     say(f"[workload] {wl.name} training step B={wl.B} nnz={b.nnz}")
     di, do = to_dev(b.indices), to_dev(b.offsets)
     dense = to_dev(b.dense)
+    # every bag over the rows it touches (monotone renumbering), regenerated on the host
+    sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
+    host_tabs = subset_tables(wl, row_ids)
+    pref, _ = oracle.emb_bag_fwd(host_tabs, sub.indices, sub.offsets, None, wl.B)
+    pooled_h = pref.astype(np.float32)  # one-hot: the rows themselves, exact
     pooled = emb_bag_fwd(tabs, di, do)
-    dlrm_interact_fwd(dense, pooled)
-    g = to_dev(b.grad_out())
-    gd, gp = dlrm_interact_bwd(g, dense, pooled)
+    # the backward calls take the oracle's upstream results: its pooled rows, then its gradient
+    gd, gp = dlrm_interact_bwd(to_dev(b.grad_out()), dense, to_dev(pooled_h))
+    rd, rp, md, mp = oracle.interact_bwd(b.grad_out(), b.dense, pooled_h)
+    gin = rp.astype(np.float32)
     outs = AdagradOutputs(b.nnz, DEV)
-    emb_bag_bwd_adagrad(tabs, states, di, do, None, gp, wl.lr, wl.eps, outputs=outs)
+    emb_bag_bwd_adagrad(tabs, states, di, do, None, to_dev(gin), wl.lr, wl.eps, outputs=outs)
     torch.cuda.synchronize()
+    assert np.array_equal(pooled.cpu().numpy(), pooled_h)
 
-    # interaction backward on sampled rows
-    S = sample_rows(wl.B, 256, 5)
-    pooled_h = pooled.cpu().numpy()
-    rd, rp, md, mp = oracle.interact_bwd(b.grad_out()[S], b.dense[S], pooled_h[S])
-    e1 = rel_err(gd.cpu().numpy()[S], rd, md)
-    e2 = rel_err(gp.cpu().numpy()[S], rp, mp)
+    e1 = rel_err(gd.cpu().numpy(), rd, md)
+    e2 = rel_err(gp.cpu().numpy(), rp, mp)
     say(f"   interact_bwd max rel err {e1:.3e} / {e2:.3e}")
     assert e1 <= 1e-5 and e2 <= 1e-5
 
-    # Adagrad on every lookup, over the touched rows only (monotone renumbering)
-    sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
-    host_tabs = subset_tables(wl, row_ids)
+    # Adagrad on every lookup, over the touched rows only
     host_states = [np.zeros(len(r), np.float32) for r in row_ids]
     r = oracle.emb_bag_bwd_adagrad(host_tabs, host_states, sub.indices, sub.offsets, None, wl.B,
-                                   gp.cpu().numpy(), wl.lr, wl.eps)
+                                   gin, wl.lr, wl.eps)
     U = int(outs.num_unique.item())
     assert U == r.U
     assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
@@ -169,6 +176,58 @@ def test_workload_training_step():
             assert np.array_equal(got.view(np.uint8), wl.table_rows(t, cand).view(np.uint8))
             assert torch.all(states[t][torch.from_numpy(cand).to(DEV)] == 0)
     say(f"   Adagrad U={U} worst row rel err {worst:.3e}")
+    del tabs, states
+    torch.cuda.empty_cache()
+
+
+def test_workload_multihot_backward():
+    """The timed backward at its full size: 26 bf16 tables (D = 128), B = 16384 multi-hot bags
+    (~8.5M lookups, Zipf rows, so hot rows make segments over hundreds of chunks), row-wise Adagrad
+    in place with every integer output requested.  The gradient is a seeded stand-alone one (not the
+    GPU's interaction backward), so the oracle's inputs are all host-generated.  Integer outputs are
+    compared whole and bit-exactly; every touched row and state against the oracle."""
+    wl = make_config(3)
+    b = wl.batch(0)
+    gp = b.grad_pooled()
+    tabs = device_tables(wl)
+    states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
+    say(f"[workload] {wl.name} multi-hot backward B={wl.B} nnz={b.nnz}")
+    outs = AdagradOutputs(b.nnz, DEV)
+    emb_bag_bwd_adagrad(tabs, states, to_dev(b.indices), to_dev(b.offsets), None, to_dev(gp), wl.lr, wl.eps,
+                        outputs=outs)
+    torch.cuda.synchronize()
+
+    sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
+    host_tabs = subset_tables(wl, row_ids)
+    r = oracle.emb_bag_bwd_adagrad(host_tabs, [np.zeros(len(x), np.float32) for x in row_ids], sub.indices,
+                                   sub.offsets, None, wl.B, gp, wl.lr, wl.eps)
+    U = int(outs.num_unique.item())
+    assert U == r.U
+    assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
+    assert np.array_equal(outs.segment_offsets.cpu().numpy()[:U + 1], r.seg_offsets)
+    rowbase = np.zeros(wl.T + 1, dtype=np.int64)
+    np.cumsum(wl.rows, out=rowbase[1:])
+    tt, rr = r.table_and_row()
+    full_keys = rowbase[tt] + np.concatenate([row_ids[t][rr[tt == t]] for t in range(wl.T)])
+    assert np.array_equal(outs.unique_keys.cpu().numpy()[:U], full_keys)
+    longest = int(np.max(np.diff(r.seg_offsets)))
+    rng = np.random.default_rng(11)
+    for t in range(wl.T):
+        sel = tt == t
+        rows_t = torch.from_numpy(row_ids[t][rr[sel]]).to(DEV)
+        ref = r.new_rows[sel]
+        got = as_f64(to_host(tabs[t][rows_t]))
+        tol = bf16_half_ulp(ref) * 1.0001 + 1e-4 * np.max(np.abs(ref), axis=1, keepdims=True)
+        assert np.all(np.abs(got - ref) <= tol), f"table {t}"
+        gs = states[t][rows_t].cpu().numpy().astype(np.float64)
+        rs = r.new_state[sel]
+        assert np.all(np.abs(gs - rs) <= 1e-4 * np.abs(rs)), f"table {t} state"
+        cand = np.setdiff1d(rng.integers(0, wl.rows[t], 512), row_ids[t])
+        if len(cand):
+            dc = torch.from_numpy(cand).to(DEV)
+            assert np.array_equal(to_host(tabs[t][dc]).view(np.uint8), wl.table_rows(t, cand).view(np.uint8))
+            assert torch.all(states[t][dc] == 0)
+    say(f"   U={U} longest segment {longest} lookups: rows and states within the gates")
     del tabs, states
     torch.cuda.empty_cache()
 
