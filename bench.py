@@ -193,6 +193,32 @@ def time_full_step(tabs, states, batches, host_batches, steps, wl, max_nnz):
             "layers": "bottom 13(16)-512-256-128, top 480-1024-1024-512-256-1, bf16 GEMMs (hipBLASLt), fp32 accumulation"}
 
 
+def hbm_context(dev):
+    """What plain streaming reaches on this GPU, as context for the kernels' figures: a 2 GiB
+    device-to-device copy, far larger than the caches (read + write bytes; HIP events, median of 5)."""
+    import torch
+    n = 1 << 29  # 2 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def med(fn):
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts[1:])) / 1e3
+
+    t_copy = med(lambda: dst.copy_(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * 4 * n / t_copy / 1e9, "bytes_copied": 4 * n,
+            "how": "2 GiB fp32 device copy, read + write bytes over its time, median of 5"}
+
+
 def inference_summary(inf, wl, nnz_avg):
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
     alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
@@ -229,6 +255,7 @@ def bench_inference_big(args, dev):
     inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     inf = time_inference(tabs, batches, args.steps, pooled, inter)
+    hbm = hbm_context(dev)
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     summ = inference_summary(inf, wl, nnz_avg)
     res = {
@@ -250,7 +277,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--cpu-samples", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--overlap-plan", action="store_true",
@@ -383,6 +410,8 @@ def main():
     torch.cuda.synchronize()
     call_ms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
                for k, n in enumerate(names)}
+    step_ev_ms = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)])
+    step_pct = {f"p{q}": float(np.percentile(step_ev_ms, q)) for q in (10, 50, 90)}
     log("[bench] per call (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in call_ms.items()))
 
     # per-kernel HIP event times recorded by the library itself (dlrm_trace_*), third region
@@ -402,6 +431,7 @@ def main():
     variants = time_variants(tabs, batches, args.steps, ws, outs, gpooled, wl)
     full = time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz)
 
+    hbm = hbm_context(dev)
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     U_last = int(outs.num_unique.item())
     es = wl.elem_size
@@ -459,6 +489,8 @@ def main():
                    "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
         "gathered_GBps": gathered_gbps,
         "gathered_frac_of_hbm_peak": gathered_gbps / HBM_PEAK_GBPS,
+        "hbm_context": hbm,
+        "step_ms_per_step_events": step_pct,
         "fwd_samples_per_s": wl.B / ((call_ms["emb_bag_fwd"] + call_ms["dlrm_interact_fwd"]) / 1e3),
         "unique_rows": U_last,
         "call_ms": call_ms,
