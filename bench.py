@@ -63,28 +63,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, batch, n_samples: int):
-    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+def cpu_baseline(wl, batches, n_samples: int, min_seconds: float = 10.0):
+    """The oracle, as it stands, on a bounded sample of the same workload (host cores): the full
+    step on the first n_samples samples of successive batches, until about min_seconds of work."""
     import oracle
     from recommendation_model_sparse_amd.synth import subset_tables
 
     cores = len(os.sched_getaffinity(0))
     S = np.arange(n_samples)
-    sub_wl, sub, row_ids = batch.sample_subset(S)
-    tabs = subset_tables(wl, row_ids)
-    states = [np.zeros(len(r), np.float32) for r in row_ids]
-    g = batch.grad_out()[S]
-    t0 = time.perf_counter()
-    pooled, _ = oracle.emb_bag_fwd(tabs, sub.indices, sub.offsets, sub.weights, len(S), threads=cores)
-    p32 = pooled.astype(np.float32)
-    oracle.interact_fwd(sub.dense, p32, threads=cores)
-    _, gp, _, _ = oracle.interact_bwd(g, sub.dense, p32, threads=cores)
-    oracle.emb_bag_bwd_adagrad(tabs, states, sub.indices, sub.offsets, sub.weights, len(S),
-                               gp.astype(np.float32), wl.lr, wl.eps)
-    dt = time.perf_counter() - t0
-    return {"value": len(S) / dt, "unit": "samples/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(S)} of {wl.B} samples of one batch ({sub.nnz} lookups): the full step "
-                      f"(pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s"}
+    done, lookups, dt = 0, 0, 0.0
+    for batch in batches:
+        sub_wl, sub, row_ids = batch.sample_subset(S)
+        tabs = subset_tables(wl, row_ids)
+        states = [np.zeros(len(r), np.float32) for r in row_ids]
+        g = batch.grad_out()[S]
+        t0 = time.perf_counter()
+        pooled, _ = oracle.emb_bag_fwd(tabs, sub.indices, sub.offsets, sub.weights, len(S), threads=cores)
+        p32 = pooled.astype(np.float32)
+        oracle.interact_fwd(sub.dense, p32, threads=cores)
+        _, gp, _, _ = oracle.interact_bwd(g, sub.dense, p32, threads=cores)
+        oracle.emb_bag_bwd_adagrad(tabs, states, sub.indices, sub.offsets, sub.weights, len(S),
+                                   gp.astype(np.float32), wl.lr, wl.eps)
+        dt += time.perf_counter() - t0
+        done += len(S)
+        lookups += sub.nnz
+        if dt >= min_seconds:
+            break
+    return {"value": done / dt, "unit": "samples/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done // len(S)} batch(es) x {len(S)} of {wl.B} samples ({lookups} lookups): the full "
+                      f"step (pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s"}
 
 
 def time_inference(tabs, batches, steps, pooled, inter):
@@ -510,7 +517,7 @@ def main():
     }
     if not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")
-        res["cpu_baseline"] = cpu_baseline(wl, host_batches[0], args.cpu_samples)
+        res["cpu_baseline"] = cpu_baseline(wl, host_batches, args.cpu_samples)
     print(json.dumps(res), flush=True)
 
 
