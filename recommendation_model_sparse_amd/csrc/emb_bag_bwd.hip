@@ -208,14 +208,17 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool valid) {
 }
 
 // Digits of RB bits (8..10): K = 2^RB / 256 digits per thread in the per-digit phases.
-// Per-tile digit counts with LDS atomics.  (Counting equal digits once per wavefront with the
-// ballot match mask, as the scatter ranks them, was slower here: 35 against 29 us per pass on the
-// multi-hot workload.)
+// Per-tile digit counts with LDS atomics.  Each thread counts kSortItems consecutive keys and adds
+// each run of equal digits with one atomic: after the first pass the keys arrive ordered by the
+// lower digits, so a tile holds long runs of one digit (hot rows, few tables per tile), and
+// atomics to one LDS address serialize.  (Counting equal digits once per wavefront with the
+// ballot match mask, as the scatter ranks them, was slower: 35 against 29 us per pass.)
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__ keys, uint32_t n,
                                                     int shift, uint32_t *__restrict__ counts,
                                                     uint32_t nblk) {
     constexpr int NBK = 1 << RB;
+    static_assert(kSortItems % 4 == 0, "keys are loaded 4 at a time");
     __shared__ uint32_t h[NBK];
     // the scatter's tile mapping: each XCD counts (and later scatters) one contiguous range of
     // tiles, so its count writes for a digit share lines in its own L2
@@ -223,15 +226,31 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
     if (tile >= nblk) return;  // block-uniform, before any barrier
     for (int d = threadIdx.x; d < NBK; d += 256) h[d] = 0;
     __syncthreads();
-    const uint32_t base = tile * kSortTile;
-    // all of a thread's keys are loaded (unconditionally) before the first atomic: interleaved,
-    // the compiler waits for each load in turn
+    const uint32_t tile0 = tile * kSortTile, base = tile0 + threadIdx.x * kSortItems;
+    // all of a thread's keys are loaded before the first atomic: interleaved, the compiler waits
+    // for each load in turn
     uint32_t key[kSortItems];
+    if (tile0 + kSortTile <= n) {  // a whole tile: 16-byte loads (base is a multiple of 16 keys)
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i) key[i] = keys[min(base + i * 256 + threadIdx.x, n - 1)];
+        for (int i = 0; i < kSortItems; i += 4) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(keys + base + i);
+            key[i] = v.x, key[i + 1] = v.y, key[i + 2] = v.z, key[i + 3] = v.w;
+        }
+    } else {
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i)
-        if (base + i * 256 + threadIdx.x < n) atomicAdd(&h[(key[i] >> shift) & (NBK - 1)], 1u);
+        for (int i = 0; i < kSortItems; ++i) key[i] = keys[min(base + i, n - 1)];
+    }
+    uint32_t cur = (key[0] >> shift) & (NBK - 1), run = 0;
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const uint32_t d = (key[i] >> shift) & (NBK - 1);
+        if (d != cur) {
+            if (run) atomicAdd(&h[cur], run);
+            cur = d, run = 0;
+        }
+        run += base + i < n ? 1u : 0u;
+    }
+    if (run) atomicAdd(&h[cur], run);
     __syncthreads();
     for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + tile] = h[d];
 }
