@@ -197,14 +197,18 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
 // ballot per digit bit (the wave's match mask of equal digits).
 template <int RB>
 __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool valid) {
-    uint64_t peers = __ballot(valid);
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    const uint32_t nd = ~d;
 #pragma unroll
     for (int bit = 0; bit < RB; ++bit) {
-        const bool on = (d >> bit) & 1u;
-        const uint64_t m = __ballot(on);
-        peers &= on ? m : ~m;
+        const uint64_t m = __ballot((d >> bit) & 1u);
+        // all ones where this lane's bit is clear (keep the lanes whose bit is clear too), else zero
+        const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(nd << (31 - bit)) >> 31);
+        lo &= static_cast<uint32_t>(m) ^ flip;
+        hi &= static_cast<uint32_t>(m >> 32) ^ flip;
     }
-    return peers;
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Digits of RB bits (8..10): K = 2^RB / 256 digits per thread in the per-digit phases.
