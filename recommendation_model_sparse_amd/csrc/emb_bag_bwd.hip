@@ -1062,7 +1062,7 @@ struct PlanShape {
     Layout L;
     uint64_t sumV;
     int passes;
-    int rb;
+    int rb[4];  // digit width of each pass (8..10 bits)
     int cur;  // ping-pong half holding the sorted keys and payloads
 };
 
@@ -1077,8 +1077,11 @@ int plan_shape(const int64_t *rows, int32_t T, int32_t D, int64_t nnz, PlanShape
     int bits = 0;
     while (bits < 32 && ((sumV - 1) >> bits) != 0) ++bits;
     ps->passes = (bits + 9) / 10;
-    ps->rb = ps->passes > 0 ? (bits + ps->passes - 1) / ps->passes : 8;
-    if (ps->rb < 8) ps->rb = 8;
+    // the bits split as evenly as they go, wider digits first, none narrower than 8 bits
+    for (int p = 0; p < 4; ++p) {
+        const int w = ps->passes > 0 ? bits / ps->passes + (p < bits % ps->passes ? 1 : 0) : 8;
+        ps->rb[p] = w < 8 ? 8 : w;
+    }
     ps->cur = ps->passes & 1;
     return DLRM_OK;
 }
@@ -1157,7 +1160,7 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
         DLRM_LAUNCH("expand", k_expand<int64_t>, dim3((ea.nbags + 255) / 256), dim3(256), 0, stream, ea);
 
     // K5
-    int cur = 0;
+    int cur = 0, shift = 0;
     uint32_t *counts = u32(L.counts), *totals = u32(L.totals);
     for (int p = 0; p < ps.passes; ++p) {
         const bool last = p + 1 == ps.passes;
@@ -1178,9 +1181,10 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
             io.pout[q++] = last ? reinterpret_cast<uint32_t *>(sorted_pos_out) : u32(L.pos[cur ^ 1]);
         }
         const int NP = q;
-        if (ps.rb == 8) launch_radix_pass<8>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
-        else if (ps.rb == 9) launch_radix_pass<9>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
-        else launch_radix_pass<10>(io, NP, n, ps.rb * p, counts, L.nblk, totals, stream);
+        if (ps.rb[p] == 8) launch_radix_pass<8>(io, NP, n, shift, counts, L.nblk, totals, stream);
+        else if (ps.rb[p] == 9) launch_radix_pass<9>(io, NP, n, shift, counts, L.nblk, totals, stream);
+        else launch_radix_pass<10>(io, NP, n, shift, counts, L.nblk, totals, stream);
+        shift += ps.rb[p];
         cur ^= 1;
     }
     const uint32_t *skeys = u32(L.keys[cur]);

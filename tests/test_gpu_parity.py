@@ -271,9 +271,10 @@ def test_adagrad_random(D, dtype, weighted):
 
 @pytest.mark.parametrize("rows,label", [([200], "8-bit keys: 1 pass of 8"),
                                         ([300, 300], "10-bit keys: 1 pass of 10"),
-                                        ([70000, 5], "17-bit keys: 2 passes of 9"),
+                                        ([70000, 5], "17-bit keys: 2 passes, 9 + 8 bits"),
+                                        ([(1 << 18) + 3], "19-bit keys: 2 passes, 10 + 9 bits"),
                                         ([(1 << 20) + 7], "21-bit keys: 3 passes of 8"),
-                                        ([(1 << 24) + 5], "25-bit keys: 3 passes of 9"),
+                                        ([(1 << 24) + 5], "25-bit keys: 3 passes, 9 + 8 + 8 bits"),
                                         ([1], "one row: no pass")])
 def test_adagrad_sort_passes(rows, label):
     run_adagrad(rows, 4, "f32", 1500, "multi", True, seed=len(rows) + rows[0] % 97, max_len=10,
