@@ -269,11 +269,11 @@ def bench_inference_big(args, dev):
         "metric": "inference samples/sec (lookup fused with the interaction), 1 MI355X",
         "value": summ["fused_samples_per_s"], "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
         "warmup": 3, "ms_per_step": inf["fused"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 tables, fp32 accumulation",
+        "vs_baseline": None, "dtype": "f32",
         "data": f"synthetic (seeded; counter-hash tables, {'Zipf(1.2)' if args.dist == 'zipf' else 'uniform'} rows)",
         "config": {"workload": "one-hot inference: 8 bf16 tables of 50M x 128 (102.4 GB), B=65536, N=9",
-                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_GB": wl.table_bytes() / 1e9,
-                   "parallelism": "single GPU"},
+                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "bf16",
+                   "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
         "inference": summ,
     }
     print(json.dumps(res), flush=True)
@@ -486,13 +486,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 tables, fp32 accumulation",
+        "dtype": "f32",
         "data": f"synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), {args.dist} rows)",
         "config": {"workload": "multi-hot bf16 training step: 26 tables, D=128, B=16384, "
                                "bag length truncated-geometric [1,100] mean 20, "
                                + ("Zipf(1.05)" if args.dist == "zipf" else "uniform") +
                                " rows, V log-uniform [1e3,1e7]",
-                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "nnz_avg": nnz_avg,
+                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "bf16", "nnz_avg": nnz_avg,
                    "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
         "gathered_GBps": gathered_gbps,
         "gathered_frac_of_hbm_peak": gathered_gbps / HBM_PEAK_GBPS,
