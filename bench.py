@@ -507,6 +507,9 @@ def main():
                      "frac": dom["frac_hbm_peak"] if dom else None,
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
+                     # the bytes the counters saw per launch over the launch time: how hard the kernel
+                     # drives HBM / the Infinity Cache, re-reads included
+                     "traffic_GBps": traffic["bytes"] / (kern_launch_ms[dominant] / 1e3) / 1e9 if traffic else None,
                      "ms_per_launch": kern_launch_ms[dominant],
                      "requested_bytes_per_launch": requested.get(dominant),
                      "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
