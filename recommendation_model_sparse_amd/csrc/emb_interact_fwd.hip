@@ -71,6 +71,25 @@ __device__ __forceinline__ void upper_block(int kb, int NB, int &I, int &J) {
     J = I + kb;
 }
 
+// The k-split Gram of the samples staged in LDS (X [S][N][XS]), one sample per wave at a time.
+template <int NR, int CPL>
+__device__ __forceinline__ void lds_ksplit(const FusedArgs &a, const float *X, int XS, int Sb, uint32_t b0, int wv,
+                                           int lane) {
+    const int N = a.N, W = a.P + 64 * CPL;
+    int pi, pj;
+    const bool holds = gram_lane_pair<NR>(lane, pi, pj);
+    for (int s = wv; s < Sb; s += 4) {
+        const float *xs = X + static_cast<size_t>(s) * N * XS + lane * CPL;
+        float x[NR][CPL];
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) x[i][c] = i < N ? xs[i * XS + c] : 0.f;
+        const float z = gram_ksplit<NR, CPL>(x);
+        if (holds && pj < N) a.out[(static_cast<uint64_t>(b0) + s) * W + triu_pos(pi, pj, N)] = z;
+    }
+}
+
 template <int DT, int G, int KC, bool WEIGHTED, bool WAVE_PER_BAG>
 __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
     constexpr int EPC = Elem<DT>::kPerChunk;
@@ -236,19 +255,8 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
     const int P = a.P, W = P + D;
     if constexpr (D == 64 || D == 128 || D == 256) {
         if (a.ksplit) {  // small N: the k-split Gram, one sample per wave
-            constexpr int CPL = D / 64;
-            int pi, pj;
-            gram_pair(lane, pi, pj);
-            for (int s = wv; s < Sb; s += 4) {
-                const float *xs = X + static_cast<size_t>(s) * N * XS + lane * CPL;
-                float x[kGramRows][CPL];
-#pragma unroll
-                for (int i = 0; i < kGramRows; ++i)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) x[i][c] = i < N ? xs[i * XS + c] : 0.f;
-                const float z = gram_ksplit<CPL>(x);
-                if (lane < kGramPairs && pj < N) a.out[(static_cast<uint64_t>(b0) + s) * W + triu_pos(pi, pj, N)] = z;
-            }
+            if (gram_rows(N) == 9) lds_ksplit<9, D / 64>(a, X, XS, Sb, b0, wv, lane);
+            else lds_ksplit<11, D / 64>(a, X, XS, Sb, b0, wv, lane);
             for (int i = tid; i < Sb * D; i += 256) {
                 const int s = i / D, d = i - s * D;
                 a.out[(static_cast<uint64_t>(b0) + s) * W + P + d] = X[static_cast<size_t>(s) * N * XS + d];
@@ -488,11 +496,11 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 // whose base is uniform.  The bag's rows are summed in order from zero, as the unfused
 // lane-group-per-bag pooling sums them, and the Gram is the unfused interaction's: the bits
 // match the two-call path.  M samples per wave go through each dependent load step together.
-template <int DT, int CPL, int M, bool WEIGHTED>
+template <int DT, int NR, int CPL, int M, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_emb_interact_fwd_ksplit(FusedArgs a) {
     constexpr int D = 64 * CPL;
     constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
-    constexpr int TMAX = kGramRows - 1;
+    constexpr int TMAX = NR - 1;
     const uint32_t b0 = (blockIdx.x * 4 + wave_id()) * M;
     if (b0 >= a.B) return;
     const int lane = threadIdx.x & 63;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd_ksplit(FusedArgs a) {
         if (!has) idx0[m] = 0;
     }
     // step 3: dense rows and the first row of every bag, all in flight together
-    float x[M][kGramRows][CPL];
+    float x[M][NR][CPL];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const uint32_t b = min(b0 + m, a.B - 1);
@@ -592,15 +600,15 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd_ksplit(FusedArgs a) {
         }
     // step 5: the Gram and [triu | dense]
     int pi, pj;
-    gram_pair(lane, pi, pj);
+    const bool holds = gram_lane_pair<NR>(lane, pi, pj);
     const int P = a.P;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const uint32_t b = b0 + m;
         if (b >= a.B) break;  // wave-uniform
-        const float z = gram_ksplit<CPL>(x[m]);
+        const float z = gram_ksplit<NR, CPL>(x[m]);
         float *orow = a.out + static_cast<uint64_t>(b) * (P + D);
-        if (lane < kGramPairs && pj < N) orow[triu_pos(pi, pj, N)] = z;
+        if (holds && pj < N) orow[triu_pos(pi, pj, N)] = z;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) orow[P + lane * CPL + c] = x[m][0][c];
     }
@@ -608,15 +616,21 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd_ksplit(FusedArgs a) {
 
 template <int DT>
 void dispatch_ksplit(const FusedArgs &a, int D, bool weighted, hipStream_t stream) {
-#define DLRM_KSPLIT(CPL, M)                                                                                         \
+#define DLRM_KSPLIT(NR, CPL, M)                                                                                     \
     do {                                                                                                            \
         const dim3 grid(static_cast<uint32_t>((a.B + 4 * (M) - 1) / (4 * (M)))), block(256);                       \
-        if (weighted) DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, CPL, M, true>), grid, block, 0, stream, a); \
-        else DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, CPL, M, false>), grid, block, 0, stream, a); \
+        if (weighted) DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, NR, CPL, M, true>), grid, block, 0, stream, a); \
+        else DLRM_LAUNCH("emb_interact_fwd_ksplit", (k_emb_interact_fwd_ksplit<DT, NR, CPL, M, false>), grid, block, 0, stream, a); \
     } while (0)
-    if (D == 64) DLRM_KSPLIT(1, DLRM_FUSED_M);
-    else if (D == 128) DLRM_KSPLIT(2, DLRM_FUSED_M);
-    else DLRM_KSPLIT(4, 1);
+    if (gram_rows(a.N) == 9) {
+        if (D == 64) DLRM_KSPLIT(9, 1, DLRM_FUSED_M);
+        else if (D == 128) DLRM_KSPLIT(9, 2, DLRM_FUSED_M);
+        else DLRM_KSPLIT(9, 4, 1);
+    } else {
+        if (D == 64) DLRM_KSPLIT(11, 1, DLRM_FUSED_M);
+        else if (D == 128) DLRM_KSPLIT(11, 2, DLRM_FUSED_M);
+        else DLRM_KSPLIT(11, 4, 1);
+    }
 #undef DLRM_KSPLIT
 }
 

@@ -141,10 +141,11 @@ __global__ __launch_bounds__(256) void k_interact_fwd_valu(const float *__restri
     for (int d = threadIdx.x; d < D; d += blockDim.x) orow[P + d] = dsrc[d];
 }
 
-// Small interactions (N <= 11, D = 64 * CPL): the k-split Gram (gram.h), M samples per wave.
-// Lane l loads columns l*CPL.. of every row (each row read is one coalesced load), and every
-// load is unconditional (rows past N re-read row N-1 and are zeroed) so all are in flight at once.
-template <int CPL, int M>
+// Small interactions (N <= 11, D = 64 * CPL): the k-split Gram (gram.h) over NR = gram_rows(N)
+// rows, M samples per wave.  Lane l loads columns l*CPL.. of every row (each row read is one
+// coalesced load), and every load is unconditional (rows past N re-read row N-1 and are zeroed)
+// so all are in flight at once.
+template <int NR, int CPL, int M>
 __global__ __launch_bounds__(256) void k_interact_fwd_ksplit(const float *__restrict__ dense,
                                                              const float *__restrict__ pooled,
                                                              float *__restrict__ out, uint32_t B,
@@ -153,12 +154,12 @@ __global__ __launch_bounds__(256) void k_interact_fwd_ksplit(const float *__rest
     const uint32_t b0 = (blockIdx.x * 4 + wave_id()) * M;
     if (b0 >= B) return;
     const int lane = threadIdx.x & 63;
-    float x[M][kGramRows][CPL];
+    float x[M][NR][CPL];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const uint32_t b = min(b0 + m, B - 1);
 #pragma unroll
-        for (int i = 0; i < kGramRows; ++i) {
+        for (int i = 0; i < NR; ++i) {
             const int ii = i < N ? i : N - 1;
             uint32_t w[CPL];
             gload_words<CPL>(x_row(dense, pooled, b, N, D, ii) + lane * CPL, w);
@@ -167,14 +168,14 @@ __global__ __launch_bounds__(256) void k_interact_fwd_ksplit(const float *__rest
         }
     }
     int pi, pj;
-    gram_pair(lane, pi, pj);
+    const bool holds = gram_lane_pair<NR>(lane, pi, pj);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const uint32_t b = b0 + m;
         if (b >= B) break;  // wave-uniform
-        const float z = gram_ksplit<CPL>(x[m]);
+        const float z = gram_ksplit<NR, CPL>(x[m]);
         float *orow = out + static_cast<uint64_t>(b) * (P + D);
-        if (lane < kGramPairs && pj < N) orow[triu_pos(pi, pj, N)] = z;
+        if (holds && pj < N) orow[triu_pos(pi, pj, N)] = z;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) orow[P + lane * CPL + c] = x[m][0][c];
     }
@@ -269,6 +270,16 @@ __global__ __launch_bounds__(256) void k_interact_bwd(const float *__restrict__ 
     }
 }
 
+template <int NR>
+void launch_fwd_ksplit(const float *dense, const float *pooled, float *out, uint32_t b, int N, int D, int P,
+                       hipStream_t stream) {
+    switch (D) {
+        case 64: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<NR, 1, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+        case 128: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<NR, 2, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+        default: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<NR, 4, 1>), dim3((b + 3) / 4), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
+    }
+}
+
 template <int NB>
 bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32_t B, int N, int D,
                      int P, hipStream_t stream) {
@@ -324,11 +335,8 @@ extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_
     const uint32_t b = static_cast<uint32_t>(B);
     bool done = false;
     if (gram_ksplit_ok(N, D)) {
-        switch (D) {
-            case 64: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<1, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
-            case 128: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<2, 2>), dim3((b + 7) / 8), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
-            default: DLRM_LAUNCH("interact_fwd_ksplit", (k_interact_fwd_ksplit<4, 1>), dim3((b + 3) / 4), dim3(256), 0, stream, dense, pooled, out, b, N, P); break;
-        }
+        if (gram_rows(N) == 9) launch_fwd_ksplit<9>(dense, pooled, out, b, N, D, P, stream);
+        else launch_fwd_ksplit<11>(dense, pooled, out, b, N, D, P, stream);
         return launch_status();
     }
     switch ((N + 15) / 16) {
