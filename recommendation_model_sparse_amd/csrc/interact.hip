@@ -289,7 +289,9 @@ bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32
         case 16: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 16, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 32: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 64: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 2, (NB <= 4 ? 2 : 1)>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        case 128: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 4, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        // one chunk's operands at a time (16 registers): more waves per SIMD, which beat loading the
+        // whole row at once (55 against 60 us for 16384 samples at N = 27)
+        case 128: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 4, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 256: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 8, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 512: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 16, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         default: return false;
