@@ -444,6 +444,8 @@ def main():
     es = wl.elem_size
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
     gathered = nnz_avg * D * es
+    sort_passes = round(kern_ms.get("radix_scatter", 0.0) / kern_launch_ms["radix_scatter"]) \
+        if kern_launch_ms.get("radix_scatter") else 0
     # algorithmic bytes per launch of the main kernels
     alg = {
         "pool_wave_per_bag": gathered + nnz_avg * 8 + (T * B + 1) * 8 + B * T * D * 4,
@@ -453,9 +455,12 @@ def main():
         "seg_reduce_adagrad": nnz_avg * 8 + B * T * D * 4 + U_last * (2 * D * es + 8),
         "interact_fwd_mfma": B * (N * D * 4 + (P + D) * 4),
         "interact_bwd": B * ((P + D) * 4 + 2 * N * D * 4),
-        "radix_scatter": nnz_avg * 3 * 4 * 2,
+        # key, grad row and position read and written per pass; the first pass makes the
+        # positions instead of reading them (mean over the passes)
+        "radix_scatter": nnz_avg * (3 * 4 * 2 - 4 / max(1, sort_passes)),
         "radix_hist": nnz_avg * 4,
-        "expand": nnz_avg * (8 + 4 * 3) + (T * B + 1) * 8,
+        # index read, key and grad row written per lookup; offsets per bag
+        "expand": nnz_avg * (8 + 4 * 2) + (T * B + 1) * 8,
     }
     # what the kernels load including re-reads (one gradient row per lookup in the backward)
     requested = {"seg_reduce_adagrad": nnz_avg * (4 * D + 8) + U_last * (2 * D * es + 8),

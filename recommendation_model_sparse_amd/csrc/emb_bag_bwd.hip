@@ -144,6 +144,37 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *t
     return off + inc - v;
 }
 
+// A thread's contiguous range [b0, b1) of a count array: its sum, and the range rewritten as
+// the exclusive prefix starting at `run`.  Counts are loaded KB at a time (clamped in bounds),
+// so a range costs one round trip per KB entries rather than one per entry.
+template <int KB>
+__device__ __forceinline__ uint32_t range_sum(const uint32_t *row, uint32_t b0, uint32_t b1) {
+    uint32_t s = 0;
+    for (uint32_t i0 = b0; i0 < b1; i0 += KB) {
+        uint32_t v[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) v[k] = row[min(i0 + k, b1 - 1)];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) s += i0 + k < b1 ? v[k] : 0u;
+    }
+    return s;
+}
+
+template <int KB>
+__device__ __forceinline__ void range_exclusive(uint32_t *row, uint32_t b0, uint32_t b1, uint32_t run) {
+    for (uint32_t i0 = b0; i0 < b1; i0 += KB) {
+        uint32_t v[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) v[k] = row[min(i0 + k, b1 - 1)];
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+            if (i0 + k < b1) {
+                row[i0 + k] = run;
+                run += v[k];
+            }
+    }
+}
+
 // ---------------------------------------------------------------- K4 expand
 
 struct ExpandArgs {
@@ -152,9 +183,9 @@ struct ExpandArgs {
     const void *indices;
     const float *weights;
     uint32_t *keys;
-    uint32_t *pos;
+    uint32_t *pos;   // NULL: the first radix pass makes the positions itself
     uint32_t *grow;
-    uint32_t *wgt;
+    uint32_t *wgt;   // NULL: the first radix pass reads the caller's weights itself
     uint32_t B;
     uint32_t T;
     uint32_t nbags;
@@ -177,17 +208,28 @@ __global__ __launch_bounds__(256) void k_expand(ExpandArgs a) {
     }
     __syncthreads();
     const int64_t p0 = so[0], p1 = so[nb];
-    for (int64_t j = p0 + threadIdx.x; j < p1; j += 256) {
-        int lo = 0, hi = nb;  // so[lo] <= j < so[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (so[mid] <= j) lo = mid;
-            else hi = mid;
+    // EU lookups per thread and round: their indices are loaded together (clamped in bounds)
+    // before the first is used, so a round costs one load round trip
+    constexpr int EU = 8;
+    for (int64_t j0 = p0 + threadIdx.x; j0 < p1; j0 += 256 * EU) {
+        IT ix[EU];
+#pragma unroll
+        for (int u = 0; u < EU; ++u) ix[u] = indices[min(j0 + u * 256, p1 - 1)];
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+            const int64_t j = j0 + u * 256;
+            if (j >= p1) break;
+            int lo = 0, hi = nb;  // so[lo] <= j < so[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (so[mid] <= j) lo = mid;
+                else hi = mid;
+            }
+            a.keys[j] = s_base[lo] + static_cast<uint32_t>(ix[u]);
+            if (a.pos) a.pos[j] = static_cast<uint32_t>(j);
+            a.grow[j] = s_grow[lo];
+            if (a.wgt) a.wgt[j] = __float_as_uint(a.weights[j]);
         }
-        a.keys[j] = s_base[lo] + static_cast<uint32_t>(indices[j]);
-        if (a.pos) a.pos[j] = static_cast<uint32_t>(j);  // only when the sorted positions are an output
-        a.grow[j] = s_grow[lo];
-        if (a.weights) a.wgt[j] = __float_as_uint(a.weights[j]);
     }
 }
 
@@ -265,22 +307,18 @@ __global__ __launch_bounds__(256) void k_radix_scan(uint32_t *__restrict__ count
     uint32_t *row = counts + static_cast<size_t>(blockIdx.x) * nblk;
     const uint32_t per = (nblk + 255) / 256;
     const uint32_t b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
-    uint32_t s = 0;
-    for (uint32_t i = b0; i < b1; ++i) s += row[i];
     uint32_t tot;
-    uint32_t run = block_exclusive_scan(s, &tot);
-    for (uint32_t i = b0; i < b1; ++i) {
-        const uint32_t c = row[i];
-        row[i] = run;
-        run += c;
-    }
+    const uint32_t run = block_exclusive_scan(range_sum<16>(row, b0, b1), &tot);
+    range_exclusive<16>(row, b0, b1, run);
     if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
 struct SortIO {
     const uint32_t *kin;
     uint32_t *kout;
-    const uint32_t *pin[3];  // payload words in: grad row, then weight and position when present
+    // payload words in: grad row, then weight and position when present.  A NULL input is the
+    // identity (each item's own index: the original positions, in the first pass).
+    const uint32_t *pin[3];
     uint32_t *pout[3];
 };
 
@@ -314,7 +352,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
         const uint32_t k = min(base + i * kWave, n - 1);  // unconditional loads
         key[i] = io.kin[k];
 #pragma unroll
-        for (int q = 0; q < NP; ++q) pay[q][i] = io.pin[q][k];
+        for (int q = 0; q < NP; ++q) pay[q][i] = io.pin[q] ? io.pin[q][k] : k;
     }
     {
         // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
@@ -449,15 +487,9 @@ __global__ __launch_bounds__(256) void k_seg_scan(uint32_t *__restrict__ bcount,
                                                   uint32_t *__restrict__ fin_count) {
     const uint32_t per = (nblk + 255) / 256;
     const uint32_t b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
-    uint32_t s = 0;
-    for (uint32_t i = b0; i < b1; ++i) s += bcount[i];
     uint32_t tot;
-    uint32_t run = block_exclusive_scan(s, &tot);
-    for (uint32_t i = b0; i < b1; ++i) {
-        const uint32_t c = bcount[i];
-        bcount[i] = run;
-        run += c;
-    }
+    const uint32_t run = block_exclusive_scan(range_sum<16>(bcount, b0, b1), &tot);
+    range_exclusive<16>(bcount, b0, b1, run);
     if (threadIdx.x == 0) {
         if (num_unique) *num_unique = tot;
         seg_offsets[tot] = n;
@@ -1148,9 +1180,12 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
     ea.indices = indices;
     ea.weights = per_sample_weights;
     ea.keys = u32(L.keys[0]);
-    ea.pos = sorted_pos_out ? u32(L.pos[0]) : nullptr;
+    // with at least one radix pass, the first pass takes the positions (the identity) and the
+    // weights from their sources, so they are not copied here; with none, they are written where
+    // the sorted ones belong
+    ea.pos = sorted_pos_out && ps.passes == 0 ? reinterpret_cast<uint32_t *>(sorted_pos_out) : nullptr;
     ea.grow = u32(L.grow[0]);
-    ea.wgt = u32(L.wgt[0]);
+    ea.wgt = weighted && ps.passes == 0 ? u32(L.wgt[0]) : nullptr;
     ea.B = static_cast<uint32_t>(B);
     ea.T = static_cast<uint32_t>(T);
     ea.nbags = static_cast<uint32_t>(T * B);
@@ -1173,11 +1208,11 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
         io.pin[q] = u32(L.grow[cur]);
         io.pout[q++] = u32(L.grow[cur ^ 1]);
         if (weighted) {
-            io.pin[q] = u32(L.wgt[cur]);
+            io.pin[q] = p == 0 ? reinterpret_cast<const uint32_t *>(per_sample_weights) : u32(L.wgt[cur]);
             io.pout[q++] = u32(L.wgt[cur ^ 1]);
         }
         if (sorted_pos_out) {
-            io.pin[q] = u32(L.pos[cur]);
+            io.pin[q] = p == 0 ? nullptr : u32(L.pos[cur]);
             io.pout[q++] = last ? reinterpret_cast<uint32_t *>(sorted_pos_out) : u32(L.pos[cur ^ 1]);
         }
         const int NP = q;
@@ -1188,11 +1223,6 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
         cur ^= 1;
     }
     const uint32_t *skeys = u32(L.keys[cur]);
-    if (sorted_pos_out && ps.passes == 0) {
-        if (hipMemcpyAsync(sorted_pos_out, u32(L.pos[0]), sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, stream) !=
-            hipSuccess)
-            return DLRM_ERR_HIP;
-    }
 
     // K6 (always: the update's finisher reads the segment offsets)
     uint32_t *seg_count = u32(L.seg_count);
