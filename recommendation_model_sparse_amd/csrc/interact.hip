@@ -11,8 +11,9 @@
 // blocks on or above the diagonal.  Each lane loads its A/B operands straight from global
 // memory with 16-byte loads (the k order inside a chunk is permuted identically for both
 // operands, which leaves every dot product's set of terms unchanged), so no LDS is needed and
-// one wavefront handles one sample.  A plain-VALU kernel serves shapes the MFMA tiling does not
-// cover (D not a multiple of 16).
+// one wavefront handles one sample, or at D = 128 and N <= 32 up to four in turn with the next
+// chunk's loads in flight during the matrix-core work.  A plain-VALU kernel serves shapes the
+// MFMA tiling does not cover (D not a multiple of 16).
 //
 // Backward: one wavefront per (sample, 128-column slice); the lane owns one or two columns d of
 // X in registers, G sits in LDS and is read with broadcast loads, and dX[i][d] = sum_j G[i][j]
@@ -107,6 +108,104 @@ __global__ __launch_bounds__(256) void k_interact_fwd_mfma(const float *__restri
 #pragma unroll
     for (int s = 0; s < DPL; ++s)
         if (lane + s * kWave < D) orow[P + lane + s * kWave] = dv[s];
+}
+
+// The same Gram as k_interact_fwd_mfma, SPW samples per wavefront in turn, one k-chunk of
+// operands in registers and the next one in flight: the loads of chunk c+1 (or of the next
+// sample's first chunk and dense vector) are issued before the matrix-core work of chunk c.
+template <int NB, int KC, int NCH, int SPW>
+__global__ __launch_bounds__(256) void k_interact_fwd_mfma_pipe(const float *__restrict__ dense,
+                                                                const float *__restrict__ pooled,
+                                                                float *__restrict__ out, uint32_t B,
+                                                                int N, int P) {
+    constexpr int D = KC * NCH;
+    constexpr int PL = KC / 4;
+    constexpr int NBLK = NB * (NB + 1) / 2;
+    constexpr int DPL = (D + kWave - 1) / kWave;
+    const uint32_t s0 = (blockIdx.x * 4 + wave_id()) * SPW;
+    if (s0 >= B) return;
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, q = lane >> 4;
+    bool rv[NB];
+    int ri[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) {
+        const int i = R * 16 + r16;
+        rv[R] = i < N;
+        ri[R] = rv[R] ? i : 0;
+    }
+    auto load_chunk = [&](uint32_t sample, int c, float (&x)[NB][PL]) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            const float *p = x_row(dense, pooled, sample, N, D, ri[R]) + q * PL + c * KC;
+#pragma unroll
+            for (int v = 0; v < PL; v += 4) {
+                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (rv[R]) f = *reinterpret_cast<const float4 *>(p + v);
+                x[R][v] = f.x, x[R][v + 1] = f.y, x[R][v + 2] = f.z, x[R][v + 3] = f.w;
+            }
+        }
+    };
+    auto load_dense = [&](uint32_t sample, float (&dv)[DPL]) {
+        const float *dsrc = dense + static_cast<uint64_t>(sample) * D;
+#pragma unroll
+        for (int s = 0; s < DPL; ++s) dv[s] = dsrc[min(lane + s * kWave, D - 1)];
+    };
+    float x[NB][PL], dv[DPL];
+    load_dense(s0, dv);
+    load_chunk(s0, 0, x);
+#pragma unroll
+    for (int si = 0; si < SPW; ++si) {
+        const uint32_t sample = s0 + si;
+        if (sample >= B) break;  // wave-uniform
+        const uint32_t next = min(sample + 1, B - 1);
+        floatx4 acc[NBLK];
+#pragma unroll
+        for (int k = 0; k < NBLK; ++k) acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        float dn[DPL];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float xn[NB][PL];
+            if (c + 1 < NCH) load_chunk(sample, c + 1, xn);
+            else if (si + 1 < SPW) {
+                load_dense(next, dn);
+                load_chunk(next, 0, xn);
+            }
+#pragma unroll
+            for (int s = 0; s < PL; ++s) {
+                int k = 0;
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+#pragma unroll
+                    for (int J = I; J < NB; ++J, ++k)
+                        acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[I][s], x[J][s], acc[k], 0, 0, 0);
+            }
+            if (c + 1 < NCH || si + 1 < SPW) {
+#pragma unroll
+                for (int R = 0; R < NB; ++R)
+#pragma unroll
+                    for (int v = 0; v < PL; ++v) x[R][v] = xn[R][v];
+            }
+        }
+        float *orow = out + static_cast<uint64_t>(sample) * (P + D);
+        int k = 0;
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+            for (int J = I; J < NB; ++J, ++k)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int gi = I * 16 + q * 4 + v, gj = J * 16 + r16;
+                    if (gi < gj && gj < N) orow[triu_pos(gi, gj, N)] = acc[k][v];
+                }
+#pragma unroll
+        for (int s = 0; s < DPL; ++s)
+            if (lane + s * kWave < D) orow[P + lane + s * kWave] = dv[s];
+        if (si + 1 < SPW) {
+#pragma unroll
+            for (int s = 0; s < DPL; ++s) dv[s] = dn[s];
+        }
+    }
 }
 
 // Any D % 4 == 0: one block per sample, one thread per pair, fp32 FMA chain over d.
@@ -280,6 +379,14 @@ void launch_fwd_ksplit(const float *dense, const float *pooled, float *out, uint
     }
 }
 
+template <int NB, int SPW>
+void launch_fwd_pipe(const float *dense, const float *pooled, float *out, uint32_t B, int N, int P,
+                     hipStream_t stream) {
+    const uint32_t waves = (B + SPW - 1) / SPW;
+    DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma_pipe<NB, 32, 4, SPW>), dim3((waves + 3) / 4), dim3(256), 0,
+                stream, dense, pooled, out, B, N, P);
+}
+
 template <int NB>
 bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32_t B, int N, int D,
                      int P, hipStream_t stream) {
@@ -289,9 +396,19 @@ bool launch_fwd_mfma(const float *dense, const float *pooled, float *out, uint32
         case 16: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 16, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 32: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 1, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 64: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 2, (NB <= 4 ? 2 : 1)>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
-        // one chunk's operands at a time (16 registers): more waves per SIMD, which beat loading the
-        // whole row at once (55 against 60 us for 16384 samples at N = 27)
-        case 128: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 4, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
+        case 128:
+            if constexpr (NB <= 2) {
+                // samples per wavefront by batch size: enough waves to fill the chip first, then
+                // longer chains of overlapped samples (16384 samples at N = 27: 55.7 us one per
+                // wave, 52.1 two, 50.8 four; 4099 samples: 18.6 / 17.3 / 20.0 us)
+                if (B >= 12288) launch_fwd_pipe<NB, 4>(dense, pooled, out, B, N, P, stream);
+                else if (B >= 3072) launch_fwd_pipe<NB, 2>(dense, pooled, out, B, N, P, stream);
+                else launch_fwd_pipe<NB, 1>(dense, pooled, out, B, N, P, stream);
+                return true;
+            }
+            // one chunk's operands at a time (16 registers): more waves per SIMD, which beat
+            // loading the whole row at once
+            DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 4, 1>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 256: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 8, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         case 512: DLRM_LAUNCH("interact_fwd_mfma", (k_interact_fwd_mfma<NB, 32, 16, (NB <= 2 ? 4 : (NB <= 4 ? 2 : 1))>), grid, block, 0, stream, dense, pooled, out, B, N, P); return true;
         default: return false;

@@ -160,6 +160,26 @@ def test_interact_fwd_random(N, D):
     assert np.array_equal(got[:, P:], dense)
 
 
+# D = 128 with N <= 32 takes 1, 2 or 4 samples per wavefront by batch size (thresholds 3072 and
+# 12288): each choice, with batches that leave the last wavefront short
+@pytest.mark.parametrize("B", [3071, 3072, 4099, 12287, 12289, 16387])
+@pytest.mark.parametrize("N", [17, 27, 32])
+def test_interact_fwd_samples_per_wave(B, N):
+    rng = np.random.default_rng(B * 100 + N)
+    D = 128
+    dense = rng.standard_normal((B, D)).astype(np.float32)
+    pooled = rng.standard_normal((B, N - 1, D)).astype(np.float32)
+    say(f"[interact_fwd] B={B} N={N} D={D}")
+    out = dlrm_interact_fwd(to_dev(dense), to_dev(pooled))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref, scale = oracle.interact_fwd(dense, pooled)
+    err = rel_err(got, ref, scale)
+    say(f"   max rel err {err:.3e}")
+    assert err <= 1e-5
+    assert np.array_equal(got[:, N * (N - 1) // 2:], dense)
+
+
 @pytest.mark.parametrize("N", [1, 2, 4, 9, 16, 27, 33, 65])
 @pytest.mark.parametrize("D", [4, 16, 32, 64, 128, 256, 512])
 def test_interact_bwd_random(N, D):
