@@ -305,3 +305,20 @@ def test_dense_layer_calls_reject(L):
     assert L.dlrm_cast_rows(FAKE, 0, 16, 4, 17, FAKE, 1, 16, None) == INVALID   # cols > dst_cols
     assert L.dlrm_cast_rows(FAKE, 0, 8, 4, 13, FAKE, 1, 16, None) == INVALID    # cols > src_ld
     assert L.dlrm_cast_rows(FAKE, 3, 16, 4, 13, FAKE, 1, 16, None) == INVALID
+
+
+def test_size_limits_rejected(L):
+    """Positions and bags are 32-bit on the device: nnz >= 2^31 or T*B >= 2^31 is refused on the
+    host by every entry point that takes a batch, before any workspace or device access."""
+    big = 1 << 31
+    assert fwd(L, nnz=big) == UNSUPPORTED
+    assert fwd(L, B=big // 2, T=2, tables=ptrs(FAKE, FAKE), rows=i64s(1, 1)) == UNSUPPORTED
+    assert fused(L, nnz=big) == UNSUPPORTED
+    rows = [10]
+    for n, B in ((big, 4), (4, big)):
+        assert L.emb_bag_bwd_update(ptrs(FAKE), ptrs(FAKE), i64s(*rows), 1, 16, 0, FAKE, FAKE, 0, None, B, n, FAKE,
+                                    0, 0.01, 1e-8, FAKE, 1, None, None, None, None, 0, None) == UNSUPPORTED
+        assert L.emb_bag_bwd_plan(i64s(*rows), 1, 16, FAKE, FAKE, 0, None, B, n, FAKE, 1, None, None, None, None,
+                                  0, None) == UNSUPPORTED
+        assert L.emb_bag_bwd_apply(ptrs(FAKE), ptrs(FAKE), i64s(*rows), 1, 16, 0, B, n, 0, FAKE, 0, 0.01, 1e-8,
+                                   FAKE, 1, None, None) == UNSUPPORTED
