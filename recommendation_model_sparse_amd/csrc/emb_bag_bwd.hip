@@ -1235,10 +1235,12 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
     return launch_status();
 }
 
-extern "C" int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
-                                 int32_t D, int32_t dtype, int64_t B, int64_t nnz, int32_t weighted,
-                                 const float *grad_pooled, int32_t optimizer, float lr, float eps, void *workspace,
-                                 size_t workspace_bytes, const int64_t *segment_offsets, dlrm_stream_t stream_) {
+// The update from a planned workspace.  `clear_worklist`: empty the finisher's worklist first
+// (not needed right after a plan on the same stream, which leaves it empty).
+static int apply_impl(void *const *tables, float *const *state, const int64_t *rows, int32_t T, int32_t D,
+                      int32_t dtype, int64_t B, int64_t nnz, int32_t weighted, const float *grad_pooled,
+                      int32_t optimizer, float lr, float eps, void *workspace, size_t workspace_bytes,
+                      const int64_t *segment_offsets, dlrm_stream_t stream_, bool clear_worklist) {
     using namespace dlrm;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     if (optimizer != DLRM_OPT_ADAGRAD && optimizer != DLRM_OPT_SGD) return DLRM_ERR_INVALID_ARG;
@@ -1266,7 +1268,7 @@ extern "C" int emb_bag_bwd_apply(void *const *tables, float *const *state, const
     auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
 
     // the finisher worklist of this update starts empty (so a plan may be applied more than once)
-    DLRM_LAUNCH("zero_u32", k_zero_u32, dim3(1), dim3(1), 0, stream, u32(L.fin_count));
+    if (clear_worklist) DLRM_LAUNCH("zero_u32", k_zero_u32, dim3(1), dim3(1), 0, stream, u32(L.fin_count));
     AdagradArgs a{};
     uint64_t acc_rows = 0;
     for (int t = 0; t < T; ++t) {
@@ -1304,6 +1306,14 @@ extern "C" int emb_bag_bwd_apply(void *const *tables, float *const *state, const
     return launch_status();
 }
 
+extern "C" int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
+                                 int32_t D, int32_t dtype, int64_t B, int64_t nnz, int32_t weighted,
+                                 const float *grad_pooled, int32_t optimizer, float lr, float eps, void *workspace,
+                                 size_t workspace_bytes, const int64_t *segment_offsets, dlrm_stream_t stream) {
+    return apply_impl(tables, state, rows, T, D, dtype, B, nnz, weighted, grad_pooled, optimizer, lr, eps, workspace,
+                      workspace_bytes, segment_offsets, stream, true);
+}
+
 extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, const int64_t *rows,
                                   int32_t T, int32_t D, int32_t dtype, const void *indices,
                                   const void *offsets, int32_t index_type,
@@ -1330,9 +1340,8 @@ extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, cons
                           workspace_bytes, unique_keys_out, segment_offsets_out, sorted_pos_out, num_unique_out,
                           flags, stream);
     if (rc != DLRM_OK) return rc;
-    return emb_bag_bwd_apply(tables, state, rows, T, D, dtype, B, nnz, per_sample_weights != nullptr ? 1 : 0,
-                             grad_pooled, optimizer, lr, eps, workspace, workspace_bytes, segment_offsets_out,
-                             stream);
+    return apply_impl(tables, state, rows, T, D, dtype, B, nnz, per_sample_weights != nullptr ? 1 : 0, grad_pooled,
+                      optimizer, lr, eps, workspace, workspace_bytes, segment_offsets_out, stream, false);
 }
 
 extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows,
