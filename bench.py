@@ -121,15 +121,25 @@ def time_inference(tabs, batches, steps, pooled, inter):
     return res
 
 
-def time_variants(tabs, batches, steps, ws, outs, gpooled, wl):
+def time_variants(tabs, states, batches, steps, ws, outs, gpooled, wl):
     """Mean ms (HIP events) of the path variants on the same batches: bf16 pooled output, int32
-    indices and offsets, and the SGD backward (updates the tables in place)."""
+    indices and offsets, the SGD backward (updates the tables in place), and the weighted lookup
+    and Adagrad backward with per-sample weights U(0,1) (seeded, one array per batch)."""
     import torch
-    from recommendation_model_sparse_amd import DLRM_OPT_SGD, emb_bag_bwd_update, emb_bag_fwd_ex
+    from recommendation_model_sparse_amd import (DLRM_OPT_SGD, emb_bag_bwd_adagrad, emb_bag_bwd_update,
+                                                 emb_bag_fwd, emb_bag_fwd_ex)
 
+    dev = tabs[0].device
     b32 = [dict(idx=b["idx"].to(torch.int32), off=b["off"].to(torch.int32)) for b in batches]
-    pooled_bf16 = torch.empty((wl.B, wl.T, wl.D), dtype=torch.bfloat16, device=tabs[0].device)
+    pooled_bf16 = torch.empty((wl.B, wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    wts = [torch.rand(b["idx"].numel(), generator=gen, device=dev) for b in batches]
     runs = {
+        "fwd_weighted": lambda i: emb_bag_fwd(tabs, batches[i]["idx"], batches[i]["off"], wts[i], out=pooled),
+        "bwd_adagrad_weighted": lambda i: emb_bag_bwd_adagrad(tabs, states, batches[i]["idx"], batches[i]["off"],
+                                                              wts[i], gpooled, wl.lr, wl.eps, workspace=ws,
+                                                              outputs=outs),
         "fwd_bf16_out": lambda i: emb_bag_fwd_ex(tabs, batches[i]["idx"], batches[i]["off"], None, out=pooled_bf16,
                                                  out_dtype=torch.bfloat16),
         "fwd_int32_indices": lambda i: emb_bag_fwd_ex(tabs, b32[i]["idx"], b32[i]["off"], None),
@@ -435,7 +445,7 @@ def main():
 
     # inference: the fused lookup + interaction against the two calls, same batches and tables
     inf = time_inference(tabs, batches, args.steps, pooled, inter)
-    variants = time_variants(tabs, batches, args.steps, ws, outs, gpooled, wl)
+    variants = time_variants(tabs, states, batches, args.steps, ws, outs, gpooled, wl)
     full = time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz)
 
     hbm = hbm_context(dev)

@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
     const IT *offsets = static_cast<const IT *>(a.offsets);
     constexpr int NG = kWave / G;
     constexpr int EPC = Elem<DT>::kPerChunk;
-    constexpr int U = 8;
+    // rows per lane group in flight: with weights, 8 took 73 registers (6 waves per SIMD) and
+    // 4 keeps 8 waves (weighted multi-hot lookup 309 -> 278 us); without, 4, 6 and 8 measure alike
+    constexpr int U = WEIGHTED ? 4 : 8;
     const uint32_t lb = xcd_contiguous(blockIdx.x, a.nblocks);
     const uint32_t bag0 = (lb * 4 + wave_id()) * kPoolBagsPerWave;
     const int lane = threadIdx.x & 63;
@@ -69,18 +71,20 @@ __global__ __launch_bounds__(256) void k_pool_wave_per_bag(PoolArgs a) {
             if constexpr (WEIGHTED) my_w = lane < n ? a.weights[base + lane] : 0.f;
             for (int r0 = 0; r0 < n; r0 += NG * U) {
                 uint4 v[U];
-                float w[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int r = r0 + u * NG + grp;
-                    const int src = r < n ? r : 0;
-                    const int64_t idx = __shfl(my_idx, src);
-                    w[u] = WEIGHTED ? __shfl(my_w, src) : 1.f;
+                    const int64_t idx = __shfl(my_idx, r < n ? r : 0);
                     v[u] = r < n ? load_row_chunk(tab, idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
                 }
+                // the weights are fetched from their lanes only now, while the rows are in flight
+                if constexpr (WEIGHTED) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (r0 + u * NG + grp < n) accumulate<DT, WEIGHTED>(acc, v[u], w[u]);
+                for (int u = 0; u < U; ++u) {
+                    const int r = r0 + u * NG + grp;
+                    const float w = WEIGHTED ? __shfl(my_w, r < n ? r : 0) : 1.f;
+                    if (r < n) accumulate<DT, WEIGHTED>(acc, v[u], w);
+                }
             }
         }
         // combine the NG group partials (fixed butterfly: every group ends with identical bits)
