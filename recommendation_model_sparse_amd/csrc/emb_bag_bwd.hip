@@ -742,9 +742,17 @@ struct PosMeta {
     float s_old;            // the accumulator's value before the update (Adagrad)
 };
 
+// Waves per SIMD asked of the compiler for K7: 5 for unweighted bf16 rows at D = 128, which then
+// fits in 95 registers without spilling (97, and 4 waves, otherwise: 502 against 495 us on the
+// multi-hot workload); the other shapes would spill under that limit, and keep the default.
+constexpr int k7_min_waves(int DT, int W, int G, bool weighted) {
+    return DT == DLRM_BF16 && W == 4 && G == 32 && !weighted ? 5 : 1;
+}
+
 // Chunk of CS = G*MP sorted positions per lane group of G lanes; U gradient rows in flight.
 template <int DT, int W, int G, int MP, bool WEIGHTED, int U, int OPT>
-__global__ __launch_bounds__(256) void k_seg_reduce_adagrad(AdagradArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_seg_reduce_adagrad(AdagradArgs a) {
     using TW = TabWords<DT, W>;
     constexpr int NG = kWave / G;
     constexpr int CS = G * MP;
