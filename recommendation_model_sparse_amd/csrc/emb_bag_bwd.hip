@@ -480,36 +480,28 @@ __global__ __launch_bounds__(256) void k_seg_count(const uint32_t *__restrict__ 
     if (threadIdx.x == 0) bcount[blockIdx.x] = tot;
 }
 
-// One block: exclusive scan of the per-tile segment counts; U and the closing offset.
-__global__ __launch_bounds__(256) void k_seg_scan(uint32_t *__restrict__ bcount, uint32_t nblk,
-                                                  uint32_t n, int64_t *__restrict__ num_unique,
-                                                  int64_t *__restrict__ seg_offsets,
-                                                  uint32_t *__restrict__ fin_count) {
-    const uint32_t per = (nblk + 255) / 256;
-    const uint32_t b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
-    uint32_t tot;
-    const uint32_t run = block_exclusive_scan(range_sum<16>(bcount, b0, b1), &tot);
-    range_exclusive<16>(bcount, b0, b1, run);
-    if (threadIdx.x == 0) {
-        if (num_unique) *num_unique = tot;
-        seg_offsets[tot] = n;
-        *fin_count = 0;  // the finisher worklist of this call starts empty
-    }
-}
-
 // Writes segment offsets (and unique keys when asked), and for every chunk of CS sorted
 // positions the segment index of the chunk's last position.
+// The tile's first segment index is the sum of the earlier tiles' counts, which each block adds
+// up itself (at most a few thousand counts, read from L2); the last tile also writes U, the
+// closing offset, and empties the finisher's worklist.
 __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ keys, uint32_t n,
-                                                   const uint32_t *__restrict__ bbase,
+                                                   const uint32_t *__restrict__ bcount, uint32_t nblk,
                                                    int64_t *__restrict__ unique_keys,
                                                    int64_t *__restrict__ seg_offsets,
-                                                   uint32_t *__restrict__ chunk_seg, uint32_t CS) {
+                                                   uint32_t *__restrict__ chunk_seg, uint32_t CS,
+                                                   int64_t *__restrict__ num_unique,
+                                                   uint32_t *__restrict__ fin_count) {
     __shared__ uint32_t wtot[4];
     const int tid = threadIdx.x, w = static_cast<int>(wave_id()), lane = tid & 63;
     const uint32_t base = blockIdx.x * kSortTile + w * (kSortTile / 4) + lane;
     bool flags[kSortItems];
     uint32_t kv[kSortItems];
     seg_flags(keys, base, kWave, n, flags, kv);
+    const uint32_t per = (blockIdx.x + 255) / 256;
+    const uint32_t c0 = tid * per, c1 = min(blockIdx.x, c0 + per);
+    uint32_t first;  // segments that start in earlier tiles
+    block_exclusive_scan(range_sum<16>(bcount, c0, c1), &first);
     uint64_t masks[kSortItems];
     uint32_t wsum = 0;
 #pragma unroll
@@ -519,8 +511,14 @@ __global__ __launch_bounds__(256) void k_seg_write(const uint32_t *__restrict__ 
     }
     if (lane == 0) wtot[w] = wsum;
     __syncthreads();
-    uint32_t run = bbase[blockIdx.x];
+    uint32_t run = first;
     for (int k = 0; k < w; ++k) run += wtot[k];
+    if (blockIdx.x + 1 == nblk && tid == 0) {
+        const uint32_t total = first + wtot[0] + wtot[1] + wtot[2] + wtot[3];
+        if (num_unique) *num_unique = total;
+        seg_offsets[total] = n;
+        *fin_count = 0;  // the finisher worklist of this call starts empty
+    }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
@@ -1236,10 +1234,9 @@ extern "C" int emb_bag_bwd_plan(const int64_t *rows, int32_t T, int32_t D, const
     uint32_t *seg_count = u32(L.seg_count);
     int64_t *seg_offsets = segment_offsets_out ? segment_offsets_out : reinterpret_cast<int64_t *>(ws + L.seg_offsets);
     DLRM_LAUNCH("seg_count", k_seg_count, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count);
-    DLRM_LAUNCH("seg_scan", k_seg_scan, dim3(1), dim3(256), 0, stream, seg_count, L.nblk, n, num_unique_out,
-                seg_offsets, u32(L.fin_count));
-    DLRM_LAUNCH("seg_write", k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count, unique_keys_out,
-                seg_offsets, u32(L.chunk_seg), static_cast<uint32_t>(L.CS));
+    DLRM_LAUNCH("seg_write", k_seg_write, dim3(L.nblk), dim3(256), 0, stream, skeys, n, seg_count, L.nblk,
+                unique_keys_out, seg_offsets, u32(L.chunk_seg), static_cast<uint32_t>(L.CS), num_unique_out,
+                u32(L.fin_count));
     return launch_status();
 }
 
