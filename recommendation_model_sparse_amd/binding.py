@@ -98,42 +98,115 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ---------------------------------------------------------------- argument checks
+#
+# The C entry points see plain pointers and sizes, so they cannot tell a CPU tensor, a wrong-sized
+# output or a buffer of the wrong type from a good one; a kernel would read or write out of bounds.
+# Every wrapper therefore checks each tensor (type, dtype, exact shape, contiguity, one CUDA device,
+# workspace and output sizes) and raises ValueError before it calls the library.
+
+def _need(t, name: str, dtype=None, shape=None, min_numel: Optional[int] = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None:
+        ok = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in ok:
+            raise ValueError(f"{name} must be {' or '.join(str(d) for d in ok)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name: str, dtype=None, shape=None, min_numel: Optional[int] = None):
+    return None if t is None else _need(t, name, dtype, shape, min_numel)
+
+
+def _device(*tensors) -> torch.device:
+    """The one CUDA device every given tensor (None entries skipped) lives on."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a CUDA (HIP) device, got {dev}")
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"all tensors must be on {dev}, found one on {t.device}")
+    return dev
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DLRM_F32
     if t.dtype == torch.bfloat16:
         return DLRM_BF16
-    raise TypeError(f"table dtype {t.dtype} is not float32 or bfloat16")
+    raise ValueError(f"table dtype {t.dtype} is not float32 or bfloat16")
 
 
 def _tables(tables: Sequence[torch.Tensor]):
     T = len(tables)
     if T == 0:
         raise ValueError("no tables")
+    for t in tables:
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("tables must be 2-D tensors [V_t, D]")
     D = tables[0].shape[1]
     code = _dtype_code(tables[0])
     for t in tables:
-        if t.dim() != 2 or t.shape[1] != D or _dtype_code(t) != code or not t.is_contiguous():
+        if t.shape[1] != D or _dtype_code(t) != code or not t.is_contiguous():
             raise ValueError("tables must be contiguous [V_t, D] of one dtype")
     ptrs = (ctypes.c_void_p * T)(*[t.data_ptr() for t in tables])
     rows = (ctypes.c_int64 * T)(*[t.shape[0] for t in tables])
     return T, D, code, ptrs, rows
 
 
-def _index_code(indices: torch.Tensor, offsets: torch.Tensor) -> int:
-    if indices.dtype != offsets.dtype or indices.dtype not in (torch.int64, torch.int32):
-        raise ValueError("indices and offsets must both be int64 or both int32")
-    if not (indices.is_contiguous() and offsets.is_contiguous()):
-        raise ValueError("indices and offsets must be contiguous")
-    return DLRM_INDEX_I32 if indices.dtype == torch.int32 else DLRM_INDEX_I64
-
-
-def _contig(t: Optional[torch.Tensor], dtype, name):
-    if t is None:
+def _states(state, tables, required: bool):
+    if state is None:
+        if required:
+            raise ValueError("row-wise Adagrad needs one state vector per table")
         return None
-    if t.dtype != dtype or not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous {dtype}")
-    return t
+    if len(state) != len(tables):
+        raise ValueError("one state vector per table")
+    for i, (st, t) in enumerate(zip(state, tables)):
+        _need(st, f"state[{i}]", torch.float32, (t.shape[0],))
+    return (ctypes.c_void_p * len(state))(*[st.data_ptr() for st in state])
+
+
+def _batch(T: int, indices, offsets, per_sample_weights, index_dtypes=(torch.int64,)):
+    """Checks the CSR batch; returns (indices, offsets, weights, index code, B, nnz)."""
+    _need(indices, "indices", index_dtypes)
+    _need(offsets, "offsets", indices.dtype)
+    if indices.dim() != 1 or offsets.dim() != 1:
+        raise ValueError("indices and offsets must be 1-D")
+    B = (offsets.numel() - 1) // T
+    if offsets.numel() < 1 or offsets.numel() != T * B + 1:
+        raise ValueError(f"offsets must have T*B+1 entries (T={T}), got {offsets.numel()}")
+    nnz = indices.numel()
+    w = _opt(per_sample_weights, "per_sample_weights", torch.float32, (nnz,))
+    code = DLRM_INDEX_I32 if indices.dtype == torch.int32 else DLRM_INDEX_I64
+    return indices, offsets, w, code, B, nnz
+
+
+def _outputs(o, nnz: int):
+    """The optional integer outputs of the embedding backward, each sized for nnz lookups."""
+    if o is None:
+        return None
+    _need(o.unique_keys, "outputs.unique_keys", torch.int64, min_numel=nnz)
+    _need(o.segment_offsets, "outputs.segment_offsets", torch.int64, min_numel=nnz + 1)
+    _need(o.sorted_pos, "outputs.sorted_pos", torch.int32, min_numel=nnz)
+    _need(o.num_unique, "outputs.num_unique", torch.int64, min_numel=1)
+    return o
+
+
+def _workspace(workspace, need: int, dev):
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    return workspace
 
 
 def emb_bag_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: torch.Tensor,
@@ -141,17 +214,13 @@ def emb_bag_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: 
                 out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
     """Pooled embeddings [B, T, D] fp32 (C: emb_bag_fwd)."""
     T, D, code, ptrs, rows = _tables(tables)
-    indices = _contig(indices, torch.int64, "indices")
-    offsets = _contig(offsets, torch.int64, "offsets")
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    B = (offsets.numel() - 1) // T
-    if offsets.numel() != T * B + 1:
-        raise ValueError("offsets must have T*B+1 entries")
-    dev = tables[0].device
+    indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
+    out = _opt(out, "out", torch.float32, (B, T, D))
+    dev = _device(*tables, indices, offsets, w, out)
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     _check(lib().emb_bag_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
-                             indices.numel(), _ptr(out), flags, _stream(dev)), "emb_bag_fwd")
+                             nnz, _ptr(out), flags, _stream(dev)), "emb_bag_fwd")
     return out
 
 
@@ -161,34 +230,42 @@ def emb_bag_fwd_ex(tables: Sequence[torch.Tensor], indices: torch.Tensor, offset
     """Pooled embeddings [B, T, D] in out_dtype (fp32 or bf16), int64 or int32 indices and
     offsets (C: emb_bag_fwd_ex)."""
     T, D, code, ptrs, rows = _tables(tables)
-    icode = _index_code(indices, offsets)
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    ocode = {torch.float32: DLRM_F32, torch.bfloat16: DLRM_BF16}[out_dtype]
-    B = (offsets.numel() - 1) // T
-    if offsets.numel() != T * B + 1:
-        raise ValueError("offsets must have T*B+1 entries")
-    dev = tables[0].device
+    indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
+                                                (torch.int64, torch.int32))
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    ocode = DLRM_F32 if out_dtype == torch.float32 else DLRM_BF16
+    out = _opt(out, "out", out_dtype, (B, T, D))
+    dev = _device(*tables, indices, offsets, w, out)
     if out is None:
         out = torch.empty((B, T, D), dtype=out_dtype, device=dev)
-    if out.dtype != out_dtype or not out.is_contiguous():
-        raise ValueError("out must be contiguous of out_dtype")
     _check(lib().emb_bag_fwd_ex(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B,
-                                indices.numel(), _ptr(out), ocode, flags, _stream(dev)), "emb_bag_fwd_ex")
+                                nnz, _ptr(out), ocode, flags, _stream(dev)), "emb_bag_fwd_ex")
     return out
+
+
+def _interaction_shapes(dense: torch.Tensor, pooled: torch.Tensor):
+    _need(dense, "dense", torch.float32)
+    _need(pooled, "pooled", torch.float32)
+    if dense.dim() != 2 or pooled.dim() != 3:
+        raise ValueError("dense must be [B, D] and pooled [B, N-1, D]")
+    B, D = dense.shape
+    if pooled.shape[0] != B or pooled.shape[2] != D:
+        raise ValueError(f"pooled must be [B={B}, N-1, D={D}], got {tuple(pooled.shape)}")
+    N = pooled.shape[1] + 1
+    return B, N, D, N * (N - 1) // 2
 
 
 def dlrm_interact_fwd(dense: torch.Tensor, pooled: torch.Tensor,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """[B, N(N-1)/2 + D] fp32 (C: dlrm_interact_fwd); pooled is [B, N-1, D]."""
-    dense = _contig(dense, torch.float32, "dense")
-    pooled = _contig(pooled, torch.float32, "pooled")
-    B, D = dense.shape
-    N = pooled.shape[1] + 1
-    P = N * (N - 1) // 2
+    B, N, D, P = _interaction_shapes(dense, pooled)
+    out = _opt(out, "out", torch.float32, (B, P + D))
+    dev = _device(dense, pooled, out)
     if out is None:
-        out = torch.empty((B, P + D), dtype=torch.float32, device=dense.device)
+        out = torch.empty((B, P + D), dtype=torch.float32, device=dev)
     _check(lib().dlrm_interact_fwd(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out),
-                                   _stream(dense.device)), "dlrm_interact_fwd")
+                                   _stream(dev)), "dlrm_interact_fwd")
     return out
 
 
@@ -197,19 +274,15 @@ def emb_bag_interact_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, 
                          out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
     """[B, N(N-1)/2 + D] fp32, N = T + 1: lookup fused with the interaction (C: emb_bag_interact_fwd)."""
     T, D, code, ptrs, rows = _tables(tables)
-    indices = _contig(indices, torch.int64, "indices")
-    offsets = _contig(offsets, torch.int64, "offsets")
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    dense = _contig(dense, torch.float32, "dense")
-    B = (offsets.numel() - 1) // T
-    if offsets.numel() != T * B + 1 or tuple(dense.shape) != (B, D):
-        raise ValueError("offsets must have T*B+1 entries and dense must be [B, D]")
+    indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
+    _need(dense, "dense", torch.float32, (B, D))
     N = T + 1
-    dev = tables[0].device
+    out = _opt(out, "out", torch.float32, (B, N * (N - 1) // 2 + D))
+    dev = _device(*tables, indices, offsets, w, dense, out)
     if out is None:
         out = torch.empty((B, N * (N - 1) // 2 + D), dtype=torch.float32, device=dev)
     _check(lib().emb_bag_interact_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
-                                      indices.numel(), _ptr(dense), _ptr(out), flags, _stream(dev)),
+                                      nnz, _ptr(dense), _ptr(out), flags, _stream(dev)),
            "emb_bag_interact_fwd")
     return out
 
@@ -218,17 +291,17 @@ def dlrm_interact_bwd(grad_out: torch.Tensor, dense: torch.Tensor, pooled: torch
                       grad_dense: Optional[torch.Tensor] = None,
                       grad_pooled: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(grad_dense [B, D], grad_pooled [B, N-1, D]) (C: dlrm_interact_bwd)."""
-    grad_out = _contig(grad_out, torch.float32, "grad_out")
-    dense = _contig(dense, torch.float32, "dense")
-    pooled = _contig(pooled, torch.float32, "pooled")
-    B, D = dense.shape
-    N = pooled.shape[1] + 1
+    B, N, D, P = _interaction_shapes(dense, pooled)
+    _need(grad_out, "grad_out", torch.float32, (B, P + D))
+    grad_dense = _opt(grad_dense, "grad_dense", torch.float32, (B, D))
+    grad_pooled = _opt(grad_pooled, "grad_pooled", torch.float32, (B, N - 1, D))
+    dev = _device(grad_out, dense, pooled, grad_dense, grad_pooled)
     if grad_dense is None:
         grad_dense = torch.empty_like(dense)
     if grad_pooled is None:
         grad_pooled = torch.empty_like(pooled)
     _check(lib().dlrm_interact_bwd(_ptr(grad_out), _ptr(dense), _ptr(pooled), B, N, D,
-                                   _ptr(grad_dense), _ptr(grad_pooled), _stream(dense.device)),
+                                   _ptr(grad_dense), _ptr(grad_pooled), _stream(dev)),
            "dlrm_interact_bwd")
     return grad_dense, grad_pooled
 
@@ -250,6 +323,16 @@ class AdagradOutputs:
         self.num_unique = torch.empty(1, dtype=torch.int64, device=device)
 
 
+def _out_ptrs(o):
+    if o is None:
+        return None, None, None, None
+    return _ptr(o.unique_keys), _ptr(o.segment_offsets), _ptr(o.sorted_pos), _ptr(o.num_unique)
+
+
+def _out_tensors(o):
+    return () if o is None else (o.unique_keys, o.segment_offsets, o.sorted_pos, o.num_unique)
+
+
 def emb_bag_bwd_adagrad(tables: Sequence[torch.Tensor], state: Sequence[torch.Tensor],
                         indices: torch.Tensor, offsets: torch.Tensor,
                         per_sample_weights: Optional[torch.Tensor], grad_pooled: torch.Tensor,
@@ -257,28 +340,17 @@ def emb_bag_bwd_adagrad(tables: Sequence[torch.Tensor], state: Sequence[torch.Te
                         outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
     """Row-wise Adagrad on the tables and states, in place (C: emb_bag_bwd_adagrad)."""
     T, D, code, ptrs, rows = _tables(tables)
-    if len(state) != T:
-        raise ValueError("one state vector per table")
-    for s, t in zip(state, tables):
-        if s.dtype != torch.float32 or s.numel() != t.shape[0] or not s.is_contiguous():
-            raise ValueError("state[t] must be contiguous fp32 [V_t]")
-    sptrs = (ctypes.c_void_p * T)(*[s.data_ptr() for s in state])
-    indices = _contig(indices, torch.int64, "indices")
-    offsets = _contig(offsets, torch.int64, "offsets")
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
-    B = (offsets.numel() - 1) // T
-    nnz = indices.numel()
-    dev = tables[0].device
+    sptrs = _states(state, tables, True)
+    indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
+    _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
+    o = _outputs(outputs, nnz)
     need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    o = outputs
+    workspace = _opt(workspace, "workspace", torch.uint8, min_numel=need)
+    dev = _device(*tables, *state, indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
+    workspace = _workspace(workspace, need, dev)
     _check(lib().emb_bag_bwd_adagrad(
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B, nnz,
-        _ptr(grad_pooled), float(lr), float(eps), _ptr(workspace), workspace.numel(),
-        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
-        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
+        _ptr(grad_pooled), float(lr), float(eps), _ptr(workspace), workspace.numel(), *_out_ptrs(o), flags,
         _stream(dev)), "emb_bag_bwd_adagrad")
     return o
 
@@ -292,30 +364,19 @@ def emb_bag_bwd_update(tables: Sequence[torch.Tensor], state: Optional[Sequence[
     """Embedding backward with DLRM_OPT_ADAGRAD (state required) or DLRM_OPT_SGD (state may be
     None), int64 or int32 indices and offsets (C: emb_bag_bwd_update)."""
     T, D, code, ptrs, rows = _tables(tables)
-    icode = _index_code(indices, offsets)
-    sptrs = None
-    if state is not None:
-        if len(state) != T:
-            raise ValueError("one state vector per table")
-        for st, t in zip(state, tables):
-            if st.dtype != torch.float32 or st.numel() != t.shape[0] or not st.is_contiguous():
-                raise ValueError("state[t] must be contiguous fp32 [V_t]")
-        sptrs = (ctypes.c_void_p * T)(*[st.data_ptr() for st in state])
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
-    B = (offsets.numel() - 1) // T
-    nnz = indices.numel()
-    dev = tables[0].device
+    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
+                                                (torch.int64, torch.int32))
+    _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
+    o = _outputs(outputs, nnz)
     need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    o = outputs
+    workspace = _opt(workspace, "workspace", torch.uint8, min_numel=need)
+    dev = _device(*tables, *(state or ()), indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
+    workspace = _workspace(workspace, need, dev)
     _check(lib().emb_bag_bwd_update(
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
         _ptr(grad_pooled), int(optimizer), float(lr), float(eps), _ptr(workspace), workspace.numel(),
-        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
-        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
-        _stream(dev)), "emb_bag_bwd_update")
+        *_out_ptrs(o), flags, _stream(dev)), "emb_bag_bwd_update")
     return o
 
 
@@ -326,16 +387,14 @@ def emb_bag_bwd_plan(rows: Sequence[int], D: int, indices: torch.Tensor, offsets
     of the indices' device; `rows` are the tables' row counts."""
     T = len(rows)
     r = (ctypes.c_int64 * T)(*rows)
-    icode = _index_code(indices, offsets)
-    w = _contig(per_sample_weights, torch.float32, "per_sample_weights")
-    B = (offsets.numel() - 1) // T
-    nnz = indices.numel()
-    o = outputs
+    indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
+                                                (torch.int64, torch.int32))
+    o = _outputs(outputs, nnz)
+    _need(workspace, "workspace", torch.uint8, min_numel=emb_bag_bwd_workspace_size(rows, D, B, nnz))
+    dev = _device(indices, offsets, w, workspace, *_out_tensors(o))
     _check(lib().emb_bag_bwd_plan(
         r, T, D, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz, _ptr(workspace), workspace.numel(),
-        _ptr(o.unique_keys) if o else None, _ptr(o.segment_offsets) if o else None,
-        _ptr(o.sorted_pos) if o else None, _ptr(o.num_unique) if o else None, flags,
-        _stream(indices.device)), "emb_bag_bwd_plan")
+        *_out_ptrs(o), flags, _stream(dev)), "emb_bag_bwd_plan")
     return o
 
 
@@ -345,29 +404,30 @@ def emb_bag_bwd_apply(tables: Sequence[torch.Tensor], state: Optional[Sequence[t
     """The update half of the embedding backward from a planned workspace (C: emb_bag_bwd_apply);
     `outputs` is the plan's, when it was given one (its segment offsets are read)."""
     T, D, code, ptrs, rows = _tables(tables)
-    sptrs = None
-    if state is not None:
-        if len(state) != T:
-            raise ValueError("one state vector per table")
-        for st, t in zip(state, tables):
-            if st.dtype != torch.float32 or st.numel() != t.shape[0] or not st.is_contiguous():
-                raise ValueError("state[t] must be contiguous fp32 [V_t]")
-        sptrs = (ctypes.c_void_p * T)(*[st.data_ptr() for st in state])
-    grad_pooled = _contig(grad_pooled, torch.float32, "grad_pooled")
+    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    B, nnz = int(B), int(nnz)
+    _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
+    seg = None
+    if outputs is not None:
+        seg = _need(outputs.segment_offsets, "outputs.segment_offsets", torch.int64, min_numel=nnz + 1)
+    _need(workspace, "workspace", torch.uint8,
+          min_numel=emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz))
+    dev = _device(*tables, *(state or ()), grad_pooled, workspace, seg)
     _check(lib().emb_bag_bwd_apply(
-        ptrs, sptrs, rows, T, D, code, int(B), int(nnz), 1 if weighted else 0, _ptr(grad_pooled), int(optimizer),
-        float(lr), float(eps), _ptr(workspace), workspace.numel(),
-        _ptr(outputs.segment_offsets) if outputs is not None else None, _stream(tables[0].device)),
+        ptrs, sptrs, rows, T, D, code, B, nnz, 1 if weighted else 0, _ptr(grad_pooled), int(optimizer),
+        float(lr), float(eps), _ptr(workspace), workspace.numel(), _ptr(seg), _stream(dev)),
         "emb_bag_bwd_apply")
 
 
 def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) -> None:
     """Fill ``table`` with the counter-hash contents of table ``t`` (input generation)."""
-    if not table.is_contiguous() or table.dim() != 2:
-        raise ValueError("table must be contiguous [V, D]")
+    _need(table, "table", (torch.float32, torch.bfloat16))
+    if table.dim() != 2:
+        raise ValueError("table must be [V, D]")
+    dev = _device(table)
     _check(lib().dlrm_synth_fill_table(_ptr(table), _dtype_code(table), table.shape[0],
                                        table.shape[1], t, seed, float(scale),
-                                       _stream(table.device)), "dlrm_synth_fill_table")
+                                       _stream(dev)), "dlrm_synth_fill_table")
 
 
 # ---------------------------------------------------------------- dense layers (dlrm_mlp.h)
@@ -384,14 +444,20 @@ def dlrm_bce_head_workspace_size(M: int, K: int) -> int:
 
 
 def _ws(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace when it is large enough, else a new one."""
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+        if workspace.device != dev:
+            raise ValueError(f"workspace must be on {dev}, found it on {workspace.device}")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     return workspace
 
 
-def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype != torch.bfloat16 or not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous bf16")
+def _mat(t, name: str, dtype) -> torch.Tensor:
+    _need(t, name, dtype)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a matrix, got shape {tuple(t.shape)}")
     return t
 
 
@@ -399,17 +465,20 @@ def dlrm_linear_fwd(x: torch.Tensor, W: torch.Tensor, b: torch.Tensor, act: int 
                     y: Optional[torch.Tensor] = None, y_dtype: torch.dtype = torch.bfloat16,
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = act(x W^T + b), x [M][K] bf16, W [N][K] bf16, b [N] fp32 (C: dlrm_linear_fwd)."""
-    x, W = _bf16(x, "x"), _bf16(W, "W")
-    b = _contig(b, torch.float32, "b")
-    M, K = x.shape
-    N = W.shape[0]
-    if W.shape[1] != K or b.numel() != N:
-        raise ValueError("shapes do not match")
+    M, K = _mat(x, "x", torch.bfloat16).shape
+    N = _mat(W, "W", torch.bfloat16).shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W must be [N, K={K}], got {tuple(W.shape)}")
+    _need(b, "b", torch.float32, (N,))
+    y = _opt(y, "y", (torch.float32, torch.bfloat16) if y is not None else None, (M, N))
+    dev = _device(x, W, b, y)
     if y is None:
-        y = torch.empty((M, N), dtype=y_dtype, device=x.device)
-    ws = _ws(dlrm_linear_workspace_size(M, N, K), x.device, workspace)
+        if y_dtype not in _TORCH_CODE:
+            raise ValueError(f"y_dtype must be float32 or bfloat16, got {y_dtype}")
+        y = torch.empty((M, N), dtype=y_dtype, device=dev)
+    ws = _ws(dlrm_linear_workspace_size(M, N, K), dev, workspace)
     _check(lib().dlrm_linear_fwd(_ptr(x), _ptr(W), _ptr(b), M, N, K, act, _ptr(y), _TORCH_CODE[y.dtype], _ptr(ws),
-                                 ws.numel(), _stream(x.device)), "dlrm_linear_fwd")
+                                 ws.numel(), _stream(dev)), "dlrm_linear_fwd")
     return y
 
 
@@ -418,11 +487,19 @@ def dlrm_linear_bwd(dy: torch.Tensor, y: Optional[torch.Tensor], act: int, x: to
                     dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None):
     """(dx or None, dW, db) of y = act(x W^T + b) given dy fp32 (C: dlrm_linear_bwd)."""
-    dy = _contig(dy, torch.float32, "dy")
-    x, W = _bf16(x, "x"), _bf16(W, "W")
-    M, K = x.shape
-    N = W.shape[0]
-    dev = x.device
+    M, K = _mat(x, "x", torch.bfloat16).shape
+    N = _mat(W, "W", torch.bfloat16).shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W must be [N, K={K}], got {tuple(W.shape)}")
+    _need(dy, "dy", torch.float32, (M, N))
+    if act == DLRM_ACT_RELU and y is None:
+        raise ValueError("the ReLU backward needs the forward output y")
+    y = _opt(y, "y", (torch.float32, torch.bfloat16), (M, N))
+    dz_bf16 = _opt(dz_bf16, "dz_bf16", torch.bfloat16, (M, N))
+    dx = _opt(dx, "dx", torch.float32, (M, K)) if want_dx else None
+    dW = _opt(dW, "dW", torch.float32, (N, K))
+    db = _opt(db, "db", torch.float32, (N,))
+    dev = _device(dy, y, x, W, dz_bf16, dx, dW, db)
     if dz_bf16 is None:
         dz_bf16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if want_dx and dx is None:
@@ -442,11 +519,14 @@ def dlrm_linear_bwd(dy: torch.Tensor, y: Optional[torch.Tensor], act: int, x: to
 def dlrm_bce_head(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, t: torch.Tensor,
                   workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
     """Sigmoid head + mean BCE, forward and backward: dict p, loss, dx, dw, db (C: dlrm_bce_head)."""
-    x, w = _bf16(x, "x"), _bf16(w, "w")
-    b = _contig(b, torch.float32, "b")
-    t = _contig(t, torch.float32, "t")
-    M, K = x.shape
-    dev = x.device
+    M, K = _mat(x, "x", torch.bfloat16).shape
+    _need(w, "w", torch.bfloat16, (K,))
+    _need(b, "b", torch.float32, (1,))
+    _need(t, "t", torch.float32, (M,))
+    if out is not None:
+        for k, shp in (("p", (M,)), ("loss", (1,)), ("dx", (M, K)), ("dw", (K,)), ("db", (1,))):
+            _need(out[k], f"out[{k!r}]", torch.float32, shp)
+    dev = _device(x, w, b, t, *(out.values() if out is not None else ()))
     o = out if out is not None else {
         "p": torch.empty(M, dtype=torch.float32, device=dev), "loss": torch.empty(1, dtype=torch.float32, device=dev),
         "dx": torch.empty((M, K), dtype=torch.float32, device=dev), "dw": torch.empty(K, dtype=torch.float32, device=dev),
@@ -459,49 +539,54 @@ def dlrm_bce_head(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, t: torch.Te
 
 def dlrm_sgd_dense(w32: torch.Tensor, w16: Optional[torch.Tensor], g: torch.Tensor, lr: float) -> None:
     """w32 -= lr * g; w16 <- bf16(w32) when given (C: dlrm_sgd_dense)."""
-    w32 = _contig(w32, torch.float32, "w32")
-    g = _contig(g, torch.float32, "g")
-    if w16 is not None and (w16.numel() != w32.numel()):
-        raise ValueError("w16 must match w32")
-    if g.numel() != w32.numel():
-        raise ValueError("g must match w32")
-    _check(lib().dlrm_sgd_dense(_ptr(w32), _ptr(w16) if w16 is not None else None, _ptr(g), w32.numel(), float(lr),
-                                _stream(w32.device)), "dlrm_sgd_dense")
+    _need(w32, "w32", torch.float32)
+    _need(g, "g", torch.float32, tuple(w32.shape))
+    w16 = _opt(w16, "w16", torch.bfloat16, tuple(w32.shape))
+    dev = _device(w32, w16, g)
+    _check(lib().dlrm_sgd_dense(_ptr(w32), _ptr(w16), _ptr(g), w32.numel(), float(lr),
+                                _stream(dev)), "dlrm_sgd_dense")
 
 
 def dlrm_sgd_dense_multi(params: Sequence, lr: float) -> None:
     """For each (w32, w16 or None, g): w32 -= lr * g and w16 <- bf16(w32), in one launch
     (C: dlrm_sgd_dense_multi)."""
     count = len(params)
-    w32s, w16s, gs, ns = [], [], [], []
-    for w32, w16, g in params:
-        if w32.dtype != torch.float32 or not w32.is_contiguous():
-            raise ValueError("w32 must be contiguous fp32")
-        if g.dtype != torch.float32 or not g.is_contiguous() or g.numel() != w32.numel():
-            raise ValueError("g must be contiguous fp32 of w32's size")
-        if w16 is not None and (w16.numel() != w32.numel() or not w16.is_contiguous()):
-            raise ValueError("w16 must match w32")
+    if count == 0:
+        return
+    w32s, w16s, gs, ns, every = [], [], [], [], []
+    for i, (w32, w16, g) in enumerate(params):
+        _need(w32, f"params[{i}].w32", torch.float32)
+        _need(g, f"params[{i}].g", torch.float32, tuple(w32.shape))
+        _opt(w16, f"params[{i}].w16", torch.bfloat16, tuple(w32.shape))
+        every += [w32, w16, g]
         w32s.append(w32.data_ptr())
         w16s.append(w16.data_ptr() if w16 is not None else None)
         gs.append(g.data_ptr())
         ns.append(w32.numel())
-    if count == 0:
-        return
+    dev = _device(*every)
     vp = ctypes.c_void_p * count
     _check(lib().dlrm_sgd_dense_multi(count, vp(*w32s), vp(*w16s), vp(*gs), (ctypes.c_int64 * count)(*ns), float(lr),
-                                      _stream(params[0][0].device)), "dlrm_sgd_dense_multi")
+                                      _stream(dev)), "dlrm_sgd_dense_multi")
 
 
 def dlrm_cast_rows(src: torch.Tensor, cols: int, dst_cols: int, dst_dtype: torch.dtype,
                    dst: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dst [M][dst_cols]: the first `cols` columns of src converted, the rest zero (C: dlrm_cast_rows)."""
-    if src.dim() != 2 or src.stride(1) != 1:
+    if not isinstance(src, torch.Tensor) or src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be a 2-D matrix with packed rows")
+    if src.dtype not in _TORCH_CODE:
+        raise ValueError(f"src must be float32 or bfloat16, got {src.dtype}")
+    if not (0 <= cols <= src.shape[1] and cols <= dst_cols):
+        raise ValueError(f"need cols <= src columns ({src.shape[1]}) and cols <= dst_cols ({dst_cols})")
     M = src.shape[0]
+    if dst_dtype not in _TORCH_CODE:
+        raise ValueError(f"dst_dtype must be float32 or bfloat16, got {dst_dtype}")
+    dst = _opt(dst, "dst", dst_dtype, (M, dst_cols))
+    dev = _device(src, dst)
     if dst is None:
-        dst = torch.empty((M, dst_cols), dtype=dst_dtype, device=src.device)
+        dst = torch.empty((M, dst_cols), dtype=dst_dtype, device=dev)
     _check(lib().dlrm_cast_rows(_ptr(src), _TORCH_CODE[src.dtype], src.stride(0), M, cols, _ptr(dst),
-                                _TORCH_CODE[dst.dtype], dst_cols, _stream(src.device)), "dlrm_cast_rows")
+                                _TORCH_CODE[dst.dtype], dst_cols, _stream(dev)), "dlrm_cast_rows")
     return dst
 
 

@@ -1,0 +1,173 @@
+"""The Python binding rejects bad tensors before it calls the library (CPU only).
+
+The C entry points take plain pointers, so a CPU tensor, an output of the wrong shape or type, or
+a short workspace would make a kernel read or write out of bounds.  Each wrapper checks its
+arguments first; here the library is replaced by a stub that fails the test if any entry point
+other than a size query is reached, so a passing test shows the error came before anything was
+enqueued.
+"""
+import pytest
+import torch
+
+import recommendation_model_sparse_amd.binding as L
+
+
+class _NoCompute:
+    """Stands in for the library: size queries answer, every other entry point fails the test."""
+
+    def __getattr__(self, name):
+        if name.endswith("workspace_size"):
+            return lambda *a: 1024
+        if name == "dlrm_status_string":
+            return lambda s: b"stub"
+
+        def call(*a):
+            raise AssertionError(f"{name} was called with a bad argument")
+        return call
+
+
+@pytest.fixture(autouse=True)
+def stub_library(monkeypatch):
+    monkeypatch.setattr(L, "_lib", _NoCompute())
+
+
+f32, bf16, i64, i32 = torch.float32, torch.bfloat16, torch.int64, torch.int32
+T, V, D, B = 3, 10, 8, 4
+
+
+def tables(dtype=f32):
+    return [torch.zeros(V, D, dtype=dtype) for _ in range(T)]
+
+
+def batch(L_per_bag=2, dtype=i64):
+    nnz = T * B * L_per_bag
+    return torch.zeros(nnz, dtype=dtype), torch.arange(0, nnz + 1, L_per_bag, dtype=dtype)
+
+
+def bad(msg, fn, *a, **k):
+    with pytest.raises((ValueError, TypeError), match=msg):
+        fn(*a, **k)
+
+
+# ---------------------------------------------------------------- lookup
+
+def test_emb_bag_fwd_checks():
+    idx, off = batch()
+    nnz = idx.numel()
+    bad("CUDA", L.emb_bag_fwd, tables(), idx, off)                      # right shapes, host memory
+    bad("out must have shape", L.emb_bag_fwd, tables(), idx, off, out=torch.zeros(B, T, D + 1))
+    bad("out must be", L.emb_bag_fwd, tables(), idx, off, out=torch.zeros(B, T, D, dtype=bf16))
+    bad("per_sample_weights must have shape", L.emb_bag_fwd, tables(), idx, off, torch.zeros(nnz - 1))
+    bad("per_sample_weights must be", L.emb_bag_fwd, tables(), idx, off, torch.zeros(nnz, dtype=torch.float64))
+    bad("offsets must have", L.emb_bag_fwd, tables(), idx, off[:-1])
+    bad("indices must be", L.emb_bag_fwd, tables(), idx.to(i32), off)
+    bad("contiguous", L.emb_bag_fwd, tables(), idx, off, out=torch.zeros(B, D, T).transpose(1, 2))
+    bad("tables must be", L.emb_bag_fwd, [torch.zeros(V, D), torch.zeros(V, D + 1)], idx, off)
+    bad("must be a torch.Tensor", L.emb_bag_fwd, tables(), idx.tolist(), off)
+
+
+def test_emb_bag_fwd_ex_checks():
+    idx, off = batch(dtype=i32)
+    bad("CUDA", L.emb_bag_fwd_ex, tables(), idx, off)
+    bad("offsets must be", L.emb_bag_fwd_ex, tables(), idx, off.to(i64))
+    bad("out must be", L.emb_bag_fwd_ex, tables(), idx, off, out=torch.zeros(B, T, D), out_dtype=bf16)
+    bad("out_dtype", L.emb_bag_fwd_ex, tables(), idx, off, out_dtype=torch.float16)
+
+
+def test_emb_bag_interact_fwd_checks():
+    idx, off = batch()
+    P = (T + 1) * T // 2
+    bad("CUDA", L.emb_bag_interact_fwd, tables(), idx, off, None, torch.zeros(B, D))
+    bad("dense must have shape", L.emb_bag_interact_fwd, tables(), idx, off, None, torch.zeros(B + 1, D))
+    bad("out must have shape", L.emb_bag_interact_fwd, tables(), idx, off, None, torch.zeros(B, D),
+        out=torch.zeros(B, P))
+
+
+# ---------------------------------------------------------------- interaction
+
+def test_interact_checks():
+    N = T + 1
+    P = N * (N - 1) // 2
+    dense, pooled = torch.zeros(B, D), torch.zeros(B, T, D)
+    bad("CUDA", L.dlrm_interact_fwd, dense, pooled)
+    bad("pooled must be", L.dlrm_interact_fwd, dense, torch.zeros(B + 1, T, D))
+    bad("pooled must be", L.dlrm_interact_fwd, dense, torch.zeros(B, T, D + 1))
+    bad("out must have shape", L.dlrm_interact_fwd, dense, pooled, out=torch.zeros(B, P))
+    bad("dense must be", L.dlrm_interact_fwd, dense.to(bf16), pooled)
+    g = torch.zeros(B, P + D)
+    bad("CUDA", L.dlrm_interact_bwd, g, dense, pooled)
+    bad("grad_out must have shape", L.dlrm_interact_bwd, torch.zeros(B, P + D - 1), dense, pooled)
+    bad("grad_dense must have shape", L.dlrm_interact_bwd, g, dense, pooled, grad_dense=torch.zeros(B, D + 1))
+    bad("grad_pooled must have shape", L.dlrm_interact_bwd, g, dense, pooled, grad_pooled=torch.zeros(B, T - 1, D))
+
+
+# ---------------------------------------------------------------- embedding backward
+
+def test_backward_checks():
+    idx, off = batch()
+    nnz = idx.numel()
+    st = [torch.zeros(V) for _ in range(T)]
+    gp = torch.zeros(B, T, D)
+    bad("CUDA", L.emb_bag_bwd_adagrad, tables(), st, idx, off, None, gp, 0.01, 1e-8)
+    bad("grad_pooled must have shape", L.emb_bag_bwd_adagrad, tables(), st, idx, off, None,
+        torch.zeros(B, T, D // 2), 0.01, 1e-8)
+    bad(r"state\[1\] must have shape", L.emb_bag_bwd_adagrad, tables(), [st[0], torch.zeros(V - 1), st[2]],
+        idx, off, None, gp, 0.01, 1e-8)
+    bad("state", L.emb_bag_bwd_adagrad, tables(), st[:2], idx, off, None, gp, 0.01, 1e-8)
+    bad("workspace must hold", L.emb_bag_bwd_adagrad, tables(), st, idx, off, None, gp, 0.01, 1e-8,
+        workspace=torch.zeros(16, dtype=torch.uint8))
+    bad("workspace must be", L.emb_bag_bwd_adagrad, tables(), st, idx, off, None, gp, 0.01, 1e-8,
+        workspace=torch.zeros(4096, dtype=f32))
+    outs = L.AdagradOutputs(nnz - 1, "cpu")
+    bad("outputs.unique_keys must hold", L.emb_bag_bwd_adagrad, tables(), st, idx, off, None, gp, 0.01, 1e-8,
+        outputs=outs)
+    bad("CUDA", L.emb_bag_bwd_update, tables(), None, idx, off, None, gp, L.DLRM_OPT_SGD, 0.01)
+    bad("needs one state vector", L.emb_bag_bwd_update, tables(), None, idx, off, None, gp, L.DLRM_OPT_ADAGRAD, 0.01)
+    bad("grad_pooled must be", L.emb_bag_bwd_update, tables(), None, idx, off, None, gp.to(bf16), L.DLRM_OPT_SGD, 0.01)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    bad("CUDA", L.emb_bag_bwd_plan, [V] * T, D, idx, off, None, ws)
+    bad("workspace must hold", L.emb_bag_bwd_plan, [V] * T, D, idx, off, None, torch.zeros(8, dtype=torch.uint8))
+    bad("CUDA", L.emb_bag_bwd_apply, tables(), st, B, nnz, False, gp, L.DLRM_OPT_ADAGRAD, 0.01, 1e-8, ws)
+    bad("grad_pooled must have shape", L.emb_bag_bwd_apply, tables(), st, B + 1, nnz, False, gp,
+        L.DLRM_OPT_ADAGRAD, 0.01, 1e-8, ws)
+
+
+def test_fill_checks():
+    bad("CUDA", L.dlrm_synth_fill_table, torch.zeros(V, D), 0, 1, 0.1)
+    bad("table must be", L.dlrm_synth_fill_table, torch.zeros(V, D, dtype=i32), 0, 1, 0.1)
+
+
+# ---------------------------------------------------------------- dense layers
+
+def test_dense_layer_checks():
+    M, K, N = 6, 16, 8
+    x, W, b = torch.zeros(M, K, dtype=bf16), torch.zeros(N, K, dtype=bf16), torch.zeros(N)
+    bad("CUDA", L.dlrm_linear_fwd, x, W, b)
+    bad("W must be", L.dlrm_linear_fwd, x, torch.zeros(N, K + 8, dtype=bf16), b)
+    bad("b must have shape", L.dlrm_linear_fwd, x, W, torch.zeros(N + 1))
+    bad("y must have shape", L.dlrm_linear_fwd, x, W, b, y=torch.zeros(M, N + 1, dtype=bf16))
+    bad("x must be", L.dlrm_linear_fwd, x.float(), W, b)
+    dy, y = torch.zeros(M, N), torch.zeros(M, N, dtype=bf16)
+    bad("CUDA", L.dlrm_linear_bwd, dy, y, L.DLRM_ACT_RELU, x, W)
+    bad("dy must have shape", L.dlrm_linear_bwd, torch.zeros(M, N + 1), y, L.DLRM_ACT_RELU, x, W)
+    bad("needs the forward output", L.dlrm_linear_bwd, dy, None, L.DLRM_ACT_RELU, x, W)
+    bad("dx must have shape", L.dlrm_linear_bwd, dy, y, L.DLRM_ACT_RELU, x, W, dx=torch.zeros(M, K - 1))
+    bad("dW must have shape", L.dlrm_linear_bwd, dy, y, L.DLRM_ACT_RELU, x, W, dW=torch.zeros(K, N))
+    bad("dz_bf16 must be", L.dlrm_linear_bwd, dy, y, L.DLRM_ACT_RELU, x, W, dz_bf16=torch.zeros(M, N))
+    w1, b1, t = torch.zeros(K, dtype=bf16), torch.zeros(1), torch.zeros(M)
+    bad("CUDA", L.dlrm_bce_head, x, w1, b1, t)
+    bad("t must have shape", L.dlrm_bce_head, x, w1, b1, torch.zeros(M + 1))
+    bad("w must have shape", L.dlrm_bce_head, x, torch.zeros(K + 1, dtype=bf16), b1, t)
+    out = {"p": torch.zeros(M), "loss": torch.zeros(1), "dx": torch.zeros(M, K), "dw": torch.zeros(K),
+           "db": torch.zeros(2)}
+    bad("out\\['db'\\] must have shape", L.dlrm_bce_head, x, w1, b1, t, out=out)
+    w32, g = torch.zeros(N, K), torch.zeros(N, K)
+    bad("CUDA", L.dlrm_sgd_dense, w32, None, g, 0.1)
+    bad("g must have shape", L.dlrm_sgd_dense, w32, None, torch.zeros(N * K), 0.1)
+    bad("w16 must have shape", L.dlrm_sgd_dense, w32, torch.zeros(N, K + 1, dtype=bf16), g, 0.1)
+    bad("CUDA", L.dlrm_sgd_dense_multi, [(w32, None, g)], 0.1)
+    bad(r"params\[1\].g must have shape", L.dlrm_sgd_dense_multi, [(w32, None, g), (b, None, torch.zeros(N + 1))], 0.1)
+    src = torch.zeros(M, 13)
+    bad("CUDA", L.dlrm_cast_rows, src, 13, 16, bf16)
+    bad("cols", L.dlrm_cast_rows, src, 14, 16, bf16)
+    bad("dst must have shape", L.dlrm_cast_rows, src, 13, 16, bf16, dst=torch.zeros(M, 15, dtype=bf16))

@@ -1,0 +1,39 @@
+"""Bad device tensors are refused by the binding before anything is enqueued (GPU)."""
+import pytest
+import torch
+
+from recommendation_model_sparse_amd import dlrm_interact_bwd, dlrm_interact_fwd, emb_bag_bwd_adagrad, emb_bag_fwd
+
+from gpu_util import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_wrong_shapes_on_the_device_are_refused():
+    T, V, D, B = 3, 20, 16, 5
+    tabs = [torch.ones(V, D, device=DEV) for _ in range(T)]
+    idx = torch.zeros(T * B * 2, dtype=torch.int64, device=DEV)
+    off = torch.arange(0, T * B * 2 + 1, 2, dtype=torch.int64, device=DEV)
+    sentinel = torch.full((B, T, D + 1), 7.0, device=DEV)
+    say("[binding] refused: out of the wrong shape")
+    with pytest.raises(ValueError, match="out must have shape"):
+        emb_bag_fwd(tabs, idx, off, out=sentinel)
+    with pytest.raises(ValueError, match="per_sample_weights"):
+        emb_bag_fwd(tabs, idx, off, torch.ones(3, device=DEV))
+    with pytest.raises(ValueError, match="CUDA|must be on"):
+        emb_bag_fwd(tabs, idx.cpu(), off)
+    dense, pooled = torch.ones(B, D, device=DEV), torch.ones(B, T, D, device=DEV)
+    with pytest.raises(ValueError, match="out must have shape"):
+        dlrm_interact_fwd(dense, pooled, out=sentinel.view(B, -1)[:, :7].contiguous())
+    with pytest.raises(ValueError, match="grad_out must have shape"):
+        dlrm_interact_bwd(torch.ones(B, 3, device=DEV), dense, pooled)
+    states = [torch.zeros(V, device=DEV) for _ in range(T)]
+    with pytest.raises(ValueError, match="grad_pooled must have shape"):
+        emb_bag_bwd_adagrad(tabs, states, idx, off, None, torch.ones(B, T, D // 2, device=DEV), 0.01, 1e-8)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
+    assert all(bool((t == 1.0).all()) for t in tabs) and all(bool((s == 0).all()) for s in states)
+    say("[binding] a good call still runs")
+    out = emb_bag_fwd(tabs, idx, off)
+    torch.cuda.synchronize()
+    assert bool((out == 2.0).all())
