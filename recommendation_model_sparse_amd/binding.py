@@ -69,10 +69,13 @@ def lib() -> ctypes.CDLL:
         L.dlrm_status_string.argtypes = [ctypes.c_int]
         L.dlrm_status_string.restype = ctypes.c_char_p
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
+        L.dlrm_probe_read.argtypes = [p, u64, p, u32, p]
+        L.dlrm_probe_gather.argtypes = [p, i64, i32, p, i64, p, u32, p]
         L.dlrm_trace_enable.argtypes = [ctypes.c_int]
         L.dlrm_trace_read.argtypes = [i32, p, p, p, p]
         for f in (L.emb_bag_fwd, L.emb_bag_fwd_ex, L.emb_bag_bwd_update, L.dlrm_interact_fwd, L.emb_bag_interact_fwd, L.dlrm_interact_bwd, L.emb_bag_bwd_adagrad,
-                  L.dlrm_synth_fill_table, L.dlrm_trace_enable, L.dlrm_trace_read):
+                  L.dlrm_synth_fill_table, L.dlrm_trace_enable, L.dlrm_trace_read, L.dlrm_probe_read,
+                  L.dlrm_probe_gather):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -428,6 +431,31 @@ def dlrm_synth_fill_table(table: torch.Tensor, t: int, seed: int, scale: float) 
     _check(lib().dlrm_synth_fill_table(_ptr(table), _dtype_code(table), table.shape[0],
                                        table.shape[1], t, seed, float(scale),
                                        _stream(dev)), "dlrm_synth_fill_table")
+
+
+# ---------------------------------------------------------------- HBM read probes (dlrm_probe.h)
+
+def dlrm_probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream-read every byte of ``buf`` once (C: dlrm_probe_read); ``sink`` is uint32/int32 scratch."""
+    _need(buf, "buf")
+    _need(sink, "sink", (torch.int32,))
+    nbytes = buf.numel() * buf.element_size()
+    if nbytes == 0 or nbytes % 16:
+        raise ValueError("buf must hold a positive multiple of 16 bytes")
+    dev = _device(buf, sink)
+    _check(lib().dlrm_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(dev)), "dlrm_probe_read")
+
+
+def dlrm_probe_gather(table: torch.Tensor, idx: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read rows ``idx`` of the 2-D ``table`` with no output (C: dlrm_probe_gather)."""
+    _need(table, "table")
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, cols]")
+    _need(idx, "idx", torch.int64)
+    _need(sink, "sink", (torch.int32,))
+    dev = _device(table, idx, sink)
+    _check(lib().dlrm_probe_gather(_ptr(table), table.shape[0], table.shape[1] * table.element_size(), _ptr(idx),
+                                   idx.numel(), _ptr(sink), sink.numel(), _stream(dev)), "dlrm_probe_gather")
 
 
 # ---------------------------------------------------------------- dense layers (dlrm_mlp.h)

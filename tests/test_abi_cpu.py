@@ -322,3 +322,20 @@ def test_size_limits_rejected(L):
                                   0, None) == UNSUPPORTED
         assert L.emb_bag_bwd_apply(ptrs(FAKE), ptrs(FAKE), i64s(*rows), 1, 16, 0, B, n, 0, FAKE, 0, 0.01, 1e-8,
                                    FAKE, 1, None, None) == UNSUPPORTED
+
+
+def test_probes_reject(L):
+    r = L.dlrm_probe_read
+    assert r(None, 1024, FAKE, 8, None) == INVALID
+    assert r(FAKE, 1000, FAKE, 8, None) == INVALID     # not a multiple of 16 bytes
+    assert r(FAKE, 0, FAKE, 8, None) == INVALID
+    assert r(FAKE + 8, 1024, FAKE, 8, None) == INVALID
+    assert r(FAKE, 1024, FAKE, 0, None) == INVALID
+    g = L.dlrm_probe_gather
+    assert g(FAKE, 0, 256, FAKE, 4, FAKE, 8, None) == INVALID
+    assert g(FAKE, 10, 24, FAKE, 4, FAKE, 8, None) == INVALID      # not a multiple of 16
+    assert g(FAKE, 10, 2048, FAKE, 4, FAKE, 8, None) == INVALID    # above 1024 bytes
+    assert g(FAKE, 10, 48, FAKE, 4, FAKE, 8, None) == INVALID      # 3 lanes per row
+    assert g(FAKE, 10, 256, None, 4, FAKE, 8, None) == INVALID
+    assert g(FAKE, 10, 256, FAKE, 1 << 31, FAKE, 8, None) == INVALID
+    assert g(FAKE, 10, 256, FAKE, 0, FAKE, 8, None) == OK          # nothing to read
