@@ -1,19 +1,30 @@
 """Benchmark of the DLRM sparse hot path on one MI355X.
 
-One step = the whole path over one synthetic batch of the multi-hot bf16
-workload (26 tables, D=128, B=16384, bag lengths truncated-geometric on
-[1,100] with mean 20, Zipf(1.05) rows):
+Headline step = the whole path over one synthetic batch of the multi-hot bf16 workload (26 tables,
+D=128, B=16384, bag lengths truncated-geometric on [1,100] with mean 20, Zipf(1.05) rows):
     emb_bag_fwd -> dlrm_interact_fwd -> dlrm_interact_bwd -> emb_bag_bwd_adagrad
-(sort / unique / segment-reduce / row-wise Adagrad in place on the bf16
-tables, all integer outputs requested), every call in order on one stream.  The
-step is also timed with the batch-only half of the embedding backward
-(emb_bag_bwd_plan: keys, sort, segments) on a second stream beside the lookup
-and the interaction, emb_bag_bwd_apply following the interaction backward (the
-results are the same bits); --overlap-plan makes that form the headline.
-Inputs are resident in HBM before the timed region; R pre-generated batches
-rotate.  Prints one JSON line.
+(sort / unique / segment-reduce / row-wise Adagrad in place on the bf16 tables, all integer outputs
+requested), every call in order on one stream.  The step is also timed with the batch-only half of
+the embedding backward (emb_bag_bwd_plan) on a second stream; --overlap-plan makes that the headline.
+Inputs are resident in HBM before the timed region; R pre-generated batches rotate.
+
+The same JSON line also carries:
+  configs      every workload timed on its own: the tiny forward, the one-hot fp32 forward, the
+               multi-hot step with uniform rows (cache-cold control), the big-table forward
+               (8 x 50M bf16 rows) with uniform and Zipf(1.2) rows, and the fp32 training step on
+               the one-hot shapes;
+  gather       per workload, the lookup kernel's time, its logical gathered GB/s, and the HBM bytes
+               the counters saw (FETCH_SIZE + WRITE_SIZE, profiles/hbm_traffic_<workload>.md) as
+               GB/s and as a fraction of the 8 TB/s HBM peak;
+  hbm_context  what plain streaming reaches here: a device copy, a read-only stream, and a gather of
+               random 256-byte rows from 102 GB with no output (the cold lookup's read ceiling);
+  cpu_baseline the oracle on the host cores (all, and one), samples/s and gathered GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu] [--overlap-plan]
+                    [--only SECTION]
+
+--only runs one section and prints its object (for profiling runs): headline, tiny, onehot,
+multihot-uniform, bigtables-uniform, bigtables-zipf, train-onehot, probes.
 """
 from __future__ import annotations
 
@@ -29,16 +40,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+SECTIONS = ("headline", "tiny", "onehot", "multihot-uniform", "bigtables-uniform", "bigtables-zipf",
+            "train-onehot", "probes")
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_multihot_bf16.md")
+def traffic_profile(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "hbm_traffic_" + workload.replace("-", "_") + ".md")
 
 
-def measured_traffic(kernel: str, workload: str, path: str = TRAFFIC_PROFILE, root: str = ROOT):
+TRAFFIC_PROFILE = traffic_profile("multihot-bf16-zipf")
+
+
+def measured_traffic(kernel: str, workload: str, path: str = None, root: str = ROOT):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when the summary is
     missing, covers another workload, or the kernel's sources changed since it was taken."""
     import hashlib
+    path = path or traffic_profile(workload)
     try:
         line = next(l for l in open(path) if l.startswith("traffic-json: "))
     except (OSError, StopIteration):
@@ -51,8 +69,11 @@ def measured_traffic(kernel: str, workload: str, path: str = TRAFFIC_PROFILE, ro
     for f in e["sources"]:
         h.update(f.encode())
         h.update(b"\0")
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
+        try:
+            with open(os.path.join(root, f), "rb") as fh:
+                h.update(fh.read())
+        except OSError:
+            return None
     if h.hexdigest() != e["source_sha256"]:
         return None
     return {"bytes": e["read_bytes"] + e["write_bytes"], "read": e["read_bytes"],
@@ -63,298 +84,297 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, batches, n_samples: int, min_seconds: float = 10.0):
-    """The oracle, as it stands, on a bounded sample of the same workload (host cores): the full
-    step on the first n_samples samples of successive batches, until about min_seconds of work."""
+# ---------------------------------------------------------------- timing helpers
+
+def ev_ms(fn, nb: int, steps: int, warm: int = 2) -> float:
+    """Mean ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warm):
+        fn(i % nb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        fn(i % nb)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def traced(fn, nb: int, steps: int):
+    """{kernel: {launches per call, ms per launch, ms per call}} from the library's own HIP events."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_trace_enable, dlrm_trace_read
+    torch.cuda.synchronize()
+    dlrm_trace_enable(True)
+    for i in range(steps):
+        fn(i % nb)
+    torch.cuda.synchronize()
+    tr = dlrm_trace_read()
+    dlrm_trace_enable(False)
+    return {k: {"launches_per_call": n / steps, "ms_per_launch": ms / n, "ms_per_call": ms / steps}
+            for k, (n, ms) in tr.items()}
+
+
+def dominant(kern: dict) -> str:
+    return max(kern, key=lambda k: kern[k]["ms_per_call"])
+
+
+def lookup_kernel(kern: dict) -> str:
+    """The pooling kernel of an emb_bag_fwd trace (the one that ran longest)."""
+    pools = {k: v for k, v in kern.items() if k.startswith("pool_")}
+    return dominant(pools) if pools else dominant(kern)
+
+
+# ---------------------------------------------------------------- inputs
+
+def device_tables(wl, dev):
+    import torch
+    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if wl.init == "normal":
+        tabs = []
+        for t in wl.host_tables():
+            x = torch.from_numpy(t.view(np.int16) if t.dtype == np.uint16 else t)
+            tabs.append((x.view(torch.bfloat16) if t.dtype == np.uint16 else x).to(dev))
+        return tabs
+    tabs = []
+    for t, v in enumerate(wl.rows):
+        x = torch.empty((v, wl.D), dtype=dt, device=dev)
+        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
+        tabs.append(x)
+    return tabs
+
+
+def device_batches(wl, dev, n: int, grads: bool = False):
+    import torch
+    out, host = [], []
+    for i in range(n):
+        b = wl.batch(i)
+        host.append(b)
+        d = dict(idx=torch.from_numpy(b.indices).to(dev), off=torch.from_numpy(b.offsets).to(dev),
+                 dense=torch.from_numpy(b.dense).to(dev), nnz=b.nnz)
+        if grads:
+            d["g"] = torch.from_numpy(b.grad_out()).to(dev)
+        out.append(d)
+    return out, host
+
+
+def lookup_bytes(wl, nnz: float):
+    """(gathered bytes, all algorithmic bytes) of one lookup call: rows, indices, offsets, fp32 output."""
+    gathered = nnz * wl.D * wl.elem_size
+    return gathered, gathered + nnz * 8 + (wl.T * wl.B + 1) * 8 + wl.B * wl.T * wl.D * 4
+
+
+def gather_entry(wl, workload: str, kernel: str, ms: float, nnz: float) -> dict:
+    """Lookup bandwidth of one workload: logical (rows gathered / time) and counted (HBM bytes the
+    FETCH_SIZE/WRITE_SIZE counters saw per launch / time), each against the 8 TB/s peak."""
+    gathered, alg = lookup_bytes(wl, nnz)
+    s = ms / 1e3
+    tr = measured_traffic(kernel, workload)
+    e = {"kernel": kernel, "ms_per_launch": ms, "lookups": nnz, "gathered_bytes": gathered,
+         "logical_gathered_GBps": gathered / s / 1e9,
+         "logical_gathered_frac_of_hbm_peak": gathered / s / 1e9 / HBM_PEAK_GBPS,
+         "algorithmic_bytes": alg, "algorithmic_GBps": alg / s / 1e9,
+         "hbm_read_bytes": None, "hbm_write_bytes": None, "hbm_GBps": None, "hbm_frac_of_peak": None,
+         "counters": os.path.relpath(traffic_profile(workload), ROOT)}
+    if tr:
+        e.update(hbm_read_bytes=tr["read"], hbm_write_bytes=tr["write"], hbm_GBps=tr["bytes"] / s / 1e9,
+                 hbm_frac_of_peak=tr["bytes"] / s / 1e9 / HBM_PEAK_GBPS)
+    return e
+
+
+# ---------------------------------------------------------------- forward-only workloads
+
+def bench_forward(wl, workload: str, dev, steps: int, rotate: int, probe_gather: bool = False):
+    """Lookup alone, the interaction alone, the two calls, and the fused call (HIP events)."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
+    t0 = time.time()
+    tabs = device_tables(wl, dev)
+    batches, _ = device_batches(wl, dev, rotate)
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {workload}: {wl.table_bytes() / 1e9:.2f} GB of tables, inputs ready in {time.time() - t0:.1f}s")
+    nb = len(batches)
+
+    def look(i):
+        b = batches[i]
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+
+    def inter_only(i):
+        dlrm_interact_fwd(batches[i]["dense"], pooled, out=inter)
+
+    def two(i):
+        look(i)
+        inter_only(i)
+
+    def fused(i):
+        b = batches[i]
+        emb_bag_interact_fwd(tabs, b["idx"], b["off"], None, b["dense"], out=inter)
+
+    ms = {"lookup": ev_ms(look, nb, steps), "interaction": ev_ms(inter_only, nb, steps),
+          "two_call": ev_ms(two, nb, steps), "fused": ev_ms(fused, nb, steps)}
+    kern = traced(two, nb, steps)
+    kern.update({("fused:" + k): v for k, v in traced(fused, nb, steps).items()})
+    nnz = float(np.mean([b["nnz"] for b in batches]))
+    lk = lookup_kernel({k: v for k, v in kern.items() if not k.startswith("fused:")})
+    gathered, alg = lookup_bytes(wl, nnz)
+    B = wl.B
+    res = {"workload": wl.note, "B": B, "tables": wl.T, "D": wl.D, "table_dtype": wl.dtype,
+           "table_GB": wl.table_bytes() / 1e9, "lookups_per_batch": nnz, "ms": ms,
+           "fwd_samples_per_s": B / (min(ms["two_call"], ms["fused"]) / 1e3),
+           "two_call_samples_per_s": B / (ms["two_call"] / 1e3), "fused_samples_per_s": B / (ms["fused"] / 1e3),
+           "fused_speedup": ms["two_call"] / ms["fused"],
+           "lookup_gathered_GBps": gathered / (ms["lookup"] / 1e3) / 1e9,
+           "lookup_algorithmic_GBps": alg / (ms["lookup"] / 1e3) / 1e9,
+           "kernels": kern}
+    gat = gather_entry(wl, workload, lk, kern[lk]["ms_per_launch"], nnz)
+    extra = {}
+    if probe_gather:
+        # the same number of random rows of the same tables, read with no output written: the
+        # lookup's read ceiling on this GPU for this access pattern
+        from recommendation_model_sparse_amd import dlrm_probe_gather
+        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        gen = torch.Generator(device=dev).manual_seed(wl.seed + 17)
+        per_t = 1 << 20  # 256 MB of 256-byte rows per launch: far above launch overhead and the caches
+        rows = [torch.randint(0, v, (per_t,), generator=gen, device=dev, dtype=torch.int64) for v in wl.rows]
+        t_probe = ev_ms(lambda i: [dlrm_probe_gather(tabs[t], rows[t], sink) for t in range(wl.T)], 1, steps)
+        nbytes = per_t * wl.T * wl.D * wl.elem_size
+        extra = {"random_row_read_GBps": nbytes / (t_probe / 1e3) / 1e9, "random_rows": per_t * wl.T,
+                 "row_bytes": wl.D * wl.elem_size,
+                 "how": f"dlrm_probe_gather: {per_t} uniform random rows of each of the {wl.T} tables, "
+                        f"no output; HIP events over {steps} passes"}
+    del tabs
+    torch.cuda.empty_cache()
+    return res, gat, extra
+
+
+# ---------------------------------------------------------------- the fp32 training step
+
+def bench_train_onehot(wl, dev, steps: int, rotate: int):
+    """The training step on the one-hot fp32 shapes: lookup, interaction forward and backward, and
+    the embedding backward with row-wise Adagrad in place (no integer outputs requested)."""
+    import torch
+    from recommendation_model_sparse_amd import (dlrm_interact_bwd, dlrm_interact_fwd, emb_bag_bwd_adagrad,
+                                                 emb_bag_bwd_workspace_size, emb_bag_fwd)
+    tabs = device_tables(wl, dev)
+    states = [torch.zeros(v, dtype=torch.float32, device=dev) for v in wl.rows]
+    batches, _ = device_batches(wl, dev, rotate, grads=True)
+    nb = len(batches)
+    max_nnz = max(b["nnz"] for b in batches)
+    ws = torch.empty(emb_bag_bwd_workspace_size(wl.rows, wl.D, wl.B, max_nnz), dtype=torch.uint8, device=dev)
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
+    gd = torch.empty((wl.B, wl.D), dtype=torch.float32, device=dev)
+    gp = torch.empty_like(pooled)
+
+    def fwd(i):
+        b = batches[i]
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+        dlrm_interact_fwd(b["dense"], pooled, out=inter)
+
+    def bwd(i):
+        b = batches[i]
+        dlrm_interact_bwd(b["g"], b["dense"], pooled, grad_dense=gd, grad_pooled=gp)
+        emb_bag_bwd_adagrad(tabs, states, b["idx"], b["off"], None, gp, wl.lr, wl.eps, workspace=ws)
+
+    def step(i):
+        fwd(i)
+        bwd(i)
+
+    for i in range(3):
+        step(i % nb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i % nb)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / steps * 1e3
+    ms_bwd = ev_ms(bwd, nb, steps)
+    kern = traced(step, nb, steps)
+    launches = sum(v["launches_per_call"] for v in kern.values())
+    del tabs, states
+    torch.cuda.empty_cache()
+    return {"workload": wl.note, "B": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "f32",
+            "ms_per_step": ms_step, "samples_per_s": wl.B / (ms_step / 1e3),
+            "ms_backward": ms_bwd, "backward_samples_per_s": wl.B / (ms_bwd / 1e3),
+            "kernel_launches_per_step": launches,
+            "kernel_ms_sum_per_step": sum(v["ms_per_call"] for v in kern.values()), "kernels": kern,
+            "note": "wall clock over the timed steps; every call of the step on one stream"}
+
+
+# ---------------------------------------------------------------- the multi-hot step (headline)
+
+def cpu_baseline(wl, batches, n_samples: int, min_seconds: float = 10.0, one_core_samples: int = 1024,
+                 one_core_seconds: float = 4.0):
+    """The oracle, as it stands, on bounded samples of the same workload (host cores): the full step
+    on the first n_samples samples of successive batches until about min_seconds of work, with every
+    core in the affinity mask; the same on one core over one_core_samples samples; and the pooling
+    alone on one full batch, as gathered GB/s."""
     import oracle
     from recommendation_model_sparse_amd.synth import subset_tables
 
     cores = len(os.sched_getaffinity(0))
-    S = np.arange(n_samples)
-    done, lookups, dt = 0, 0, 0.0
-    for batch in batches:
-        sub_wl, sub, row_ids = batch.sample_subset(S)
-        tabs = subset_tables(wl, row_ids)
-        states = [np.zeros(len(r), np.float32) for r in row_ids]
-        g = batch.grad_out()[S]
-        t0 = time.perf_counter()
-        pooled, _ = oracle.emb_bag_fwd(tabs, sub.indices, sub.offsets, sub.weights, len(S), threads=cores)
-        p32 = pooled.astype(np.float32)
-        oracle.interact_fwd(sub.dense, p32, threads=cores)
-        _, gp, _, _ = oracle.interact_bwd(g, sub.dense, p32, threads=cores)
-        oracle.emb_bag_bwd_adagrad(tabs, states, sub.indices, sub.offsets, sub.weights, len(S),
-                                   gp.astype(np.float32), wl.lr, wl.eps)
-        dt += time.perf_counter() - t0
-        done += len(S)
-        lookups += sub.nnz
-        if dt >= min_seconds:
-            break
-    return {"value": done / dt, "unit": "samples/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done // len(S)} batch(es) x {len(S)} of {wl.B} samples ({lookups} lookups): the full "
-                      f"step (pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s"}
+
+    def run(samples, threads, budget):
+        S = np.arange(samples)
+        done, lookups, dt, dt_pool = 0, 0, 0.0, 0.0
+        for batch in batches:
+            sub_wl, sub, row_ids = batch.sample_subset(S)
+            tabs = subset_tables(wl, row_ids)
+            states = [np.zeros(len(r), np.float32) for r in row_ids]
+            g = batch.grad_out()[S]
+            t0 = time.perf_counter()
+            pooled, _ = oracle.emb_bag_fwd(tabs, sub.indices, sub.offsets, sub.weights, len(S), threads=threads)
+            dt_pool += time.perf_counter() - t0
+            p32 = pooled.astype(np.float32)
+            oracle.interact_fwd(sub.dense, p32, threads=threads)
+            _, gp, _, _ = oracle.interact_bwd(g, sub.dense, p32, threads=threads)
+            oracle.emb_bag_bwd_adagrad(tabs, states, sub.indices, sub.offsets, sub.weights, len(S),
+                                       gp.astype(np.float32), wl.lr, wl.eps)
+            dt += time.perf_counter() - t0
+            done += len(S)
+            lookups += sub.nnz
+            if dt >= budget:
+                break
+        return done / dt, done, lookups, dt, dt_pool
+
+    v_all, done, lookups, dt, dt_pool = run(n_samples, cores, min_seconds)
+    v_one, done1, _, dt1, _ = run(one_core_samples, 1, one_core_seconds)
+    return {"value": v_all, "unit": "samples/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done // n_samples} batch(es) x {n_samples} of {wl.B} samples ({lookups} lookups): the full "
+                      f"step (pool, interaction fwd/bwd, sort/segment/Adagrad) in fp64, {dt:.1f} s",
+            "value_1_core": v_one, "cores_1": 1,
+            "sample_1_core": f"{done1 // one_core_samples} batch(es) x {one_core_samples} samples, the same step "
+                             f"on one thread, {dt1:.1f} s",
+            # the pooling step of the all-core run alone, by the GPU's formula (rows gathered / time)
+            "gathered_GBps": lookups * wl.D * wl.elem_size / dt_pool / 1e9,
+            "gathered_sample": f"the oracle's pooling in the all-core run ({lookups} lookups, {cores} threads), "
+                               f"{dt_pool:.2f} s",
+            "threads_note": "pooling and the interaction run on OpenMP threads; the sort, segments and "
+                            "Adagrad step of the oracle are single-threaded"}
 
 
-def time_inference(tabs, batches, steps, pooled, inter):
-    """Mean ms of emb_bag_interact_fwd and of emb_bag_fwd + dlrm_interact_fwd (HIP events)."""
+def bench_headline(args, dev):
     import torch
-    from recommendation_model_sparse_amd import dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
-
-    def fused(b):
-        emb_bag_interact_fwd(tabs, b["idx"], b["off"], None, b["dense"], out=inter)
-
-    def two(b):
-        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
-        dlrm_interact_fwd(b["dense"], pooled, out=inter)
-
-    res = {}
-    for name, fn in (("fused", fused), ("two_call", two)):
-        for i in range(3):
-            fn(batches[i % len(batches)])
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(steps):
-            fn(batches[i % len(batches)])
-        ev[1].record()
-        torch.cuda.synchronize()
-        res[name] = ev[0].elapsed_time(ev[1]) / steps
-    return res
-
-
-def time_variants(tabs, states, batches, steps, ws, outs, gpooled, wl):
-    """Mean ms (HIP events) of the path variants on the same batches: bf16 pooled output, int32
-    indices and offsets, the SGD backward (updates the tables in place), and the weighted lookup
-    and Adagrad backward with per-sample weights U(0,1) (seeded, one array per batch)."""
-    import torch
-    from recommendation_model_sparse_amd import (DLRM_OPT_SGD, emb_bag_bwd_adagrad, emb_bag_bwd_update,
-                                                 emb_bag_fwd, emb_bag_fwd_ex)
-
-    dev = tabs[0].device
-    b32 = [dict(idx=b["idx"].to(torch.int32), off=b["off"].to(torch.int32)) for b in batches]
-    pooled_bf16 = torch.empty((wl.B, wl.T, wl.D), dtype=torch.bfloat16, device=dev)
-    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
-    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
-    wts = [torch.rand(b["idx"].numel(), generator=gen, device=dev) for b in batches]
-    runs = {
-        "fwd_weighted": lambda i: emb_bag_fwd(tabs, batches[i]["idx"], batches[i]["off"], wts[i], out=pooled),
-        "bwd_adagrad_weighted": lambda i: emb_bag_bwd_adagrad(tabs, states, batches[i]["idx"], batches[i]["off"],
-                                                              wts[i], gpooled, wl.lr, wl.eps, workspace=ws,
-                                                              outputs=outs),
-        "fwd_bf16_out": lambda i: emb_bag_fwd_ex(tabs, batches[i]["idx"], batches[i]["off"], None, out=pooled_bf16,
-                                                 out_dtype=torch.bfloat16),
-        "fwd_int32_indices": lambda i: emb_bag_fwd_ex(tabs, b32[i]["idx"], b32[i]["off"], None),
-        "bwd_sgd": lambda i: emb_bag_bwd_update(tabs, None, batches[i]["idx"], batches[i]["off"], None, gpooled,
-                                                DLRM_OPT_SGD, wl.lr, 0.0, workspace=ws, outputs=outs),
-    }
-    res = {}
-    for name, fn in runs.items():
-        for i in range(2):
-            fn(i % len(batches))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(steps):
-            fn(i % len(batches))
-        ev[1].record()
-        torch.cuda.synchronize()
-        res[name + "_ms"] = ev[0].elapsed_time(ev[1]) / steps
-    return res
-
-
-def time_full_step(tabs, states, batches, host_batches, steps, wl, max_nnz):
-    """The full single-GPU DLRM training step around the sparse path: bottom MLP 13-512-256-128,
-    the lookup, the interaction, top MLP 480-1024-1024-512-256 and the sigmoid + BCE head, the
-    backward pass, SGD on the dense layers and row-wise Adagrad on the tables (HIP events)."""
-    import torch
-    from recommendation_model_sparse_amd.dlrm_step import DlrmStep
-
-    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
-
-    dev = tabs[0].device
-    # start from the initial tables: the timed regions before this one updated them with
-    # synthetic upstream gradients, which are no training signal
-    for t, (x, v) in enumerate(zip(tabs, wl.rows)):
-        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
-    for st in states:
-        st.zero_()
-    m = DlrmStep(tabs, states, wl.B, 13, bottom=[512, 256, wl.D], top=[1024, 1024, 512, 256], lr_dense=0.01,
-                 lr_emb=wl.lr, eps=wl.eps, seed=wl.seed + 99, max_nnz=max_nnz)
-    extra = [(torch.from_numpy(hb.features(13)).to(dev), torch.from_numpy(hb.labels()).to(dev)) for hb in host_batches]
-
-    def run(i):
-        b = batches[i % len(batches)]
-        x, y = extra[i % len(extra)]
-        m.step(b["idx"], b["off"], x, y)
-
-    def region(overlap):
-        m.overlap = overlap
-        for i in range(2):
-            run(i)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(steps):
-            run(i)
-        ev[1].record()
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / steps
-
-    ms_one = region(False)
-    ms = region(True)
-    dims_b = [(16, 512), (512, 256), (256, wl.D)]
-    dims_t = [(m.Ip, 1024), (1024, 1024), (1024, 512), (512, 256), (256, 1)]
-    flops = 3 * 2 * wl.B * sum(k * n for k, n in dims_b + dims_t)  # forward + two backward GEMMs
-    return {"ms_per_step": ms, "samples_per_s": wl.B / (ms / 1e3), "ms_per_step_one_stream": ms_one,
-            "dense_gemm_tflop_per_step": flops / 1e12,
-            "loss_after": float(m.head_out["loss"].item()),
-            "layers": "bottom 13(16)-512-256-128, top 480-1024-1024-512-256-1, bf16 GEMMs (hipBLASLt), fp32 accumulation"}
-
-
-def hbm_context(dev):
-    """What plain streaming reaches on this GPU, as context for the kernels' figures: a 2 GiB
-    device-to-device copy, far larger than the caches (read + write bytes; HIP events, median of 5)."""
-    import torch
-    n = 1 << 29  # 2 GiB of fp32
-    src = torch.ones(n, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-
-    def med(fn):
-        ts = []
-        for _ in range(6):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts[1:])) / 1e3
-
-    t_copy = med(lambda: dst.copy_(src))
-    del src, dst
-    torch.cuda.empty_cache()
-    return {"copy_GBps": 2 * 4 * n / t_copy / 1e9, "bytes_copied": 4 * n,
-            "how": "2 GiB fp32 device copy, read + write bytes over its time, median of 5"}
-
-
-def inference_summary(inf, wl, nnz_avg):
-    D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
-    alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
-    f = inf["fused"] / 1e3
-    return {"fused_ms": inf["fused"], "two_call_ms": inf["two_call"],
-            "fused_samples_per_s": B / f, "two_call_samples_per_s": B / (inf["two_call"] / 1e3),
-            "speedup": inf["two_call"] / inf["fused"],
-            "fused_algorithmic_bytes": alg, "fused_GBps": alg / f / 1e9,
-            "fused_frac_hbm_peak": alg / f / 1e9 / HBM_PEAK_GBPS,
-            "gathered_GBps": nnz_avg * D * wl.elem_size / f / 1e9}
-
-
-def bench_inference_big(args, dev):
-    """Inference on one GPU's share of 8 x 50M-row bf16 tables (102.4 GB), one-hot, B=65536."""
-    import torch
-    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
-    from recommendation_model_sparse_amd.configs import make_config
-
-    wl = make_config(4)
-    if args.dist == "zipf":
-        wl = wl.with_(dist="zipf", alpha=1.2)
-    log(f"[bench] workload {wl.name} ({args.dist})")
-    tabs = []
-    for t, v in enumerate(wl.rows):
-        x = torch.empty((v, wl.D), dtype=torch.bfloat16, device=dev)
-        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
-        tabs.append(x)
-    batches = []
-    for i in range(args.rotate):
-        b = wl.batch(i)
-        batches.append(dict(idx=torch.from_numpy(b.indices).to(dev), off=torch.from_numpy(b.offsets).to(dev),
-                            dense=torch.from_numpy(b.dense).to(dev), nnz=b.nnz))
-    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
-    inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    inf = time_inference(tabs, batches, args.steps, pooled, inter)
-    hbm = hbm_context(dev)
-    nnz_avg = float(np.mean([b["nnz"] for b in batches]))
-    summ = inference_summary(inf, wl, nnz_avg)
-    res = {
-        "metric": "inference samples/sec (lookup fused with the interaction), 1 MI355X",
-        "value": summ["fused_samples_per_s"], "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": 3, "ms_per_step": inf["fused"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32",
-        "data": f"synthetic (seeded; counter-hash tables, {'Zipf(1.2)' if args.dist == 'zipf' else 'uniform'} rows)",
-        "config": {"workload": "one-hot inference: 8 bf16 tables of 50M x 128 (102.4 GB), B=65536, N=9",
-                   "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "bf16",
-                   "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
-        "inference": summ,
-    }
-    print(json.dumps(res), flush=True)
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rotate", type=int, default=8)
-    ap.add_argument("--cpu-samples", type=int, default=16384)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--overlap-plan", action="store_true",
-                    help="headline the step form with the backward's sort on a second stream")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
-    ap.add_argument("--dist", choices=["zipf", "uniform"], default="zipf",
-                    help="row distribution of the lookups (uniform: a cache-cold control)")
-    ap.add_argument("--workload", choices=["multihot", "onehot-big"], default="multihot",
-                    help="multihot: the training step (default); onehot-big: inference only "
-                         "(fused lookup + interaction against the two calls) on 8 x 50M-row "
-                         "bf16 tables, B=65536 one-hot, uniform or --dist zipf (Zipf 1.2)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
-              f"single-GPU: tables are not sharded and no collective runs).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    if args.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy probe: 3 copies of 1 GiB")
-        return
     from recommendation_model_sparse_amd import (DLRM_OPT_ADAGRAD, AdagradOutputs, dlrm_interact_bwd,
-                                                 dlrm_interact_fwd, dlrm_synth_fill_table, dlrm_trace_enable,
-                                                 dlrm_trace_read, emb_bag_bwd_adagrad, emb_bag_bwd_apply,
-                                                 emb_bag_bwd_plan, emb_bag_bwd_workspace_size, emb_bag_fwd,
-                                                 synth)
+                                                 dlrm_interact_fwd, emb_bag_bwd_adagrad, emb_bag_bwd_apply,
+                                                 emb_bag_bwd_plan, emb_bag_bwd_workspace_size, emb_bag_fwd)
     from recommendation_model_sparse_amd.configs import make_config
 
-    dev = torch.device("cuda:0")
-    if args.workload == "onehot-big":
-        return bench_inference_big(args, dev)
     wl = make_config(3)
-    if args.dist == "uniform":
-        wl = wl.with_(dist="uniform")
     log(f"[bench] workload {wl.name}: {wl.note}")
     t0 = time.time()
-    tabs = []
-    for t, v in enumerate(wl.rows):
-        x = torch.empty((v, wl.D), dtype=torch.bfloat16, device=dev)
-        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
-        tabs.append(x)
+    tabs = device_tables(wl, dev)
     states = [torch.zeros(v, dtype=torch.float32, device=dev) for v in wl.rows]
     torch.cuda.synchronize()
     log(f"[bench] tables {wl.table_bytes() / 1e9:.2f} GB filled in {time.time() - t0:.1f}s")
-
-    batches, host_batches = [], []
-    for i in range(args.rotate):
-        b = wl.batch(i)
-        host_batches.append(b)
-        batches.append(dict(idx=torch.from_numpy(b.indices).to(dev),
-                            off=torch.from_numpy(b.offsets).to(dev),
-                            dense=torch.from_numpy(b.dense).to(dev),
-                            g=torch.from_numpy(b.grad_out()).to(dev), nnz=b.nnz))
-        log(f"[bench] batch {i}: nnz={b.nnz}")
+    batches, host_batches = device_batches(wl, dev, 1 if args.only == "multihot-uniform" else args.rotate,
+                                           grads=True)
+    for i, b in enumerate(batches):
+        log(f"[bench] batch {i}: nnz={b['nnz']}")
     max_nnz = max(b["nnz"] for b in batches)
     ws = torch.empty(emb_bag_bwd_workspace_size(wl.rows, wl.D, wl.B, max_nnz), dtype=torch.uint8, device=dev)
     outs = AdagradOutputs(max_nnz, dev)
@@ -399,6 +419,11 @@ def main():
         emb_bag_bwd_apply(tabs, states, wl.B, b["nnz"], False, gpooled, DLRM_OPT_ADAGRAD, wl.lr, wl.eps, ws,
                           outputs=outs)
 
+    if args.only == "multihot-uniform":
+        # the uniform control alone (its counter profile must hold no Zipf launches)
+        uni, gat_u = bench_multihot_uniform(wl, dev, args, tabs, states, ws, outs, pooled, inter, gdense, gpooled)
+        return None, None, uni, gat_u, None
+
     def timed(fn):
         """Whole-step wall clock over args.steps steps between two synchronisations (ms/step)."""
         torch.cuda.synchronize()
@@ -412,6 +437,12 @@ def main():
         step(i)
         step_overlap(i)
     torch.cuda.synchronize()
+    if not args.overlap_plan:
+        # the two-stream form (timed beside the headline, for the record) settles only after a few
+        # dozen steps: its first ones ran near 3 times slower (3.3 against 1.19 ms) on the GPU
+        for i in range(30):
+            step_overlap(i)
+        torch.cuda.synchronize()
 
     # timed region: the step as configured; the other form timed beside it for the record
     headline = step_overlap if args.overlap_plan else step
@@ -432,33 +463,29 @@ def main():
     log("[bench] per call (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in call_ms.items()))
 
     # per-kernel HIP event times recorded by the library itself (dlrm_trace_*), third region
-    dlrm_trace_enable(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    trace = dlrm_trace_read()
-    dlrm_trace_enable(False)
-    kern_ms = {k: ms / args.steps for k, (n, ms) in trace.items()}  # per step
-    kern_launch_ms = {k: ms / n for k, (n, ms) in trace.items()}    # per launch
+    kern = traced(step, len(batches), args.steps)
+    kern_ms = {k: v["ms_per_call"] for k, v in kern.items()}  # per step
+    kern_launch_ms = {k: v["ms_per_launch"] for k, v in kern.items()}
     log("[bench] per kernel (ms/step): " + ", ".join(f"{k}={v:.4f}" for k, v in
                                                      sorted(kern_ms.items(), key=lambda x: -x[1])))
+    extras = {}
+    if args.only is None:
+        # inference: the fused lookup + interaction against the two calls, same batches and tables
+        extras["inference"] = inference_summary(time_inference(tabs, batches, args.steps, pooled, inter), wl,
+                                                float(np.mean([b["nnz"] for b in batches])))
+        extras["variants"] = time_variants(tabs, states, batches, args.steps, ws, outs, gpooled, wl)
+        extras["full_step"] = time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz)
 
-    # inference: the fused lookup + interaction against the two calls, same batches and tables
-    inf = time_inference(tabs, batches, args.steps, pooled, inter)
-    variants = time_variants(tabs, states, batches, args.steps, ws, outs, gpooled, wl)
-    full = time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz)
-
-    hbm = hbm_context(dev)
     nnz_avg = float(np.mean([b["nnz"] for b in batches]))
     U_last = int(outs.num_unique.item())
     es = wl.elem_size
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
-    gathered = nnz_avg * D * es
+    gathered, alg_lookup = lookup_bytes(wl, nnz_avg)
     sort_passes = round(kern_ms.get("radix_scatter", 0.0) / kern_launch_ms["radix_scatter"]) \
         if kern_launch_ms.get("radix_scatter") else 0
     # algorithmic bytes per launch of the main kernels
     alg = {
-        "pool_wave_per_bag": gathered + nnz_avg * 8 + (T * B + 1) * 8 + B * T * D * 4,
+        "pool_wave_per_bag": alg_lookup,
         # sorted key + grad-row index per lookup, each pooled-gradient row once (the kernel reads
         # it once per lookup: the re-reads are served by L2 / Infinity Cache or count in traffic),
         # each touched table row read and written, its state read and written
@@ -481,12 +508,10 @@ def main():
             gbps = b_alg / (kern_launch_ms[k] / 1e3) / 1e9
             kernels[k] = {"ms_per_launch": kern_launch_ms[k], "ms_per_step": kern_ms[k],
                           "algorithmic_bytes": b_alg, "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
-    dominant = max(kern_ms, key=lambda k: kern_ms[k])
-    dom = kernels.get(dominant)
-    k1_s = call_ms["emb_bag_fwd"] / 1e3
-    gathered_gbps = gathered / k1_s / 1e9
-
-    traffic = measured_traffic(dominant, "multihot-bf16-" + args.dist)
+    dom = max(kern_ms, key=lambda k: kern_ms[k])
+    dk = kernels.get(dom)
+    traffic = measured_traffic(dom, "multihot-bf16-zipf")
+    lk = lookup_kernel(kern)
     res = {
         "metric": "samples/sec + gathered-embedding GB/s (fraction of HBM peak), 1 MI355X",
         "value": wl.B / (ms / 1e3),
@@ -502,41 +527,311 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": f"synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), {args.dist} rows)",
+        "data": "synthetic (seeded; counter-hash tables U(+-1/sqrt(V)), zipf rows)",
         "config": {"workload": "multi-hot bf16 training step: 26 tables, D=128, B=16384, "
-                               "bag length truncated-geometric [1,100] mean 20, "
-                               + ("Zipf(1.05)" if args.dist == "zipf" else "uniform") +
-                               " rows, V log-uniform [1e3,1e7]",
+                               "bag length truncated-geometric [1,100] mean 20, Zipf(1.05) rows, "
+                               "V log-uniform [1e3,1e7]",
                    "global_batch": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "bf16", "nnz_avg": nnz_avg,
                    "table_GB": wl.table_bytes() / 1e9, "parallelism": "single GPU"},
-        "gathered_GBps": gathered_gbps,
-        "gathered_frac_of_hbm_peak": gathered_gbps / HBM_PEAK_GBPS,
-        "hbm_context": hbm,
+        # rows gathered per second by the lookup: logical bytes, mostly served by L2 and the
+        # Infinity Cache at Zipf(1.05); the HBM bytes the counters saw are in gather[...]
+        "gathered_GBps": gathered / (call_ms["emb_bag_fwd"] / 1e3) / 1e9,
+        "gathered_logical_frac_of_hbm_peak": gathered / (call_ms["emb_bag_fwd"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "step_ms_per_step_events": step_pct,
         "fwd_samples_per_s": wl.B / ((call_ms["emb_bag_fwd"] + call_ms["dlrm_interact_fwd"]) / 1e3),
         "unique_rows": U_last,
         "call_ms": call_ms,
         "kernel_ms_per_step": kern_ms,
-        "roofline": {"bound": "hbm", "kernel": dominant,
-                     "achieved": dom["GBps"] if dom else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom["frac_hbm_peak"] if dom else None,
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": dk["GBps"] if dk else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dk["frac_hbm_peak"] if dk else None,
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_read_write": [traffic["read"], traffic["write"]] if traffic else None,
                      # the bytes the counters saw per launch over the launch time: how hard the kernel
                      # drives HBM / the Infinity Cache, re-reads included
-                     "traffic_GBps": traffic["bytes"] / (kern_launch_ms[dominant] / 1e3) / 1e9 if traffic else None,
-                     "ms_per_launch": kern_launch_ms[dominant],
-                     "requested_bytes_per_launch": requested.get(dominant),
-                     "algorithmic_bytes_per_launch": dom["algorithmic_bytes"] if dom else None},
+                     "traffic_GBps": traffic["bytes"] / (kern_launch_ms[dom] / 1e3) / 1e9 if traffic else None,
+                     "ms_per_launch": kern_launch_ms[dom],
+                     "requested_bytes_per_launch": requested.get(dom),
+                     "algorithmic_bytes_per_launch": dk["algorithmic_bytes"] if dk else None},
         "kernels": kernels,
-        "inference": inference_summary(inf, wl, nnz_avg),
-        "variants": variants,
-        "full_step": full,
     }
-    if not args.no_cpu:
+    res.update(extras)
+    gat = gather_entry(wl, "multihot-bf16-zipf", lk, kern_launch_ms[lk], nnz_avg)
+
+    # the same step with uniform rows: the cache-cold control of the lookup and the backward
+    uni = gat_u = None
+    if args.only is None:
+        uni, gat_u = bench_multihot_uniform(wl, dev, args, tabs, states, ws, outs, pooled, inter, gdense, gpooled)
+    cpu = None
+    if args.only is None and not args.no_cpu:
         log(f"[bench] cpu baseline on {args.cpu_samples} samples ...")
-        res["cpu_baseline"] = cpu_baseline(wl, host_batches, args.cpu_samples)
-    print(json.dumps(res), flush=True)
+        cpu = cpu_baseline(wl, host_batches, args.cpu_samples)
+    del tabs, states, ws
+    torch.cuda.empty_cache()
+    return res, gat, uni, gat_u, cpu
+
+
+def bench_multihot_uniform(wl3, dev, args, tabs, states, ws, outs, pooled, inter, gdense, gpooled):
+    """The multi-hot step on the same tables with uniform rows (4 batches): lookup alone and the step."""
+    import torch
+    from recommendation_model_sparse_amd import (dlrm_interact_bwd, dlrm_interact_fwd, emb_bag_bwd_adagrad,
+                                                 emb_bag_fwd)
+    wl = wl3.with_(dist="uniform")
+    batches, _ = device_batches(wl, dev, min(args.rotate, 4), grads=True)
+    nb = len(batches)
+    if max(b["nnz"] for b in batches) > outs.unique_keys.numel():
+        from recommendation_model_sparse_amd import AdagradOutputs, emb_bag_bwd_workspace_size
+        n = max(b["nnz"] for b in batches)
+        outs = AdagradOutputs(n, dev)
+        ws = torch.empty(emb_bag_bwd_workspace_size(wl.rows, wl.D, wl.B, n), dtype=torch.uint8, device=dev)
+
+    def look(i):
+        b = batches[i]
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+
+    def step(i):
+        b = batches[i]
+        look(i)
+        dlrm_interact_fwd(b["dense"], pooled, out=inter)
+        dlrm_interact_bwd(b["g"], b["dense"], pooled, grad_dense=gdense, grad_pooled=gpooled)
+        emb_bag_bwd_adagrad(tabs, states, b["idx"], b["off"], None, gpooled, wl.lr, wl.eps, workspace=ws,
+                            outputs=outs)
+
+    for i in range(2):
+        step(i % nb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % nb)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    ms_look = ev_ms(look, nb, args.steps)
+    kern = traced(step, nb, args.steps)
+    nnz = float(np.mean([b["nnz"] for b in batches]))
+    lk = lookup_kernel(kern)
+    gathered, _ = lookup_bytes(wl, nnz)
+    res = {"workload": "multi-hot bf16 step (the headline's shapes and tables) with uniform rows",
+           "ms_per_step": ms_step, "samples_per_s": wl.B / (ms_step / 1e3), "lookup_ms": ms_look,
+           "lookup_gathered_GBps": gathered / (ms_look / 1e3) / 1e9, "unique_rows": int(outs.num_unique.item()),
+           "kernels": kern}
+    return res, gather_entry(wl, "multihot-bf16-uniform", lk, kern[lk]["ms_per_launch"], nnz)
+
+
+# ---------------------------------------------------------------- headline extras (inference, variants, full step)
+
+def time_inference(tabs, batches, steps, pooled, inter):
+    """Mean ms of emb_bag_interact_fwd and of emb_bag_fwd + dlrm_interact_fwd (HIP events)."""
+    from recommendation_model_sparse_amd import dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
+
+    def fused(i):
+        b = batches[i]
+        emb_bag_interact_fwd(tabs, b["idx"], b["off"], None, b["dense"], out=inter)
+
+    def two(i):
+        b = batches[i]
+        emb_bag_fwd(tabs, b["idx"], b["off"], None, out=pooled)
+        dlrm_interact_fwd(b["dense"], pooled, out=inter)
+
+    return {"fused": ev_ms(fused, len(batches), steps, 3), "two_call": ev_ms(two, len(batches), steps, 3)}
+
+
+def inference_summary(inf, wl, nnz_avg):
+    D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
+    alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
+    f = inf["fused"] / 1e3
+    return {"fused_ms": inf["fused"], "two_call_ms": inf["two_call"],
+            "fused_samples_per_s": B / f, "two_call_samples_per_s": B / (inf["two_call"] / 1e3),
+            "speedup": inf["two_call"] / inf["fused"],
+            "fused_algorithmic_bytes": alg, "fused_GBps": alg / f / 1e9,
+            "fused_frac_hbm_peak": alg / f / 1e9 / HBM_PEAK_GBPS,
+            "gathered_GBps": nnz_avg * D * wl.elem_size / f / 1e9}
+
+
+def time_variants(tabs, states, batches, steps, ws, outs, gpooled, wl):
+    """Mean ms (HIP events) of the path variants on the same batches: bf16 pooled output, int32
+    indices and offsets, the SGD backward (updates the tables in place), and the weighted lookup
+    and Adagrad backward with per-sample weights U(0,1) (seeded, one array per batch)."""
+    import torch
+    from recommendation_model_sparse_amd import (DLRM_OPT_SGD, emb_bag_bwd_adagrad, emb_bag_bwd_update,
+                                                 emb_bag_fwd, emb_bag_fwd_ex)
+
+    dev = tabs[0].device
+    b32 = [dict(idx=b["idx"].to(torch.int32), off=b["off"].to(torch.int32)) for b in batches]
+    pooled_bf16 = torch.empty((wl.B, wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    wts = [torch.rand(b["idx"].numel(), generator=gen, device=dev) for b in batches]
+    runs = {
+        "fwd_weighted": lambda i: emb_bag_fwd(tabs, batches[i]["idx"], batches[i]["off"], wts[i], out=pooled),
+        "bwd_adagrad_weighted": lambda i: emb_bag_bwd_adagrad(tabs, states, batches[i]["idx"], batches[i]["off"],
+                                                              wts[i], gpooled, wl.lr, wl.eps, workspace=ws,
+                                                              outputs=outs),
+        "fwd_bf16_out": lambda i: emb_bag_fwd_ex(tabs, batches[i]["idx"], batches[i]["off"], None, out=pooled_bf16,
+                                                 out_dtype=torch.bfloat16),
+        "fwd_int32_indices": lambda i: emb_bag_fwd_ex(tabs, b32[i]["idx"], b32[i]["off"], None, out=pooled),
+        "bwd_sgd": lambda i: emb_bag_bwd_update(tabs, None, batches[i]["idx"], batches[i]["off"], None, gpooled,
+                                                DLRM_OPT_SGD, wl.lr, 0.0, workspace=ws, outputs=outs),
+    }
+    return {name + "_ms": ev_ms(fn, len(batches), steps) for name, fn in runs.items()}
+
+
+def time_full_step(tabs, states, batches, host_batches, steps, wl, max_nnz):
+    """The full single-GPU DLRM training step around the sparse path: bottom MLP 13-512-256-128,
+    the lookup, the interaction, top MLP 480-1024-1024-512-256 and the sigmoid + BCE head, the
+    backward pass, SGD on the dense layers and row-wise Adagrad on the tables (HIP events)."""
+    import torch
+    from recommendation_model_sparse_amd.dlrm_step import DlrmStep
+
+    from recommendation_model_sparse_amd import dlrm_synth_fill_table, synth
+
+    dev = tabs[0].device
+    # start from the initial tables: the timed regions before this one updated them with
+    # synthetic upstream gradients, which are no training signal
+    for t, (x, v) in enumerate(zip(tabs, wl.rows)):
+        dlrm_synth_fill_table(x, t, wl.seed_tab(), float(synth.table_scale(v)))
+    for st in states:
+        st.zero_()
+    m = DlrmStep(tabs, states, wl.B, 13, bottom=[512, 256, wl.D], top=[1024, 1024, 512, 256], lr_dense=0.01,
+                 lr_emb=wl.lr, eps=wl.eps, seed=wl.seed + 99, max_nnz=max_nnz)
+    extra = [(torch.from_numpy(hb.features(13)).to(dev), torch.from_numpy(hb.labels()).to(dev)) for hb in host_batches]
+
+    def run(i):
+        b = batches[i % len(batches)]
+        x, y = extra[i % len(extra)]
+        m.step(b["idx"], b["off"], x, y)
+
+    def region(overlap):
+        m.overlap = overlap
+        return ev_ms(run, len(batches), steps)
+
+    ms_one = region(False)
+    ms = region(True)
+    dims_b = [(16, 512), (512, 256), (256, wl.D)]
+    dims_t = [(m.Ip, 1024), (1024, 1024), (1024, 512), (512, 256), (256, 1)]
+    flops = 3 * 2 * wl.B * sum(k * n for k, n in dims_b + dims_t)  # forward + two backward GEMMs
+    return {"ms_per_step": ms, "samples_per_s": wl.B / (ms / 1e3), "ms_per_step_one_stream": ms_one,
+            "dense_gemm_tflop_per_step": flops / 1e12,
+            "loss_after": float(m.head_out["loss"].item()),
+            "layers": "bottom 13(16)-512-256-128, top 480-1024-1024-512-256-1, bf16 GEMMs (hipBLASLt), fp32 accumulation"}
+
+
+# ---------------------------------------------------------------- streaming context
+
+def hbm_context(dev, steps: int):
+    """What plain streaming reaches on this GPU, as context for the kernels' figures: a 4 GiB
+    device-to-device copy (read + write bytes), and a 4 GiB read-only stream (dlrm_probe_read),
+    both far larger than the caches; HIP events, median of 5."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_probe_read
+    n = 1 << 30  # 4 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+
+    def med(fn):
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts[1:])) / 1e3
+
+    t_copy = med(lambda: dst.copy_(src))
+    t_read = med(lambda: dlrm_probe_read(src, sink))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * 4 * n / t_copy / 1e9, "read_GBps": 4 * n / t_read / 1e9, "bytes": 4 * n,
+            "how": "4 GiB fp32: device copy (read + write bytes over its time) and dlrm_probe_read "
+                   "(read-only stream, 16-byte loads); HIP events, median of 5"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--cpu-samples", type=int, default=16384)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--overlap-plan", action="store_true",
+                    help="headline the step form with the backward's sort on a second stream")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    ap.add_argument("--only", choices=SECTIONS, default=None,
+                    help="run one section and print its object (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
+              f"single-GPU: tables are not sharded and no collective runs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 3 copies of 1 GiB")
+        return
+    from recommendation_model_sparse_amd.configs import make_config
+
+    dev = torch.device("cuda:0")
+    only = args.only
+    out = {}
+    configs, gather = {}, {}
+    if only in (None, "headline", "multihot-uniform"):
+        res, gat, uni, gat_u, cpu = bench_headline(args, dev)
+        if only == "multihot-uniform":
+            print(json.dumps({"multihot_uniform": uni, "gather": gat_u}), flush=True)
+            return
+        if only == "headline":
+            print(json.dumps(dict(res, gather={"multihot-bf16-zipf": gat})), flush=True)
+            return
+        out = res
+        gather["multihot-bf16-zipf"] = gat
+        configs["multihot_bf16_uniform"] = uni
+        gather["multihot-bf16-uniform"] = gat_u
+    else:
+        cpu = None
+    ctx = {}
+    if only in (None, "tiny"):
+        r, g, _ = bench_forward(make_config(1), "tiny-f32", dev, args.steps, 1)
+        configs["tiny_f32"] = r
+    if only in (None, "onehot"):
+        r, g, _ = bench_forward(make_config(2), "onehot-f32-zipf", dev, args.steps, min(args.rotate, 4))
+        configs["onehot_f32"] = r
+        gather["onehot-f32-zipf"] = g
+    for dist in ("uniform", "zipf"):
+        name = f"bigtables-{dist}"
+        if only in (None, name):
+            wl4 = make_config(4)
+            if dist == "zipf":
+                wl4 = wl4.with_(dist="zipf", alpha=1.2)
+            r, g, probe = bench_forward(wl4, f"bigtables-bf16-{dist}", dev, args.steps, min(args.rotate, 4),
+                                        probe_gather=dist == "uniform")
+            configs[f"bigtables_bf16_{dist}"] = r
+            gather[f"bigtables-bf16-{dist}"] = g
+            if probe:
+                ctx["random_row_gather"] = probe
+    if only in (None, "train-onehot"):
+        configs["train_onehot_f32"] = bench_train_onehot(make_config(5), dev, args.steps, min(args.rotate, 4))
+    if only in (None, "probes"):
+        ctx.update(hbm_context(dev, args.steps))
+    if only is not None:
+        print(json.dumps({"configs": configs, "gather": gather, "hbm_context": ctx}), flush=True)
+        return
+    out["configs"] = configs
+    out["gather"] = gather
+    out["hbm_context"] = ctx
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

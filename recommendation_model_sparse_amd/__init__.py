@@ -26,6 +26,8 @@ from .binding import (  # noqa: F401
     DlrmError,
     dlrm_interact_bwd,
     dlrm_interact_fwd,
+    dlrm_probe_gather,
+    dlrm_probe_read,
     dlrm_status_string,
     dlrm_synth_fill_table,
     dlrm_trace_enable,
