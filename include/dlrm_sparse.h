@@ -265,6 +265,32 @@ int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *r
                       void *workspace, size_t workspace_bytes, const int64_t *segment_offsets,
                       dlrm_stream_t stream);
 
+/*
+ * Allocation-free embedding backward, for callers that cannot allocate device memory or hand the
+ * library a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It is emb_bag_bwd_update with the workspace taken from a fixed array of device
+ * memory the library holds on each GPU it runs on (emb_bag_bwd_noalloc_max_bytes() = 64 MiB,
+ * kept until the process ends); the results are emb_bag_bwd_update's, bit for bit.
+ *   Arguments: as emb_bag_bwd_update, without the workspace.
+ *   A batch whose workspace (emb_bag_bwd_workspace_size) exceeds the array is refused with
+ *   DLRM_ERR_WORKSPACE before anything is enqueued (at D = 128 about 1.1M lookups fit; the
+ *   one-hot training batch of 26 tables x 2048 samples needs 3 MB).
+ *   Every call on one GPU uses that GPU's single array: calls that overlap in time on one GPU
+ *   (two streams, two host threads) race, and the caller must order them.  The first call on a
+ *   device looks the array's address up there; no call allocates memory.
+ */
+int emb_bag_bwd_update_noalloc(void *const *tables, float *const *state, const int64_t *rows,
+                               int32_t T, int32_t D, int32_t dtype, const void *indices,
+                               const void *offsets, int32_t index_type,
+                               const float *per_sample_weights, int64_t B, int64_t nnz,
+                               const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                               int64_t *unique_keys_out, int64_t *segment_offsets_out,
+                               int32_t *sorted_pos_out, int64_t *num_unique_out, uint32_t flags,
+                               dlrm_stream_t stream);
+
+/* Bytes of the fixed device array emb_bag_bwd_update_noalloc works in. */
+size_t emb_bag_bwd_noalloc_max_bytes(void);
+
 /* Static description of a status code. */
 const char *dlrm_status_string(int status);
 

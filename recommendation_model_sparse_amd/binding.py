@@ -69,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.dlrm_status_string.argtypes = [ctypes.c_int]
         L.dlrm_status_string.restype = ctypes.c_char_p
         L.dlrm_synth_fill_table.argtypes = [p, i32, i64, i32, i32, u64, f32, p]
+        L.emb_bag_bwd_update_noalloc.argtypes = [p, p, p, i32, i32, i32, p, p, i32, p, i64, i64, p, i32, f32,
+                                                 f32, p, p, p, p, u32, p]
+        L.emb_bag_bwd_update_noalloc.restype = ctypes.c_int
+        L.emb_bag_bwd_noalloc_max_bytes.argtypes = []
+        L.emb_bag_bwd_noalloc_max_bytes.restype = sz
         L.dlrm_probe_read.argtypes = [p, u64, p, u32, p]
         L.dlrm_probe_gather.argtypes = [p, i64, i32, p, i64, p, u32, p]
         L.dlrm_trace_enable.argtypes = [ctypes.c_int]
@@ -380,6 +385,31 @@ def emb_bag_bwd_update(tables: Sequence[torch.Tensor], state: Optional[Sequence[
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
         _ptr(grad_pooled), int(optimizer), float(lr), float(eps), _ptr(workspace), workspace.numel(),
         *_out_ptrs(o), flags, _stream(dev)), "emb_bag_bwd_update")
+    return o
+
+
+def emb_bag_bwd_noalloc_max_bytes() -> int:
+    return int(lib().emb_bag_bwd_noalloc_max_bytes())
+
+
+def emb_bag_bwd_update_noalloc(tables: Sequence[torch.Tensor], state: Optional[Sequence[torch.Tensor]],
+                               indices: torch.Tensor, offsets: torch.Tensor,
+                               per_sample_weights: Optional[torch.Tensor], grad_pooled: torch.Tensor,
+                               optimizer: int, lr: float, eps: float = 0.0,
+                               outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
+    """emb_bag_bwd_update with the library's fixed per-GPU scratch as the workspace: allocates
+    nothing (C: emb_bag_bwd_update_noalloc).  Calls that overlap on one GPU race."""
+    T, D, code, ptrs, rows = _tables(tables)
+    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
+                                                (torch.int64, torch.int32))
+    _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
+    o = _outputs(outputs, nnz)
+    dev = _device(*tables, *(state or ()), indices, offsets, w, grad_pooled, *_out_tensors(o))
+    _check(lib().emb_bag_bwd_update_noalloc(
+        ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
+        _ptr(grad_pooled), int(optimizer), float(lr), float(eps), *_out_ptrs(o), flags, _stream(dev)),
+        "emb_bag_bwd_update_noalloc")
     return o
 
 

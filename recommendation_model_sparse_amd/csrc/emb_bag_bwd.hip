@@ -25,6 +25,8 @@
 //       queued on a worklist; K7b takes each listed segment with a whole block, reads its end
 //       from the segment offsets, adds the partials in chunk order and applies the update.
 //       Every sum has a fixed order, so the update is bitwise reproducible; no float atomics.
+#include <mutex>
+
 #include "common.h"
 
 namespace dlrm {
@@ -1361,4 +1363,79 @@ extern "C" int emb_bag_bwd_adagrad(void *const *tables, float *const *state, con
                               per_sample_weights, B, nnz, grad_pooled, DLRM_OPT_ADAGRAD, lr, eps,
                               workspace, workspace_bytes, unique_keys_out, segment_offsets_out,
                               sorted_pos_out, num_unique_out, flags, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+//
+// For callers that cannot allocate (code under graph capture, tight serving loops): the same
+// plan and update, with the workspace in a fixed array of device memory that the library owns.
+// Each GPU the library runs on holds its own copy of the array until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress gives on that device (the array's name
+// is a host-side stand-in, not a device address).  Calls that overlap on one GPU share the array
+// and race.
+
+namespace dlrm {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace dlrm
+
+static __device__ __align__(256) char scratch[dlrm::kScratchBytes];
+
+namespace dlrm {
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of the scratch array, looked up once per device with that device current.
+int scratch_on(hipStream_t stream, void **out) {
+    hipDevice_t dev = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return DLRM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DLRM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return DLRM_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return DLRM_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return DLRM_ERR_HIP;
+        if (e != hipSuccess || !p || !aligned(p, 256)) return DLRM_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DLRM_OK;
+}
+
+}  // namespace
+}  // namespace dlrm
+
+extern "C" size_t emb_bag_bwd_noalloc_max_bytes(void) { return dlrm::kScratchBytes; }
+
+extern "C" int emb_bag_bwd_update_noalloc(void *const *tables, float *const *state, const int64_t *rows,
+                                          int32_t T, int32_t D, int32_t dtype, const void *indices,
+                                          const void *offsets, int32_t index_type,
+                                          const float *per_sample_weights, int64_t B, int64_t nnz,
+                                          const float *grad_pooled, int32_t optimizer, float lr, float eps,
+                                          int64_t *unique_keys_out, int64_t *segment_offsets_out,
+                                          int32_t *sorted_pos_out, int64_t *num_unique_out, uint32_t flags,
+                                          dlrm_stream_t stream_) {
+    using namespace dlrm;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    // the batch and size checks first: a batch the scratch cannot hold is refused on the host
+    int rc = check_batch(const_cast<const void *const *>(tables), rows, T, D, dtype, indices, offsets, index_type,
+                         per_sample_weights, B, nnz);
+    if (rc != DLRM_OK) return rc;
+    int G, W;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    PlanShape ps;
+    rc = plan_shape(rows, T, D, nnz, &ps);
+    if (rc != DLRM_OK) return rc;
+    if (ps.L.total > kScratchBytes) return DLRM_ERR_WORKSPACE;
+    void *ws = nullptr;
+    rc = scratch_on(stream, &ws);
+    if (rc != DLRM_OK) return rc;
+    return emb_bag_bwd_update(tables, state, rows, T, D, dtype, indices, offsets, index_type, per_sample_weights, B,
+                              nnz, grad_pooled, optimizer, lr, eps, ws, kScratchBytes, unique_keys_out,
+                              segment_offsets_out, sorted_pos_out, num_unique_out, flags, stream_);
 }

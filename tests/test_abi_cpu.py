@@ -339,3 +339,18 @@ def test_probes_reject(L):
     assert g(FAKE, 10, 256, None, 4, FAKE, 8, None) == INVALID
     assert g(FAKE, 10, 256, FAKE, 1 << 31, FAKE, 8, None) == INVALID
     assert g(FAKE, 10, 256, FAKE, 0, FAKE, 8, None) == OK          # nothing to read
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch(L):
+    """The allocation-free backward sizes the batch on the host: one whose workspace exceeds the
+    fixed scratch is refused with DLRM_ERR_WORKSPACE before any device access."""
+    cap = binding.emb_bag_bwd_noalloc_max_bytes()
+    assert cap == 64 << 20
+    big = 4 << 20
+    assert binding.emb_bag_bwd_workspace_size([1000], 128, 1, big) > cap
+    rc = L.emb_bag_bwd_update_noalloc(ptrs(FAKE), ptrs(FAKE), i64s(1000), 1, 128, 0, FAKE, FAKE, 0, None, 1, big,
+                                      FAKE, 0, 0.01, 1e-8, None, None, None, None, 0, None)
+    assert rc == WORKSPACE
+    # the ordinary argument checks come first
+    assert L.emb_bag_bwd_update_noalloc(ptrs(FAKE), ptrs(FAKE), i64s(1000), 1, 24, 0, FAKE, FAKE, 0, None, 1, 4,
+                                        FAKE, 0, 0.01, 1e-8, None, None, None, None, 0, None) == UNSUPPORTED
