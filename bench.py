@@ -126,6 +126,22 @@ def lookup_kernel(kern: dict) -> str:
     return dominant(pools) if pools else dominant(kern)
 
 
+def gpu_spinup(dev, seconds: float = 0.3) -> float:
+    """Bring the GPU to its working clock before anything is timed: an idle MI355X starts near
+    200 MHz and ramps up over the first ~0.1 s of load, so the first steps of a run take close to
+    3 times longer.  Plain 256 MB device copies until `seconds` have passed; returns the time spent."""
+    import torch
+    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    del src, dst
+    return time.perf_counter() - t0
+
+
 # ---------------------------------------------------------------- inputs
 
 def device_tables(wl, dev):
@@ -433,16 +449,19 @@ def bench_headline(args, dev):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps * 1e3
 
+    # before the W warm-up steps: the GPU brought to its working clock, and 50 untimed steps of each
+    # step form, because once within a process's first few dozen steps the HIP runtime holds the
+    # host for ~35 ms inside a launch (measured: the GPU then idles and one region of 20 steps reads
+    # 2.8-3.6 ms/step instead of 1.15); neither is part of the step
+    spin = {"seconds": gpu_spinup(dev), "untimed_steps_per_form": 50}
+    for i in range(50):
+        step(i)
+        step_overlap(i)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
         step_overlap(i)
     torch.cuda.synchronize()
-    if not args.overlap_plan:
-        # the two-stream form (timed beside the headline, for the record) settles only after a few
-        # dozen steps: its first ones ran near 3 times slower (3.3 against 1.19 ms) on the GPU
-        for i in range(30):
-            step_overlap(i)
-        torch.cuda.synchronize()
 
     # timed region: the step as configured; the other form timed beside it for the record
     headline = step_overlap if args.overlap_plan else step
@@ -521,6 +540,7 @@ def bench_headline(args, dev):
         "warmup": args.warmup,
         "ms_per_step": ms,
         "step_form": "plan on a second stream" if args.overlap_plan else "one stream",
+        "spinup": spin,
         "ms_per_step_one_stream": ms_one,
         "ms_per_step_plan_overlapped": ms_ovl,
         "higher_is_better": True,

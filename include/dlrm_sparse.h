@@ -169,7 +169,10 @@ int emb_bag_interact_fwd(const void *const *tables, const int64_t *rows, int32_t
                          const float *dense, float *out, uint32_t flags, dlrm_stream_t stream);
 
 /* Bytes of device workspace emb_bag_bwd_adagrad needs for these sizes
- * (0 on invalid sizes).  rows is a host array of T row counts. */
+ * (0 on invalid sizes).  rows is a host array of T row counts.  D is an argument because part
+ * of the workspace scales with it: the segment sums that cross chunk boundaries are kept as fp32
+ * rows of D values, one or two per chunk, and the chunk length follows from D (a lane group of
+ * D/4 lanes walks each chunk). */
 size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int32_t D, int64_t B,
                                   int64_t nnz);
 
@@ -203,7 +206,11 @@ size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int32_t D, int
  *     segment_offsets_out [nnz+1] int64: first sorted position of each key; entry U = nnz
  *     sorted_pos_out      [nnz] int32: original position of each sorted position
  *     num_unique_out      [1] int64: U
- *   Limits: D a power of two in [4, 512] (bf16: [8, 512]).
+ *   Limits: D a power of two in [4, 512] (bf16: [8, 512]).  The segment sums run on lane
+ *   groups of D/4 lanes (D/8 at D = 512) that must tile the 64-lane wavefront exactly: the
+ *   group sums are DPP/permute trees inside the group, and segment starts are read from the
+ *   wave's ballot mask by group.  (The forward takes any row of a multiple of 16 bytes.)
+ *   Keys are 32-bit: the sum of rows must be at most 2^32.
  */
 int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows, int32_t T,
                         int32_t D, int32_t dtype, const int64_t *indices, const int64_t *offsets,

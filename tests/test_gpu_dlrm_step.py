@@ -9,7 +9,9 @@ enters it.  Each link of the chain, forward or backward, rounds one operand to b
 side, so a result k links from the exact inputs is compared norm-wise, ||gpu - oracle|| <= k * 2^-8
 ||oracle|| (the gradients of a link are bilinear in two operands that each carry their own depth;
 the larger is used).  Element-wise gates hold where the inputs are exact: the bf16 input rows bit
-for bit, the pooled rows within 1e-5 of their error scale, untouched table rows bit for bit.  The
+for bit, the first bottom layer's output (one GEMM and one bf16 rounding from exact inputs) within
+its fp32 accumulation bound plus the roundings, the pooled rows within 1e-5 of their error scale,
+untouched table rows bit for bit.  The
 isolated kernels are checked element-wise against the oracle on host inputs in test_gpu_mlp.py and
 test_gpu_parity.py; this test checks that the step wires them together.
 """
@@ -23,7 +25,7 @@ from recommendation_model_sparse_amd import AdagradOutputs, synth
 from recommendation_model_sparse_amd.dlrm_step import DlrmStep
 from recommendation_model_sparse_amd.synth import Workload, subset_tables
 
-from gpu_util import DEV, device_tables, rel_err, say, to_dev, to_host
+from gpu_util import DEV, bf16_half_ulp, device_tables, rel_err, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 E = 2.0 ** -8  # one bf16 rounding on each side
@@ -139,6 +141,14 @@ def test_full_training_step(overlap):
 
     # ---- forward
     assert np.array_equal(gpu["x0"], o.x0)
+    # the first layer is one GEMM and one bf16 rounding from exact inputs (x0 and W bit-equal on both
+    # sides): element-wise, the fp32 accumulation error gamma_K * scale plus the two roundings (half
+    # a bf16 ulp of each side's value)
+    W0, b0, _, _ = params[id(m.bottom[0])]
+    _, s0, _ = mlp.linear_fwd(o.x0, W0, b0, relu=True)
+    K0 = o.x0.shape[1]
+    gate0 = bf16_half_ulp(o.hb[0]) + bf16_half_ulp(gpu["hb"][0]) + (K0 + 2) * 2.0 ** -24 * s0  # K products and the bias
+    assert np.all(np.abs(gpu["hb"][0] - o.hb[0]) <= gate0)
     for i in range(len(m.bottom)):
         close(gpu["hb"][i], o.hb[i], i + 1, f"bottom layer {i}")
     assert rel_err(gpu["pooled"], o.pooled, o.pooled_scale) <= 1e-5

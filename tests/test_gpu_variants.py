@@ -2,7 +2,8 @@
 output (emb_bag_fwd_ex), and the SGD update (emb_bag_bwd_update).
 
 Gates: int32 runs are bit-identical to the int64 runs of the same batch (forward values, updated
-tables and states, integer outputs); the bf16 output is bit-identical to the round-to-nearest-even
+tables and states, integer outputs), and the int32 forward is also held to the oracle directly
+(1e-5, one-row bags exact); the bf16 output is bit-identical to the round-to-nearest-even
 of the fp32 output and within the bf16 gate (1e-2) of the oracle; SGD rows against the oracle as
 for Adagrad (fp32: per-row infinity-norm relative error <= 1e-4; bf16: half a bf16 ulp plus that),
 integer outputs bit-exact, untouched rows unchanged, every update bitwise reproducible.
@@ -59,7 +60,13 @@ def test_fwd_index_and_output_types(dtype, D, mode, weighted):
     assert np.array_equal(to_host(bf64), want), "bf16 output is not the RNE of the fp32 sums"
     assert np.array_equal(to_host(bf32), want)
     ref, scale = oracle.emb_bag_fwd(tables, idx, off, w, B)
+    # the int32 path against the oracle directly, at the fp32 gate (both table dtypes accumulate in
+    # fp32), besides its bit-identity with the int64 path above
+    assert rel_err(out32.cpu().numpy(), ref, scale) <= 1e-5
+    if mode == "onehot" and not weighted:  # a one-row bag is the row itself
+        assert np.array_equal(out32.cpu().numpy().astype(np.float64), ref)
     assert rel_err(synth.bf16_bits_to_f32(to_host(bf64)), ref, scale) <= 1e-2
+    assert rel_err(synth.bf16_bits_to_f32(to_host(bf32)), ref, scale) <= 1e-2
 
 
 def run_update(rows, D, dtype, B, lengths, weighted, seed, opt, index32, max_len=12, hot=None, lr=0.01,
