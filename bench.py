@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 SECTIONS = ("headline", "tiny", "onehot", "multihot-uniform", "bigtables-uniform", "bigtables-zipf",
-            "train-onehot", "probes")
+            "train-onehot", "probes", "interaction")
 
 
 def traffic_profile(workload: str) -> str:
@@ -265,6 +265,34 @@ def bench_forward(wl, workload: str, dev, steps: int, rotate: int, probe_gather:
     del tabs
     torch.cuda.empty_cache()
     return res, gat, extra
+
+
+# ---------------------------------------------------------------- the interaction's Gram paths
+
+def bench_interaction_paths(dev, steps: int):
+    """dlrm_interact_fwd_ex on each Gram path (the automatic choice, the fp32 matrix-core Gram, the
+    LDS-staged VALU Gram) at the multi-hot shape (N=27, D=128, B=16384) and the big-table shape
+    (N=9, D=128, B=65536), on seeded N(0,1) inputs resident in HBM; HIP events."""
+    import torch
+    from recommendation_model_sparse_amd import (DLRM_GRAM_AUTO, DLRM_GRAM_MFMA, DLRM_GRAM_VALU,
+                                                 dlrm_interact_fwd_ex)
+    res = {}
+    gen = torch.Generator(device=dev).manual_seed(20261227)
+    for name, N, D, B in (("multihot_N27", 27, 128, 16384), ("bigtables_N9", 9, 128, 65536)):
+        dense = torch.randn((B, D), generator=gen, device=dev)
+        pooled = torch.randn((B, N - 1, D), generator=gen, device=dev)
+        P = N * (N - 1) // 2
+        out = torch.empty((B, P + D), device=dev)
+        alg = B * (N * D * 4 + (P + D) * 4)
+        r = {"N": N, "D": D, "B": B, "algorithmic_bytes": alg, "gflop": 2.0 * D * P * B / 1e9}
+        for pname, path in (("auto", DLRM_GRAM_AUTO), ("mfma", DLRM_GRAM_MFMA), ("valu_lds", DLRM_GRAM_VALU)):
+            ms = ev_ms(lambda i: dlrm_interact_fwd_ex(dense, pooled, path, out=out), 1, steps, 3)
+            r[pname] = {"ms": ms, "GBps": alg / (ms / 1e3) / 1e9, "TFLOPs": 2.0 * D * P * B / (ms / 1e3) / 1e12}
+        res[name] = r
+        log(f"[bench] interaction {name}: " + ", ".join(f"{k} {r[k]['ms'] * 1e3:.1f} us" for k in
+                                                        ("auto", "mfma", "valu_lds")))
+        del dense, pooled, out
+    return res
 
 
 # ---------------------------------------------------------------- the fp32 training step
@@ -843,6 +871,8 @@ def main():
         configs["train_onehot_f32"] = bench_train_onehot(make_config(5), dev, args.steps, min(args.rotate, 4))
     if only in (None, "probes"):
         ctx.update(hbm_context(dev, args.steps))
+    if only in (None, "interaction"):
+        configs["interaction_paths"] = bench_interaction_paths(dev, args.steps)
     if only is not None:
         print(json.dumps({"configs": configs, "gather": gather, "hbm_context": ctx}), flush=True)
         return

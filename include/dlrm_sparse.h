@@ -131,6 +131,24 @@ int emb_bag_fwd_ex(const void *const *tables, const int64_t *rows, int32_t T, in
 int dlrm_interact_fwd(const float *dense, const float *pooled, int64_t B, int32_t N, int32_t D,
                       float *out, dlrm_stream_t stream);
 
+/* Gram path of dlrm_interact_fwd_ex. */
+enum { DLRM_GRAM_AUTO = 0, DLRM_GRAM_MFMA = 1, DLRM_GRAM_VALU = 2 };
+
+/*
+ * dlrm_interact_fwd with the kernel chosen by the caller, for measuring one Gram path against the
+ * other on the same shapes.  Same output, same arguments, plus:
+ *   path  DLRM_GRAM_AUTO: dlrm_interact_fwd's own choice (the k-split VALU Gram for N <= 11 and
+ *           D in {64, 128, 256}, else the fp32 matrix-core Gram);
+ *         DLRM_GRAM_MFMA: the matrix-core Gram (v_mfma_f32_16x16x4_f32) for every N
+ *           (DLRM_ERR_UNSUPPORTED where D is not a multiple of 16 or above 512);
+ *         DLRM_GRAM_VALU: the plain-VALU Gram with X staged in LDS and 2x2 register tiles of dots
+ *           (D a multiple of 16 and N*(D+4)*4 <= 64 KiB, else DLRM_ERR_UNSUPPORTED).
+ * Each path sums every dot in fp32; the paths add the D products in different orders, so their
+ * results agree to rounding, not bit for bit.
+ */
+int dlrm_interact_fwd_ex(const float *dense, const float *pooled, int64_t B, int32_t N, int32_t D,
+                         float *out, int32_t path, dlrm_stream_t stream);
+
 /*
  * Dot-product interaction, backward: the derivative of dlrm_interact_fwd
  * (the pages give the forward map and say it is trained by gradient descent,

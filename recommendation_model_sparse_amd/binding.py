@@ -21,6 +21,7 @@ DLRM_INDEX_I64, DLRM_INDEX_I32 = 0, 1
 DLRM_OPT_ADAGRAD, DLRM_OPT_SGD = 0, 1
 DLRM_ACT_NONE, DLRM_ACT_RELU = 0, 1
 DLRM_FLAG_CHECK_INDICES = 1
+DLRM_GRAM_AUTO, DLRM_GRAM_MFMA, DLRM_GRAM_VALU = 0, 1, 2
 
 _lib = None
 
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.emb_bag_bwd_plan.argtypes = [p, i32, i32, p, p, i32, p, i64, i64, p, sz, p, p, p, p, u32, p]
         L.emb_bag_bwd_apply.argtypes = [p, p, p, i32, i32, i32, i64, i64, i32, p, i32, f32, f32, p, sz, p, p]
         L.dlrm_interact_fwd.argtypes = [p, p, i64, i32, i32, p, p]
+        L.dlrm_interact_fwd_ex.argtypes = [p, p, i64, i32, i32, p, i32, p]
+        L.dlrm_interact_fwd_ex.restype = ctypes.c_int
         L.emb_bag_interact_fwd.argtypes = [p, p, i32, i32, i32, p, p, p, i64, i64, p, p, u32, p]
         L.dlrm_interact_bwd.argtypes = [p, p, p, i64, i32, i32, p, p, p]
         L.emb_bag_bwd_workspace_size.argtypes = [i32, p, i32, i64, i64]
@@ -274,6 +277,19 @@ def dlrm_interact_fwd(dense: torch.Tensor, pooled: torch.Tensor,
         out = torch.empty((B, P + D), dtype=torch.float32, device=dev)
     _check(lib().dlrm_interact_fwd(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out),
                                    _stream(dev)), "dlrm_interact_fwd")
+    return out
+
+
+def dlrm_interact_fwd_ex(dense: torch.Tensor, pooled: torch.Tensor, path: int = DLRM_GRAM_AUTO,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dlrm_interact_fwd with the Gram path chosen: DLRM_GRAM_AUTO, _MFMA or _VALU (C: dlrm_interact_fwd_ex)."""
+    B, N, D, P = _interaction_shapes(dense, pooled)
+    out = _opt(out, "out", torch.float32, (B, P + D))
+    dev = _device(dense, pooled, out)
+    if out is None:
+        out = torch.empty((B, P + D), dtype=torch.float32, device=dev)
+    _check(lib().dlrm_interact_fwd_ex(_ptr(dense), _ptr(pooled), B, N, D, _ptr(out), int(path), _stream(dev)),
+           "dlrm_interact_fwd_ex")
     return out
 
 

@@ -240,6 +240,71 @@ __global__ __launch_bounds__(256) void k_interact_fwd_valu(const float *__restri
     for (int d = threadIdx.x; d < D; d += blockDim.x) orow[P + d] = dsrc[d];
 }
 
+// The plain-VALU contender of the matrix-core Gram (selected by dlrm_interact_fwd_ex): the X of S
+// samples staged in LDS with contiguous 16-byte loads, rows padded by 4 floats; each thread then
+// computes a TILE x TILE block of dots of one sample, an FMA chain over d in order, with its
+// 2*TILE operand rows read from LDS.  Blocks (I, J) with I <= J cover the upper triangle.
+template <int TILE>
+__global__ __launch_bounds__(256) void k_interact_fwd_lds(const float *__restrict__ dense,
+                                                          const float *__restrict__ pooled,
+                                                          float *__restrict__ out, uint32_t B, int N, int D,
+                                                          int P, int S) {
+    extern __shared__ float xs[];  // [S][N][D + 4]
+    const int LD = D + 4, D4 = D / 4;
+    const uint32_t b0 = blockIdx.x * S;
+    const int ns = static_cast<int>(min(static_cast<uint32_t>(S), B - b0));
+    for (int q = threadIdx.x; q < ns * N * D4; q += blockDim.x) {
+        const int sm = q / (N * D4), rem = q - sm * (N * D4), i = rem / D4, d4 = rem - i * D4;
+        const float4 v = *reinterpret_cast<const float4 *>(x_row(dense, pooled, b0 + sm, N, D, i) + d4 * 4);
+        *reinterpret_cast<float4 *>(xs + (sm * N + i) * LD + d4 * 4) = v;
+    }
+    __syncthreads();
+    const int NT = (N + TILE - 1) / TILE;
+    const int tiles = NT * (NT + 1) / 2;
+    for (int q = threadIdx.x; q < ns * tiles; q += blockDim.x) {
+        const int sm = q / tiles;
+        int t = q - sm * tiles, I = 0;
+        while (t >= NT - I) t -= NT - I, ++I;
+        const int J = I + t;
+        const float *xi = xs + (sm * N + I * TILE) * LD, *xj = xs + (sm * N + J * TILE) * LD;
+        float acc[TILE][TILE];
+#pragma unroll
+        for (int a = 0; a < TILE; ++a)
+#pragma unroll
+            for (int c = 0; c < TILE; ++c) acc[a][c] = 0.f;
+        for (int d = 0; d < D; d += 4) {
+            float4 u[TILE], v[TILE];
+#pragma unroll
+            for (int a = 0; a < TILE; ++a) {  // rows past N read row N-1's slot and are never stored
+                u[a] = *reinterpret_cast<const float4 *>(xi + min(a, N - 1 - I * TILE) * LD + d);
+                v[a] = *reinterpret_cast<const float4 *>(xj + min(a, N - 1 - J * TILE) * LD + d);
+            }
+#pragma unroll
+            for (int a = 0; a < TILE; ++a)
+#pragma unroll
+                for (int c = 0; c < TILE; ++c) {
+                    acc[a][c] = fmaf(u[a].x, v[c].x, acc[a][c]);
+                    acc[a][c] = fmaf(u[a].y, v[c].y, acc[a][c]);
+                    acc[a][c] = fmaf(u[a].z, v[c].z, acc[a][c]);
+                    acc[a][c] = fmaf(u[a].w, v[c].w, acc[a][c]);
+                }
+        }
+        float *orow = out + static_cast<uint64_t>(b0 + sm) * (P + D);
+#pragma unroll
+        for (int a = 0; a < TILE; ++a)
+#pragma unroll
+            for (int c = 0; c < TILE; ++c) {
+                const int i = I * TILE + a, j = J * TILE + c;
+                if (i < j && j < N) orow[triu_pos(i, j, N)] = acc[a][c];
+            }
+    }
+    // the dense vector after the dots
+    for (int q = threadIdx.x; q < ns * D; q += blockDim.x) {
+        const int sm = q / D, d = q - sm * D;
+        out[static_cast<uint64_t>(b0 + sm) * (P + D) + P + d] = xs[sm * N * LD + d];
+    }
+}
+
 // Small interactions (N <= 11, D = 64 * CPL): the k-split Gram (gram.h) over NR = gram_rows(N)
 // rows, M samples per wave.  Lane l loads columns l*CPL.. of every row (each row read is one
 // coalesced load), and every load is unconditional (rows past N re-read row N-1 and are zeroed)
@@ -444,20 +509,37 @@ int check_interact(const void *a, const void *b, const void *c, int64_t B, int32
 }  // namespace
 }  // namespace dlrm
 
-extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_t B, int32_t N,
-                                 int32_t D, float *out, dlrm_stream_t stream_) {
-    using namespace dlrm;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+namespace dlrm {
+namespace {
+
+// Samples per block of the LDS kernel: enough 2x2 tiles for the block's 256 threads, within 64 KiB.
+int lds_samples(int N, int D) {
+    const int NT = (N + 1) / 2, tiles = NT * (NT + 1) / 2;
+    const int bytes = N * (D + 4) * 4;
+    int S = (256 + tiles - 1) / tiles;
+    while (S > 1 && S * bytes > 64 * 1024) --S;
+    return S;
+}
+
+int interact_fwd_impl(const float *dense, const float *pooled, int64_t B, int32_t N, int32_t D, float *out,
+                      int32_t path, hipStream_t stream) {
     int rc = check_interact(dense, pooled, out, B, N, D);
     if (rc != DLRM_OK || B == 0) return rc;
     const int P = N * (N - 1) / 2;
     const uint32_t b = static_cast<uint32_t>(B);
-    bool done = false;
-    if (gram_ksplit_ok(N, D)) {
+    if (path == DLRM_GRAM_VALU) {
+        if (N < 2 || D % 16 != 0 || N * (D + 4) * 4 > 64 * 1024) return DLRM_ERR_UNSUPPORTED;
+        const int S = lds_samples(N, D);
+        DLRM_LAUNCH("interact_fwd_lds", k_interact_fwd_lds<2>, dim3((b + S - 1) / S), dim3(256),
+                    static_cast<size_t>(S) * N * (D + 4) * 4, stream, dense, pooled, out, b, N, D, P, S);
+        return launch_status();
+    }
+    if (path == DLRM_GRAM_AUTO && gram_ksplit_ok(N, D)) {
         if (gram_rows(N) == 9) launch_fwd_ksplit<9>(dense, pooled, out, b, N, D, P, stream);
         else launch_fwd_ksplit<11>(dense, pooled, out, b, N, D, P, stream);
         return launch_status();
     }
+    bool done = false;
     switch ((N + 15) / 16) {
         case 1: done = launch_fwd_mfma<1>(dense, pooled, out, b, N, D, P, stream); break;
         case 2: done = launch_fwd_mfma<2>(dense, pooled, out, b, N, D, P, stream); break;
@@ -465,10 +547,27 @@ extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_
         case 4: done = launch_fwd_mfma<4>(dense, pooled, out, b, N, D, P, stream); break;
         case 5: done = launch_fwd_mfma<5>(dense, pooled, out, b, N, D, P, stream); break;
     }
-    if (!done)
+    if (!done) {
+        if (path == DLRM_GRAM_MFMA) return DLRM_ERR_UNSUPPORTED;
         DLRM_LAUNCH("interact_fwd_valu", k_interact_fwd_valu, dim3(b), dim3(256), 0, stream, dense, pooled, out,
-                           N, D, P);
+                    N, D, P);
+    }
     return launch_status();
+}
+
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_interact_fwd(const float *dense, const float *pooled, int64_t B, int32_t N,
+                                 int32_t D, float *out, dlrm_stream_t stream_) {
+    return dlrm::interact_fwd_impl(dense, pooled, B, N, D, out, DLRM_GRAM_AUTO,
+                                   reinterpret_cast<hipStream_t>(stream_));
+}
+
+extern "C" int dlrm_interact_fwd_ex(const float *dense, const float *pooled, int64_t B, int32_t N, int32_t D,
+                                    float *out, int32_t path, dlrm_stream_t stream_) {
+    if (path != DLRM_GRAM_AUTO && path != DLRM_GRAM_MFMA && path != DLRM_GRAM_VALU) return DLRM_ERR_INVALID_ARG;
+    return dlrm::interact_fwd_impl(dense, pooled, B, N, D, out, path, reinterpret_cast<hipStream_t>(stream_));
 }
 
 extern "C" int dlrm_interact_bwd(const float *grad_out, const float *dense, const float *pooled,

@@ -354,3 +354,14 @@ def test_noalloc_refuses_batches_beyond_its_scratch(L):
     # the ordinary argument checks come first
     assert L.emb_bag_bwd_update_noalloc(ptrs(FAKE), ptrs(FAKE), i64s(1000), 1, 24, 0, FAKE, FAKE, 0, None, 1, 4,
                                         FAKE, 0, 0.01, 1e-8, None, None, None, None, 0, None) == UNSUPPORTED
+
+
+def test_interact_fwd_ex_rejects(L):
+    f = L.dlrm_interact_fwd_ex
+    assert f(FAKE, FAKE, 4, 5, 16, FAKE, 3, None) == INVALID          # no such path
+    assert f(FAKE, FAKE, 4, 5, 16, FAKE, -1, None) == INVALID
+    assert f(FAKE, FAKE, 4, 200, 16, FAKE, 1, None) == INVALID        # N beyond 65
+    assert f(FAKE, FAKE, 4, 27, 1024, FAKE, 2, None) == UNSUPPORTED   # D above 512
+    assert f(FAKE, FAKE, 4, 27, 12, FAKE, 2, None) == UNSUPPORTED     # VALU: D not a multiple of 16
+    assert f(FAKE, FAKE, 4, 65, 256, FAKE, 2, None) == UNSUPPORTED    # VALU: one sample's X over 64 KiB
+    assert f(FAKE, FAKE, 0, 27, 128, FAKE, 2, None) == OK             # empty batch

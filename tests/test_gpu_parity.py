@@ -15,10 +15,13 @@ import torch
 import oracle
 from recommendation_model_sparse_amd import (
     DLRM_FLAG_CHECK_INDICES,
+    DLRM_GRAM_MFMA,
+    DLRM_GRAM_VALU,
     AdagradOutputs,
     DlrmError,
     dlrm_interact_bwd,
     dlrm_interact_fwd,
+    dlrm_interact_fwd_ex,
     emb_bag_bwd_adagrad,
     emb_bag_fwd,
 )
@@ -158,6 +161,34 @@ def test_interact_fwd_random(N, D):
     say(f"   max rel err {err:.3e}")
     assert err <= 1e-5
     assert np.array_equal(got[:, P:], dense)
+
+
+# each Gram path on its own (the matrix-core Gram at every N, the LDS-staged VALU Gram), against the
+# oracle; the batch leaves the VALU kernel's last block with fewer samples than the others
+@pytest.mark.parametrize("N", [2, 3, 9, 11, 17, 27, 32, 33, 65])
+@pytest.mark.parametrize("D", [16, 64, 128, 256])
+@pytest.mark.parametrize("path", [DLRM_GRAM_MFMA, DLRM_GRAM_VALU])
+def test_interact_fwd_paths(N, D, path):
+    rng = np.random.default_rng(N * 31 + D + path)
+    B = 37
+    dense = rng.standard_normal((B, D)).astype(np.float32)
+    pooled = rng.standard_normal((B, N - 1, D)).astype(np.float32)
+    if path == DLRM_GRAM_VALU and N * (D + 4) * 4 > 64 * 1024:
+        with pytest.raises(DlrmError) as e:
+            dlrm_interact_fwd_ex(to_dev(dense), to_dev(pooled), path)
+        assert e.value.status == -2
+        return
+    say(f"[interact_fwd path={path}] B={B} N={N} D={D}")
+    out = dlrm_interact_fwd_ex(to_dev(dense), to_dev(pooled), path)
+    out2 = dlrm_interact_fwd_ex(to_dev(dense), to_dev(pooled), path)
+    torch.cuda.synchronize()
+    assert bits_equal(out, out2)
+    got = out.cpu().numpy()
+    ref, scale = oracle.interact_fwd(dense, pooled)
+    err = rel_err(got, ref, scale)
+    say(f"   max rel err {err:.3e}")
+    assert err <= 1e-5
+    assert np.array_equal(got[:, N * (N - 1) // 2:], dense)
 
 
 # D = 128 with N <= 32 takes 1, 2 or 4 samples per wavefront by batch size (thresholds 3072 and
