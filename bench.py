@@ -24,7 +24,7 @@ The same JSON line also carries:
                     [--only SECTION]
 
 --only runs one section and prints its object (for profiling runs): headline, tiny, onehot,
-multihot-uniform, bigtables-uniform, bigtables-zipf, train-onehot, probes.
+multihot-uniform, bigtables-uniform, bigtables-zipf, train-onehot, probes, interaction, inference.
 """
 from __future__ import annotations
 
@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 SECTIONS = ("headline", "tiny", "onehot", "multihot-uniform", "bigtables-uniform", "bigtables-zipf",
-            "train-onehot", "probes", "interaction")
+            "train-onehot", "probes", "interaction", "inference")
 
 
 def traffic_profile(workload: str) -> str:
@@ -467,6 +467,12 @@ def bench_headline(args, dev):
         # the uniform control alone (its counter profile must hold no Zipf launches)
         uni, gat_u = bench_multihot_uniform(wl, dev, args, tabs, states, ws, outs, pooled, inter, gdense, gpooled)
         return None, None, uni, gat_u, None
+    if args.only == "inference":
+        # the fused lookup + interaction against the two calls alone (for its counter profiles)
+        gpu_spinup(dev)
+        inf = inference_summary(time_inference(tabs, batches, args.steps, pooled, inter), wl,
+                                float(np.mean([b["nnz"] for b in batches])))
+        return inf, None, None, None, None
 
     def timed(fn):
         """Whole-step wall clock over args.steps steps between two synchronisations (ms/step)."""
@@ -684,15 +690,28 @@ def time_inference(tabs, batches, steps, pooled, inter):
 
 
 def inference_summary(inf, wl, nnz_avg):
+    """Fused call against the two calls; with the counters' bytes past L2 per call of each form
+    (profiles/hbm_traffic_multihot_bf16_zipf_inference.md) while the kernels' sources match."""
     D, T, B, N, P = wl.D, wl.T, wl.B, wl.N, wl.P
     alg = nnz_avg * (D * wl.elem_size + 8) + (T * B + 1) * 8 + B * D * 4 + B * (P + D) * 4
     f = inf["fused"] / 1e3
-    return {"fused_ms": inf["fused"], "two_call_ms": inf["two_call"],
-            "fused_samples_per_s": B / f, "two_call_samples_per_s": B / (inf["two_call"] / 1e3),
-            "speedup": inf["two_call"] / inf["fused"],
-            "fused_algorithmic_bytes": alg, "fused_GBps": alg / f / 1e9,
-            "fused_frac_hbm_peak": alg / f / 1e9 / HBM_PEAK_GBPS,
-            "gathered_GBps": nnz_avg * D * wl.elem_size / f / 1e9}
+    out = {"fused_ms": inf["fused"], "two_call_ms": inf["two_call"],
+           "fused_samples_per_s": B / f, "two_call_samples_per_s": B / (inf["two_call"] / 1e3),
+           "speedup": inf["two_call"] / inf["fused"],
+           "fused_algorithmic_bytes": alg, "fused_GBps": alg / f / 1e9,
+           "fused_frac_hbm_peak": alg / f / 1e9 / HBM_PEAK_GBPS,
+           "gathered_GBps": nnz_avg * D * wl.elem_size / f / 1e9,
+           "fused_hbm_bytes": None, "two_call_hbm_bytes": None}
+    wkl = "multihot-bf16-zipf-inference"
+    tf = measured_traffic("emb_interact_fwd", wkl)
+    tp, ti = measured_traffic("pool_wave_per_bag", wkl), measured_traffic("interact_fwd_mfma_pipe", wkl)
+    if tf:
+        out["fused_hbm_bytes"] = tf["bytes"]
+        out["fused_hbm_GBps"] = tf["bytes"] / f / 1e9
+    if tp and ti:
+        out["two_call_hbm_bytes"] = tp["bytes"] + ti["bytes"]
+    out["counters"] = os.path.relpath(traffic_profile(wkl), ROOT)
+    return out
 
 
 def time_variants(tabs, states, batches, steps, ws, outs, gpooled, wl):
@@ -833,8 +852,11 @@ def main():
     only = args.only
     out = {}
     configs, gather = {}, {}
-    if only in (None, "headline", "multihot-uniform"):
+    if only in (None, "headline", "multihot-uniform", "inference"):
         res, gat, uni, gat_u, cpu = bench_headline(args, dev)
+        if only == "inference":
+            print(json.dumps({"inference": res}), flush=True)
+            return
         if only == "multihot-uniform":
             print(json.dumps({"multihot_uniform": uni, "gather": gat_u}), flush=True)
             return

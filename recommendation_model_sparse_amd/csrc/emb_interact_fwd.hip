@@ -90,8 +90,19 @@ __device__ __forceinline__ void lds_ksplit(const FusedArgs &a, const float *X, i
     }
 }
 
-template <int DT, int G, int KC, bool WEIGHTED, bool WAVE_PER_BAG>
-__global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
+// Waves per SIMD the compiler is asked to fit.  The unweighted multi-hot kernel with the
+// matrix-core Gram and rows of 16+ chunks fits 8 in 64 registers with no spill, against 7 by
+// default (62 VGPRs + 4 AGPRs for the MFMA accumulators at 256-byte rows); the extra wave keeps
+// more row loads in flight.  With 8-chunk rows the same request spills, so those keep the default.
+constexpr int fused_min_waves(int G, bool weighted, bool wpb, bool ksplit) {
+    return wpb && !weighted && !ksplit && G >= 16 ? 8 : 1;
+}
+
+// KSPLIT: the Gram is the k-split one of gram.h (N <= 11, D in {64, 128, 256}), else the
+// matrix-core one; a template parameter, so each kernel carries only its own Gram's registers.
+template <int DT, int G, int KC, bool WEIGHTED, bool WAVE_PER_BAG, bool KSPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_min_waves(G, WEIGHTED, WAVE_PER_BAG, KSPLIT))))
+void k_emb_interact_fwd(FusedArgs a) {
     constexpr int EPC = Elem<DT>::kPerChunk;
     constexpr int D = G * EPC;  // G 16-byte chunks per row
     constexpr int NG = kWave / G;
@@ -156,12 +167,12 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
                     uint4 v[U];
                     float w[U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {  // unconditional loads: past the bag, row of lookup 0
+                    for (int u = 0; u < U; ++u) {  // lanes past the bag load nothing (no address cycles)
                         const int r = r0 + u * NG + grp;
                         const int src = r < n ? r : 0;
                         const int64_t idx = __shfl(my_idx, src);
                         w[u] = WEIGHTED ? __shfl(my_w, src) : 1.f;
-                        v[u] = load_row_chunk(tab, idx, a.row_bytes);
+                        v[u] = r < n ? load_row_chunk(tab, idx, a.row_bytes) : make_uint4(0, 0, 0, 0);
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u)
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(256) void k_emb_interact_fwd(FusedArgs a) {
 
     const int P = a.P, W = P + D;
     if constexpr (D == 64 || D == 128 || D == 256) {
-        if (a.ksplit) {  // small N: the k-split Gram, one sample per wave
+        if constexpr (KSPLIT) {  // small N: the k-split Gram, one sample per wave
             if (gram_rows(N) == 9) lds_ksplit<9, D / 64>(a, X, XS, Sb, b0, wv, lane);
             else lds_ksplit<11, D / 64>(a, X, XS, Sb, b0, wv, lane);
             for (int i = tid; i < Sb * D; i += 256) {
@@ -657,7 +668,14 @@ bool dispatch_regs(const FusedArgs &a, int D, bool weighted, hipStream_t stream)
 
 template <int DT, int G, int KC, bool W, bool WPB>
 void launch_fused(const FusedArgs &a, size_t lds, uint32_t blocks, hipStream_t stream) {
-    DLRM_LAUNCH("emb_interact_fwd", (k_emb_interact_fwd<DT, G, KC, W, WPB>), dim3(blocks), dim3(256), lds, stream, a);
+    constexpr int D = G * Elem<DT>::kPerChunk;
+    if constexpr (D == 64 || D == 128 || D == 256) {
+        if (a.ksplit) {
+            DLRM_LAUNCH("emb_interact_fwd", (k_emb_interact_fwd<DT, G, KC, W, WPB, true>), dim3(blocks), dim3(256), lds, stream, a);
+            return;
+        }
+    }
+    DLRM_LAUNCH("emb_interact_fwd", (k_emb_interact_fwd<DT, G, KC, W, WPB, false>), dim3(blocks), dim3(256), lds, stream, a);
 }
 
 template <int DT, int G, int KC>
