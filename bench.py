@@ -593,6 +593,7 @@ def bench_headline(args, dev):
         "gathered_logical_frac_of_hbm_peak": gathered / (call_ms["emb_bag_fwd"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "step_ms_per_step_events": step_pct,
         "fwd_samples_per_s": wl.B / ((call_ms["emb_bag_fwd"] + call_ms["dlrm_interact_fwd"]) / 1e3),
+        "bwd_samples_per_s": wl.B / ((call_ms["dlrm_interact_bwd"] + call_ms["emb_bag_bwd_adagrad"]) / 1e3),
         "unique_rows": U_last,
         "call_ms": call_ms,
         "kernel_ms_per_step": kern_ms,
@@ -817,6 +818,15 @@ def hbm_context(dev, steps: int):
 
 # ---------------------------------------------------------------- main
 
+def add_read_ceiling(gather: dict, ctx: dict):
+    """Each lookup's counted HBM rate also as a fraction of what a gather of random 256-byte rows
+    with no output reaches on the same GPU (the probe in hbm_context), when both were measured."""
+    ceil = (ctx.get("random_row_gather") or {}).get("random_row_read_GBps")
+    for e in gather.values():
+        if ceil and e.get("hbm_GBps"):
+            e["hbm_frac_of_random_row_read_ceiling"] = e["hbm_GBps"] / ceil
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -896,11 +906,13 @@ def main():
     if only in (None, "interaction"):
         configs["interaction_paths"] = bench_interaction_paths(dev, args.steps)
     if only is not None:
+        add_read_ceiling(gather, ctx)
         print(json.dumps({"configs": configs, "gather": gather, "hbm_context": ctx}), flush=True)
         return
     out["configs"] = configs
     out["gather"] = gather
     out["hbm_context"] = ctx
+    add_read_ceiling(gather, ctx)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
