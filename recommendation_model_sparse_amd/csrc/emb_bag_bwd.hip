@@ -971,60 +971,77 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
 // Finishes the chunk-crossing segments: a grid-stride loop over the worklist K7 filled, one
 // listed chunk per block at a time.  The segment's partials are added in chunk order (slot B of
 // its first chunk, then slot A of every later chunk it covers), then the row is updated.
+// The first wavefront loads the chunk, the last chunk and the table row of up to 64 of the
+// block's items at once, so an item waits on one round trip (its partials, row and state) rather
+// than on the chain worklist -> segment -> segment end -> key -> row.
 template <int DT, int W, int G, int CS, int OPT>
 __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
     constexpr int NS = 256 / G;  // partial rows read per pass of the block
     constexpr int U = 8;
     constexpr int ES = DT == DLRM_BF16 ? 2 : 4;
     __shared__ float red[NS][G * W];
+    __shared__ uint32_t s_chunk[kWave], s_ce[kWave], s_t[kWave], s_r[kWave];
     __shared__ TableLDS sl;
     stage_tables(a, sl);
     const int sub = threadIdx.x / G, c = threadIdx.x % G;
     const uint32_t count = *a.fin_count;
-    for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {  // block-uniform
-        const uint32_t chunk = a.fin_list[item];
-        const uint32_t lo = chunk * CS, hi = lo + CS;
-        const uint32_t u = a.chunk_seg[chunk];
-        const uint32_t ce = static_cast<uint32_t>((a.seg_offsets[u + 1] - 1) / CS);  // last chunk it covers
-        float acc[W];
-#pragma unroll
-        for (int q = 0; q < W; ++q) acc[q] = 0.f;
-        if (sub == 0) load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-        for (uint32_t c1 = chunk + 1 + sub; c1 <= ce; c1 += NS * U) {
-            uint32_t pa[U][W];
-#pragma unroll
-            for (int k = 0; k < U; ++k)  // unconditional loads (clamped), all in flight together
-                gload_words<W>(a.part_a + static_cast<uint64_t>(min(c1 + k * NS, ce)) * a.D + c * W, pa[k]);
-#pragma unroll
-            for (int k = 0; k < U; ++k)
-                if (c1 + k * NS <= ce)
-#pragma unroll
-                    for (int q = 0; q < W; ++q) acc[q] += __uint_as_float(pa[k][q]);
-        }
-        // combine the NS row slots in a fixed order
-#pragma unroll
-        for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
-        __syncthreads();
-        if (sub == 0) {
-#pragma unroll
-            for (int q = 0; q < W; ++q) {
-                float x = red[0][c * W + q];
-                for (int k = 1; k < NS; ++k) x += red[k][c * W + q];
-                acc[q] = x;
-            }
+    for (uint32_t first = blockIdx.x; first < count; first += gridDim.x * kWave) {  // block-uniform
+        if (threadIdx.x < kWave) {
+            const uint32_t item = first + threadIdx.x * gridDim.x;
+            const uint32_t chunk = a.fin_list[item < count ? item : first];
+            const uint32_t u = a.chunk_seg[chunk];
+            const uint32_t hi = chunk * CS + CS;
             const uint32_t K = a.skeys[hi - 1];
             const uint32_t grow = a.sgrow[hi - 1];
             const uint32_t t = grow - fast_div(grow, a.divT) * a.divT.d;
-            const uint32_t r = K - sl.rowbase[t];
-            char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
-            uint32_t old[TabWords<DT, W>::N];
-            gload_words<TabWords<DT, W>::N>(row, old);
-            float *st = OPT == DLRM_OPT_ADAGRAD ? sl.state[t] + r : nullptr;
-            update_row<DT, W, G, OPT>(a, row, st, c, acc, old,
-                                      OPT == DLRM_OPT_ADAGRAD ? *(const DLRM_GLOBAL float *)st : 0.f);
+            s_chunk[threadIdx.x] = chunk;
+            s_ce[threadIdx.x] = static_cast<uint32_t>((a.seg_offsets[u + 1] - 1) / CS);  // last chunk it covers
+            s_t[threadIdx.x] = t;
+            s_r[threadIdx.x] = K - sl.rowbase[t];
         }
-        __syncthreads();  // red[] is reused by the next item
-        (void)lo;
+        __syncthreads();
+        for (uint32_t k = 0; k < kWave && first + k * gridDim.x < count; ++k) {  // block-uniform
+            const uint32_t chunk = s_chunk[k], ce = s_ce[k], t = s_t[k], r = s_r[k];
+            // the row and its state, loaded with the partials
+            char *row = sl.tab[t] + (static_cast<uint64_t>(r) * a.D + c * W) * ES;
+            float *st = OPT == DLRM_OPT_ADAGRAD ? sl.state[t] + r : nullptr;
+            uint32_t old[TabWords<DT, W>::N];
+            float s_old = 0.f;
+            if (sub == 0) {
+                gload_words<TabWords<DT, W>::N>(row, old);
+                if constexpr (OPT == DLRM_OPT_ADAGRAD) s_old = *(const DLRM_GLOBAL float *)st;
+            }
+            float acc[W];
+#pragma unroll
+            for (int q = 0; q < W; ++q) acc[q] = 0.f;
+            if (sub == 0) load_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+            for (uint32_t c1 = chunk + 1 + sub; c1 <= ce; c1 += NS * U) {
+                uint32_t pa[U][W];
+#pragma unroll
+                for (int kk = 0; kk < U; ++kk)  // unconditional loads (clamped), all in flight together
+                    gload_words<W>(a.part_a + static_cast<uint64_t>(min(c1 + kk * NS, ce)) * a.D + c * W, pa[kk]);
+#pragma unroll
+                for (int kk = 0; kk < U; ++kk)
+                    if (c1 + kk * NS <= ce)
+#pragma unroll
+                        for (int q = 0; q < W; ++q) acc[q] += __uint_as_float(pa[kk][q]);
+            }
+            // combine the NS row slots in a fixed order
+#pragma unroll
+            for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
+            __syncthreads();
+            if (sub == 0) {
+#pragma unroll
+                for (int q = 0; q < W; ++q) {
+                    float x = red[0][c * W + q];
+                    for (int kk = 1; kk < NS; ++kk) x += red[kk][c * W + q];
+                    acc[q] = x;
+                }
+                update_row<DT, W, G, OPT>(a, row, st, c, acc, old, s_old);
+            }
+            __syncthreads();  // red[] is reused by the next item
+        }
+        __syncthreads();  // the staged items are reused by the next batch
     }
 }
 
