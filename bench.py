@@ -830,7 +830,7 @@ def add_read_ceiling(gather: dict, ctx: dict):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--cpu-samples", type=int, default=16384)
