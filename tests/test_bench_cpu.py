@@ -58,3 +58,28 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_read_ceiling_fraction():
+    gather = {"zipf": {"hbm_GBps": 3000.0}, "uniform": {"hbm_GBps": None}, "cold": {}}
+    bench.add_read_ceiling(gather, {"random_row_gather": {"random_row_read_GBps": 6000.0}})
+    assert gather["zipf"]["hbm_frac_of_random_row_read_ceiling"] == 0.5
+    assert "hbm_frac_of_random_row_read_ceiling" not in gather["uniform"]
+    assert "hbm_frac_of_random_row_read_ceiling" not in gather["cold"]
+    # no probe measured: nothing added
+    g2 = {"zipf": {"hbm_GBps": 3000.0}}
+    bench.add_read_ceiling(g2, {})
+    assert g2 == {"zipf": {"hbm_GBps": 3000.0}}
+
+
+def test_inference_summary_bytes_and_rates():
+    class WL:
+        D, T, B, N, P, elem_size = 128, 26, 16384, 27, 351, 2
+    nnz = 1000000
+    out = bench.inference_summary({"fused": 0.25, "two_call": 0.30}, WL, nnz)
+    alg = nnz * (128 * 2 + 8) + (26 * 16384 + 1) * 8 + 16384 * 128 * 4 + 16384 * (351 + 128) * 4
+    assert out["fused_algorithmic_bytes"] == alg
+    assert abs(out["fused_GBps"] - alg / 0.25e-3 / 1e9) < 1e-6
+    assert abs(out["speedup"] - 1.2) < 1e-12
+    assert abs(out["fused_samples_per_s"] - 16384 / 0.25e-3) < 1e-3
+    assert out["fused_frac_hbm_peak"] == out["fused_GBps"] / bench.HBM_PEAK_GBPS
