@@ -35,27 +35,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 
 // ---------------------------------------------------------------- ReLU backward + bias gradient
 
-// Block (bx, by): rows [bx*kGradRows, +kGradRows), columns 4*(by*256 + tid) .. +3 (N % 8 == 0, so
-// each thread's 4 columns are 16 bytes of dy, 8 bytes of a bf16 y and of dz: vector accesses, a
-// quarter of the instructions of one column per thread).  dz = dy * [y > 0] (or dy); dz rounded
-// to bf16; partial[bx][c] = sum of the block's fp32 dz of column c, in row order.
+// Block (bx, by): rows [bx*kGradRows, +kGradRows), columns 4*(by*256 + g) .. +3 for the block's
+// column groups g (N % 8 == 0, so a group's 4 columns are 16 bytes of dy, 8 bytes of a bf16 y and
+// of dz: vector accesses, a quarter of the instructions of one column per thread).  A layer
+// narrower than 1024 columns has fewer than 256 groups: the block's threads then split its rows
+// into RL = 256 / groups interleaved row lanes (lane j takes rows r0 + j, r0 + j + RL, ...), so
+// every thread has work and the block's rows are walked RL at a time.  dz = dy * [y > 0] (or dy);
+// dz rounded to bf16; partial[bx][c] = sum of the block's fp32 dz of column c: each row lane adds
+// its rows in order, then the lanes' sums are added in lane order.
 template <bool RELU, int YT>
 __global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy, const void *__restrict__ y,
                                                    int64_t M, int32_t N, uint16_t *__restrict__ dz,
                                                    float *__restrict__ partial) {
-    const int32_t c = (blockIdx.y * 256 + threadIdx.x) * 4;
-    if (c >= N) return;
+    __shared__ float4 lane_sum[256];
+    const int32_t groups = min(N / 4, 256);  // column groups per block
+    const int RL = 256 / groups;             // row lanes
+    const int tid = threadIdx.x, j = tid / groups, g = tid % groups;
+    const int32_t c = (blockIdx.y * 256 + g) * 4;
+    const bool active = j < RL && c < N;
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGradRows;
     const int64_t r1 = min<int64_t>(r0 + kGradRows, M);
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     constexpr int R = 8;  // rows whose loads are in flight together (unconditional: clamped rows)
-    for (int64_t r = r0; r < r1; r += R) {
-        float4 g[R];
+    // a lane's rows r0 + j + RL*k; the last one it has is clamped to in every batch
+    const int64_t rl = active && r0 + j < r1 ? r1 - 1 - (r1 - 1 - r0 - j) % RL : -1;
+    for (int64_t r = r0 + j; active && r < r1; r += static_cast<int64_t>(R) * RL) {
+        float4 g4[R];
         float yv[R][4];
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            const uint64_t i = static_cast<uint64_t>(min(r + u, r1 - 1)) * N + c;
-            g[u] = *reinterpret_cast<const float4 *>(dy + i);
+            const uint64_t i = static_cast<uint64_t>(min(r + static_cast<int64_t>(u) * RL, rl)) * N + c;
+            g4[u] = *reinterpret_cast<const float4 *>(dy + i);
             if constexpr (RELU) {
                 if constexpr (YT == DLRM_F32) {
                     const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(y) + i);
@@ -69,8 +79,9 @@ __global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy,
         }
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            if (r + u >= r1) break;
-            float gu[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+            const int64_t ru = r + static_cast<int64_t>(u) * RL;
+            if (ru >= r1) break;
+            float gu[4] = {g4[u].x, g4[u].y, g4[u].z, g4[u].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if constexpr (RELU) gu[e] = yv[u][e] > 0.f ? gu[e] : 0.f;
@@ -78,10 +89,25 @@ __global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy,
             }
             const uint2 o = make_uint2(static_cast<uint32_t>(f32_to_bf16(gu[0])) | (static_cast<uint32_t>(f32_to_bf16(gu[1])) << 16),
                                        static_cast<uint32_t>(f32_to_bf16(gu[2])) | (static_cast<uint32_t>(f32_to_bf16(gu[3])) << 16));
-            *reinterpret_cast<uint2 *>(dz + static_cast<uint64_t>(r + u) * N + c) = o;
+            *reinterpret_cast<uint2 *>(dz + static_cast<uint64_t>(ru) * N + c) = o;
         }
     }
-    *reinterpret_cast<float4 *>(partial + static_cast<uint64_t>(blockIdx.x) * N + c) = make_float4(s[0], s[1], s[2], s[3]);
+    if (RL == 1) {  // block-uniform: one lane per column group, no combine
+        if (active)
+            *reinterpret_cast<float4 *>(partial + static_cast<uint64_t>(blockIdx.x) * N + c) =
+                make_float4(s[0], s[1], s[2], s[3]);
+        return;
+    }
+    lane_sum[tid] = make_float4(s[0], s[1], s[2], s[3]);
+    __syncthreads();
+    if (j == 0 && c < N) {
+        float4 t = lane_sum[g];
+        for (int q = 1; q < RL; ++q) {
+            const float4 v = lane_sum[q * groups + g];
+            t.x += v.x, t.y += v.y, t.z += v.z, t.w += v.w;
+        }
+        *reinterpret_cast<float4 *>(partial + static_cast<uint64_t>(blockIdx.x) * N + c) = t;
+    }
 }
 
 // Sum over blocks of partial[blk][c] (row stride `ld`) for column c: one wavefront per column;
