@@ -224,10 +224,12 @@ size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int32_t D, int
  *     segment_offsets_out [nnz+1] int64: first sorted position of each key; entry U = nnz
  *     sorted_pos_out      [nnz] int32: original position of each sorted position
  *     num_unique_out      [1] int64: U
- *   Limits: D a power of two in [4, 512] (bf16: [8, 512]).  The segment sums run on lane
- *   groups of D/4 lanes (D/8 at D = 512) that must tile the 64-lane wavefront exactly: the
- *   group sums are DPP/permute trees inside the group, and segment starts are read from the
- *   wave's ballot mask by group.  (The forward takes any row of a multiple of 16 bytes.)
+ *   Limits: D in [4, 512], a multiple of 4 up to 256 and of 8 above (bf16: a multiple of 8),
+ *   so every row is a multiple of 16 bytes as in the forward, except fp32 rows of 260-508
+ *   values that are an odd multiple of 4 (unsupported).  The segment sums run on lane groups
+ *   of D/4 lanes (D/8 above 256) rounded up to a power of two, so that groups tile the 64-lane
+ *   wavefront: the group sums are DPP/permute trees inside the group, and segment starts are
+ *   read from the wave's ballot mask by group.
  *   Keys are 32-bit: the sum of rows must be at most 2^32.
  */
 int emb_bag_bwd_adagrad(void *const *tables, float *const *state, const int64_t *rows, int32_t T,

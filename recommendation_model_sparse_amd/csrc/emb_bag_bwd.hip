@@ -73,10 +73,17 @@ struct Layout {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // lanes per row (G) and fp32 columns per lane (W) of the K7 kernels
+// W columns per lane (16 bytes of fp32), D/W lanes per row, in a lane group of G lanes: D/W
+// rounded up to a power of two, so that groups tile the 64-lane wavefront.  The G - D/W lanes past
+// the row address its last W columns again (every load stays inside the row) and neither store
+// nor add to the row's mean square.
 bool bwd_geometry(int32_t D, int *G, int *W) {
-    if (D < 4 || D > 512 || (D & (D - 1)) != 0) return false;
-    *W = D >= 512 ? 8 : 4;
-    *G = D / *W;
+    if (D < 4 || D > 512 || D % 4 != 0) return false;
+    *W = D > 256 ? 8 : 4;
+    if (D % *W != 0) return false;
+    int g = 1;
+    while (g < D / *W) g <<= 1;
+    *G = g;
     return true;
 }
 
@@ -700,9 +707,10 @@ struct TabWords {
 
 // The update of one row (the lane's W columns).  Row-wise Adagrad: s += mean(G^2);
 // row -= lr*G/(sqrt(s)+eps).  SGD: row -= lr*G (no state).  `row` points at the lane's first
-// column of the row, `old` holds those columns as stored.
+// column of the row, `old` holds those columns as stored; a lane past the row (`col` false) takes
+// no part.
 template <int DT, int W, int G, int OPT>
-__device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, float *state, int c,
+__device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, float *state, int cg, bool col,
                                            const float *g, const uint32_t *old, float old_state) {
     using TW = TabWords<DT, W>;
     if constexpr (OPT == DLRM_OPT_SGD) {
@@ -712,14 +720,14 @@ __device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, floa
         for (int e = 0; e < W; ++e) x[e] = fmaf(-a.lr, g[e], x[e]);
         uint32_t nw[TW::N];
         TW::from_f32(x, nw);
-        gstore_words<TW::N>(row, nw);
-        (void)state, (void)c, (void)old_state;
+        if (col) gstore_words<TW::N>(row, nw);
+        (void)state, (void)cg, (void)old_state;
         return;
     }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < W; ++e) ss = fmaf(g[e], g[e], ss);
-    ss = group_sum<G>(ss);
+    ss = group_sum<G>(col ? ss : 0.f);
     const float s_new = old_state + ss * a.inv_D;
     // hardware square root and reciprocal (about 1 ulp each)
     const float step = a.lr * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(s_new) + a.eps);
@@ -729,8 +737,8 @@ __device__ __forceinline__ void update_row(const AdagradArgs &a, char *row, floa
     for (int e = 0; e < W; ++e) x[e] = fmaf(-step, g[e], x[e]);
     uint32_t nw[TW::N];
     TW::from_f32(x, nw);
-    gstore_words<TW::N>(row, nw);
-    if (c == 0) *(DLRM_GLOBAL float *)state = s_new;
+    if (col) gstore_words<TW::N>(row, nw);
+    if (cg == 0) *(DLRM_GLOBAL float *)state = s_new;
 }
 
 // Per sorted position, staged in LDS by the lane that owns it and read back as broadcasts.
@@ -761,7 +769,10 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
     __shared__ PosMeta meta[4][NG][CS];
     __shared__ TableLDS sl;
     stage_tables(a, sl);
-    const int wv = static_cast<int>(wave_id()), lane = threadIdx.x & 63, grp = lane / G, c = lane % G;
+    const int wv = static_cast<int>(wave_id()), lane = threadIdx.x & 63, grp = lane / G, cg = lane % G;
+    const int dw = a.D / W;           // lanes that hold columns of the row
+    const bool col = cg < dw;
+    const int c = col ? cg : dw - 1;  // the lane's columns (past the row: the last W again)
     const uint32_t chunk = (blockIdx.x * 4 + wv) * NG + grp;
     if (chunk >= a.nchunk) return;  // group-uniform
     const uint32_t lo = chunk * CS, hi = min(lo + CS, a.n), cnt = hi - lo;
@@ -776,11 +787,12 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
     const uint32_t key_hi = a.skeys[min(hi, a.n - 1)];
     const uint32_t key_e = a.skeys[e_next - 1];
 
-    // build the chunk's metadata: lane c owns positions lo + c + m*G
+    // build the chunk's metadata: lane cg of the group owns positions lo + cg + m*G (every lane of
+    // the group, also those past the row: ownership of positions does not depend on the columns)
     uint64_t starts = 0;  // bit r: position lo + r opens a segment
 #pragma unroll
     for (int m = 0; m < MP; ++m) {
-        const uint32_t r = c + m * G, k = lo + r;
+        const uint32_t r = cg + m * G, k = lo + r;
         const bool have = k < hi;
         const uint32_t kk = have ? k : hi - 1;  // loads stay unconditional
         const uint32_t key = a.skeys[kk];
@@ -832,7 +844,7 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
                 }
             }
         }
-        store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+        if (col) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
         return;
     }
     bool open_before = !(starts & 1ull);  // the first piece began in an earlier chunk
@@ -861,7 +873,7 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
     for (int e = 0; e < TW::N; ++e) cur_row[e] = 0u;
     auto flush = [&](uint32_t rs) {
         const PosMeta &p = pm[rs];
-        update_row<DT, W, G, OPT>(a, p.tab_row + c * W * ES, p.state, c, acc, cur_row, cur_s);
+        update_row<DT, W, G, OPT>(a, p.tab_row + c * W * ES, p.state, cg, col, acc, cur_row, cur_s);
     };
 
     for (uint32_t r0 = 0; r0 < cnt; r0 += U) {
@@ -889,7 +901,9 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
             const bool s_u = valid && ((starts >> (r & 63u)) & 1ull);
             if (s_u) {
                 if (r > r_begin) {  // the previous piece ended inside this chunk
-                    if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+                    if (open_before) {
+                        if (col) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+                    }
                     else flush(cur_r);
                 }
 #pragma unroll
@@ -909,8 +923,9 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
     }
     // the last piece of the chunk
     const bool carry_on = runs_past && key_e != key_last;
-    if (open_before) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
-    else if (carry_on) {
+    if (open_before) {
+        if (col) store_f32<W>(a.part_a + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+    } else if (carry_on) {
         // read on to the segment's end in the next chunk (fewer than CS positions), then update
         const uint32_t span = e_next - hi;  // positions of the next chunk
         char *row_ptr = pm[cur_r].tab_row + c * W * ES;
@@ -921,7 +936,7 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
         uint32_t m = 0;  // positions of the segment in the next chunk: its keys equal key_last
 #pragma unroll
         for (int k = 0; k < MP; ++k) {
-            const uint32_t r = c + k * G;
+            const uint32_t r = cg + k * G;
             const uint32_t kk = hi + min(r, span - 1);
             const bool same = r < span && a.skeys[kk] == key_last;
             PosMeta p;
@@ -957,12 +972,12 @@ __attribute__((amdgpu_waves_per_eu(k7_min_waves(DT, W, G, WEIGHTED)))) void k_se
                 }
             }
         }
-        update_row<DT, W, G, OPT>(a, row_ptr, st_ptr, c, acc, cur_row, cur_s);
+        update_row<DT, W, G, OPT>(a, row_ptr, st_ptr, cg, col, acc, cur_row, cur_s);
     } else if (runs_past) {
-        store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
+        if (col) store_f32<W>(a.part_b + static_cast<uint64_t>(chunk) * a.D + c * W, acc);
         // the segment starting here crosses into later chunks: queue it for the finisher
         // (list order is arbitrary; each entry's work is fixed, so results do not depend on it)
-        if (c == 0) a.fin_list[atomicAdd(a.fin_count, 1u)] = chunk;
+        if (cg == 0) a.fin_list[atomicAdd(a.fin_count, 1u)] = chunk;
     } else {
         flush(cur_r);
     }
@@ -983,7 +998,10 @@ __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
     __shared__ uint32_t s_chunk[kWave], s_ce[kWave], s_t[kWave], s_r[kWave];
     __shared__ TableLDS sl;
     stage_tables(a, sl);
-    const int sub = threadIdx.x / G, c = threadIdx.x % G;
+    const int sub = threadIdx.x / G, cg = threadIdx.x % G;
+    const int dw = a.D / W;           // lanes that hold columns of the row
+    const bool col = cg < dw;
+    const int c = col ? cg : dw - 1;  // the lane's columns (past the row: the last W again)
     const uint32_t count = *a.fin_count;
     for (uint32_t first = blockIdx.x; first < count; first += gridDim.x * kWave) {  // block-uniform
         if (threadIdx.x < kWave) {
@@ -1028,16 +1046,16 @@ __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
             }
             // combine the NS row slots in a fixed order
 #pragma unroll
-            for (int q = 0; q < W; ++q) red[sub][c * W + q] = acc[q];
+            for (int q = 0; q < W; ++q) red[sub][cg * W + q] = acc[q];
             __syncthreads();
             if (sub == 0) {
 #pragma unroll
                 for (int q = 0; q < W; ++q) {
-                    float x = red[0][c * W + q];
-                    for (int kk = 1; kk < NS; ++kk) x += red[kk][c * W + q];
+                    float x = red[0][cg * W + q];
+                    for (int kk = 1; kk < NS; ++kk) x += red[kk][cg * W + q];
                     acc[q] = x;
                 }
-                update_row<DT, W, G, OPT>(a, row, st, c, acc, old, s_old);
+                update_row<DT, W, G, OPT>(a, row, st, cg, col, acc, old, s_old);
             }
             __syncthreads();  // red[] is reused by the next item
         }
@@ -1273,7 +1291,7 @@ static int apply_impl(void *const *tables, float *const *state, const int64_t *r
     if (!tables || D < 1 || B < 0 || nnz < 0) return DLRM_ERR_INVALID_ARG;
     if (dtype != DLRM_F32 && dtype != DLRM_BF16) return DLRM_ERR_INVALID_ARG;
     int G, W;
-    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D % 8 != 0)) return DLRM_ERR_UNSUPPORTED;
     if (nnz >= (int64_t(1) << 31) || static_cast<int64_t>(T) * B >= (int64_t(1) << 31)) return DLRM_ERR_UNSUPPORTED;
     const bool adagrad = optimizer == DLRM_OPT_ADAGRAD;
     if (adagrad && !state) return DLRM_ERR_INVALID_ARG;
@@ -1353,7 +1371,7 @@ extern "C" int emb_bag_bwd_update(void *const *tables, float *const *state, cons
                          per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     int G, W;
-    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D % 8 != 0)) return DLRM_ERR_UNSUPPORTED;
     if (optimizer == DLRM_OPT_ADAGRAD) {
         if (!state) return DLRM_ERR_INVALID_ARG;
         for (int t = 0; t < T; ++t)
@@ -1444,7 +1462,7 @@ extern "C" int emb_bag_bwd_update_noalloc(void *const *tables, float *const *sta
                          per_sample_weights, B, nnz);
     if (rc != DLRM_OK) return rc;
     int G, W;
-    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D < 8)) return DLRM_ERR_UNSUPPORTED;
+    if (!bwd_geometry(D, &G, &W) || (dtype == DLRM_BF16 && D % 8 != 0)) return DLRM_ERR_UNSUPPORTED;
     PlanShape ps;
     rc = plan_shape(rows, T, D, nnz, &ps);
     if (rc != DLRM_OK) return rc;

@@ -125,7 +125,8 @@ def test_emb_bag_bwd_update_rejects(L):
     assert upd(L, optimizer=0, state=False) == INVALID       # Adagrad needs its state
     assert upd(L, optimizer=1, state=False, wsz=1) == WORKSPACE  # SGD takes no state; reaches the workspace check
     assert upd(L, index_type=1, idx=FAKE + 2) == INVALID
-    assert upd(L, D=24) == UNSUPPORTED
+    assert upd(L, D=20, wsz=1) == WORKSPACE        # any multiple of 4 passes the width check
+    assert upd(L, D=260) == UNSUPPORTED
 
 
 def plan(L, T=1, D=16, index_type=0, wsz=None, flags=0, rows=None, idx=FAKE):
@@ -139,7 +140,8 @@ def plan(L, T=1, D=16, index_type=0, wsz=None, flags=0, rows=None, idx=FAKE):
 def test_emb_bag_bwd_plan_rejects(L):
     assert plan(L, index_type=5) == INVALID
     assert plan(L, T=0, rows=[]) == INVALID
-    assert plan(L, D=24) == UNSUPPORTED
+    assert plan(L, D=260) == UNSUPPORTED
+    assert plan(L, D=24, wsz=1) == WORKSPACE       # any multiple of 4 passes the width check
     assert plan(L, flags=4) == INVALID
     assert plan(L, wsz=1) == WORKSPACE
     assert plan(L, index_type=1, idx=FAKE + 2) == INVALID
@@ -160,7 +162,9 @@ def test_emb_bag_bwd_apply_rejects(L):
     assert apply(L, optimizer=2) == INVALID
     assert apply(L, state=False) == INVALID                 # Adagrad needs its state
     assert apply(L, optimizer=1, state=False, wsz=1) == WORKSPACE
-    assert apply(L, D=24) == UNSUPPORTED
+    assert apply(L, D=260) == UNSUPPORTED
+    assert apply(L, D=12, dtype=1) == UNSUPPORTED   # 24-byte bf16 rows
+    assert apply(L, D=24, wsz=1) == WORKSPACE       # any multiple of 4 passes the width check
     assert apply(L, D=4, dtype=1) == UNSUPPORTED            # bf16 rows under 16 bytes
     assert apply(L, dtype=3) == INVALID
     assert apply(L, grad=FAKE + 4) == INVALID               # grad_pooled 16-byte aligned
@@ -220,8 +224,11 @@ def test_sgd_dense_multi_rejects(L):
 
 def test_workspace_size(L):
     ws = lambda rows, D, B, nnz: binding.emb_bag_bwd_workspace_size(rows, D, B, nnz)
-    assert ws([100], 6, 4, 10) == 0          # D must be a power of two
+    assert ws([100], 6, 4, 10) == 0          # D must be a multiple of 4
+    assert ws([100], 260, 4, 10) == 0        # and of 8 above 256
     assert ws([100], 1024, 4, 10) == 0
+    for D in (4, 12, 24, 48, 96, 136, 200, 264, 384, 504):
+        assert ws([100], D, 4, 10) > 0, D    # any other row of 16-byte multiples
     a, b = ws([100, 200], 128, 64, 1000), ws([100, 200], 128, 64, 100000)
     assert 0 < a < b
     assert a % 256 == 0 and b % 256 == 0
@@ -241,8 +248,10 @@ def bwd(L, T=1, D=16, dtype=0, B=4, nnz=4, rows=None, ws=FAKE, wsz=None, grad=FA
 
 
 def test_emb_bag_bwd_rejects(L):
-    assert bwd(L, D=24) == UNSUPPORTED         # not a power of two
+    assert bwd(L, D=6) == UNSUPPORTED          # rows of 24 bytes: not a multiple of 16
+    assert bwd(L, D=260) == UNSUPPORTED        # fp32 above 256 needs a multiple of 8
     assert bwd(L, D=4, dtype=1) == UNSUPPORTED  # bf16 rows below 16 bytes
+    assert bwd(L, D=12, dtype=1) == UNSUPPORTED  # 24-byte bf16 rows
     assert bwd(L, rows=[1 << 31, 1 << 31, 5], T=3) == UNSUPPORTED  # keys beyond 32 bits
     assert bwd(L, state=ptrs(0)) == INVALID
     assert bwd(L, grad=0) == INVALID
@@ -352,7 +361,7 @@ def test_noalloc_refuses_batches_beyond_its_scratch(L):
                                       FAKE, 0, 0.01, 1e-8, None, None, None, None, 0, None)
     assert rc == WORKSPACE
     # the ordinary argument checks come first
-    assert L.emb_bag_bwd_update_noalloc(ptrs(FAKE), ptrs(FAKE), i64s(1000), 1, 24, 0, FAKE, FAKE, 0, None, 1, 4,
+    assert L.emb_bag_bwd_update_noalloc(ptrs(FAKE), ptrs(FAKE), i64s(1000), 1, 260, 0, FAKE, FAKE, 0, None, 1, 4,
                                         FAKE, 0, 0.01, 1e-8, None, None, None, None, 0, None) == UNSUPPORTED
 
 

@@ -310,11 +310,13 @@ def run_adagrad(rows, D, dtype, B, lengths, weighted, seed, max_len=12, hot=None
     return r
 
 
-@pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256, 512])
+# powers of two fill their lane groups; the others leave lanes past the row (12: 3 of 4 lanes,
+# 200: 50 of 64, 384: 48 of 64 lanes of 8 columns, 504: 63 of 64)
+@pytest.mark.parametrize("D", [4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 136, 200, 256, 264, 384, 504, 512])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("weighted", [False, True])
 def test_adagrad_random(D, dtype, weighted):
-    if dtype == "bf16" and D < 8:
+    if dtype == "bf16" and D % 8:
         pytest.skip("bf16 rows must be a multiple of 16 bytes")
     run_adagrad([300, 7, 1000], D, dtype, 257, "multi", weighted, seed=D * 3 + weighted,
                 label="random")
@@ -336,6 +338,14 @@ def test_adagrad_long_segments_cross_chunks():
     """One row hit by every lookup: one segment over ~150 chunks (finisher path)."""
     run_adagrad([50], 128, "f32", 2000, "multi", True, seed=11, max_len=10, hot=3, label="hot-f32")
     run_adagrad([50, 9], 64, "bf16", 1200, "multi", False, seed=12, max_len=10, hot=0, label="hot-bf16")
+
+
+def test_adagrad_long_segments_partial_lane_groups():
+    """Segments over many chunks (partials and the finisher) at widths whose lane groups hold
+    lanes past the row."""
+    run_adagrad([50], 96, "f32", 2000, "multi", True, seed=15, max_len=10, hot=3, label="hot-f32-D96")
+    run_adagrad([40, 9], 200, "bf16", 1200, "multi", False, seed=16, max_len=10, hot=0, label="hot-bf16-D200")
+    run_adagrad([30], 384, "f32", 1500, "multi", True, seed=17, max_len=10, hot=1, label="hot-f32-D384")
 
 
 def test_adagrad_onehot_and_zipf_like():

@@ -98,7 +98,8 @@ def run_update(rows, D, dtype, B, lengths, weighted, seed, opt, index32, max_len
 
 
 @pytest.mark.parametrize("dtype,D", [("f32", 4), ("f32", 32), ("f32", 128), ("f32", 512), ("bf16", 8),
-                                     ("bf16", 128), ("bf16", 256)])
+                                     ("bf16", 128), ("bf16", 256), ("f32", 20), ("f32", 392), ("bf16", 40),
+                                     ("bf16", 168)])
 @pytest.mark.parametrize("lengths", ["onehot", "multi"])
 @pytest.mark.parametrize("weighted", [False, True])
 def test_sgd_vs_oracle(dtype, D, lengths, weighted):
