@@ -25,6 +25,7 @@
 //       queued on a worklist; K7b takes each listed segment with a whole block, reads its end
 //       from the segment offsets, adds the partials in chunk order and applies the update.
 //       Every sum has a fixed order, so the update is bitwise reproducible; no float atomics.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -68,6 +69,7 @@ struct Layout {
     uint32_t nblk;    // sort / segment tiles
     uint32_t nchunk;  // K7 chunks of CS sorted positions
     int G, W, CS;
+    bool short_chunks;  // CS is the shorter of the two chunk lengths
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -87,13 +89,21 @@ bool bwd_geometry(int32_t D, int *G, int *W) {
     return true;
 }
 
-// sorted positions per K7 chunk: G lanes times MP positions per lane (at most 64)
-inline int chunk_positions(int G) { return G * (G >= 16 ? 64 / G : 4); }
+// Sorted positions per K7 chunk: G lanes times MP positions per lane, at most 64.  A batch of
+// fewer than kShortChunkMax lookups takes chunks of half that length where the lane group allows
+// it (32 instead of 64 at D = 128): at full length its segment reduce would have fewer than about
+// two blocks per CU, each walking a longer chain of dependent batches of loads.
+constexpr int64_t kShortChunkMax = int64_t(1) << 18;
+
+constexpr int chunk_mp(int G, bool shorter) {
+    return G >= 64 ? 1 : G >= 16 ? (shorter ? 32 / G : 64 / G) : (shorter ? 2 : 4);
+}
 
 Layout make_layout(int32_t D, int64_t nnz) {
     Layout L{};
     bwd_geometry(D, &L.G, &L.W);
-    L.CS = chunk_positions(L.G);
+    L.short_chunks = nnz < kShortChunkMax;
+    L.CS = L.G * chunk_mp(L.G, L.short_chunks);
     const size_t n = static_cast<size_t>(nnz > 0 ? nnz : 1);
     L.nblk = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
     L.nchunk = static_cast<uint32_t>((n + L.CS - 1) / L.CS);
@@ -1063,14 +1073,10 @@ __global__ __launch_bounds__(256) void k_seg_finish(AdagradArgs a) {
     }
 }
 
-template <int G>
-constexpr int chunk_mp() { return G >= 16 ? 64 / G : 4; }
-
-template <int DT, int W, int G, int OPT>
-void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
+template <int DT, int W, int G, int MP, int OPT>
+void launch_k7_mp(const AdagradArgs &a, bool weighted, hipStream_t stream) {
     constexpr const char *name = OPT == DLRM_OPT_SGD ? "seg_reduce_sgd" : "seg_reduce_adagrad";
     constexpr int NG = kWave / G;
-    constexpr int MP = chunk_mp<G>();
     constexpr int U = DLRM_K7_U;
     const uint32_t blocks = (a.nchunk + 4 * NG - 1) / (4 * NG);
     if (weighted)
@@ -1081,20 +1087,26 @@ void launch_k7(const AdagradArgs &a, bool weighted, hipStream_t stream) {
     DLRM_LAUNCH("seg_finish", (k_seg_finish<DT, W, G, G * MP, OPT>), dim3(fin_blocks), dim3(256), 0, stream, a);
 }
 
+template <int DT, int W, int G, int OPT>
+void launch_k7(const AdagradArgs &a, bool weighted, bool shorter, hipStream_t stream) {
+    if (shorter) launch_k7_mp<DT, W, G, chunk_mp(G, true), OPT>(a, weighted, stream);
+    else launch_k7_mp<DT, W, G, chunk_mp(G, false), OPT>(a, weighted, stream);
+}
+
 template <int DT, int OPT>
-void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, hipStream_t stream) {
+void dispatch_k7(const AdagradArgs &a, int G, int W, bool weighted, bool shorter, hipStream_t stream) {
     if (W == 8) {
-        launch_k7<DT, 8, 64, OPT>(a, weighted, stream);
+        launch_k7<DT, 8, 64, OPT>(a, weighted, shorter, stream);
         return;
     }
     switch (G) {
-        case 1: launch_k7<DT, 4, 1, OPT>(a, weighted, stream); break;
-        case 2: launch_k7<DT, 4, 2, OPT>(a, weighted, stream); break;
-        case 4: launch_k7<DT, 4, 4, OPT>(a, weighted, stream); break;
-        case 8: launch_k7<DT, 4, 8, OPT>(a, weighted, stream); break;
-        case 16: launch_k7<DT, 4, 16, OPT>(a, weighted, stream); break;
-        case 32: launch_k7<DT, 4, 32, OPT>(a, weighted, stream); break;
-        case 64: launch_k7<DT, 4, 64, OPT>(a, weighted, stream); break;
+        case 1: launch_k7<DT, 4, 1, OPT>(a, weighted, shorter, stream); break;
+        case 2: launch_k7<DT, 4, 2, OPT>(a, weighted, shorter, stream); break;
+        case 4: launch_k7<DT, 4, 4, OPT>(a, weighted, shorter, stream); break;
+        case 8: launch_k7<DT, 4, 8, OPT>(a, weighted, shorter, stream); break;
+        case 16: launch_k7<DT, 4, 16, OPT>(a, weighted, shorter, stream); break;
+        case 32: launch_k7<DT, 4, 32, OPT>(a, weighted, shorter, stream); break;
+        case 64: launch_k7<DT, 4, 64, OPT>(a, weighted, shorter, stream); break;
     }
 }
 
@@ -1124,7 +1136,11 @@ extern "C" size_t emb_bag_bwd_workspace_size(int32_t T, const int64_t *rows, int
     using namespace dlrm;
     int G, W;
     if (T < 1 || T > kMaxTables || !rows || B < 0 || nnz < 0 || !bwd_geometry(D, &G, &W)) return 0;
-    return make_layout(D, nnz).total;
+    // a smaller batch may take the shorter chunks and then needs more partial rows: the size for
+    // nnz lookups covers every batch of at most nnz
+    size_t total = make_layout(D, nnz).total;
+    if (nnz >= kShortChunkMax) total = std::max(total, make_layout(D, kShortChunkMax - 1).total);
+    return total;
 }
 
 namespace dlrm {
@@ -1339,11 +1355,11 @@ static int apply_impl(void *const *tables, float *const *state, const int64_t *r
     a.inv_D = 1.0f / static_cast<float>(D);
     const bool w = weighted != 0;
     if (adagrad) {
-        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, stream);
-        else dispatch_k7<DLRM_BF16, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, stream);
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, L.short_chunks, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_ADAGRAD>(a, L.G, L.W, w, L.short_chunks, stream);
     } else {
-        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_SGD>(a, L.G, L.W, w, stream);
-        else dispatch_k7<DLRM_BF16, DLRM_OPT_SGD>(a, L.G, L.W, w, stream);
+        if (dtype == DLRM_F32) dispatch_k7<DLRM_F32, DLRM_OPT_SGD>(a, L.G, L.W, w, L.short_chunks, stream);
+        else dispatch_k7<DLRM_BF16, DLRM_OPT_SGD>(a, L.G, L.W, w, L.short_chunks, stream);
     }
     return launch_status();
 }

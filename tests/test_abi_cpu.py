@@ -235,6 +235,15 @@ def test_workspace_size(L):
     assert ws([100], 128, 4, 0) > 0           # valid for an empty batch too
 
 
+def test_workspace_size_covers_smaller_batches(L):
+    """A workspace sized for nnz lookups serves every smaller batch: sizes never decrease with nnz,
+    also where batches below 2^18 lookups switch to shorter segment-reduce chunks (more partials)."""
+    ws = lambda D, nnz: binding.emb_bag_bwd_workspace_size([1000, 5000], D, 64, nnz)
+    for D in (4, 16, 128, 200, 512):
+        sizes = [ws(D, n) for n in (1, 4096, (1 << 18) - 2, (1 << 18) - 1, 1 << 18, (1 << 18) + 1, 1 << 19)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), (D, sizes)
+
+
 def bwd(L, T=1, D=16, dtype=0, B=4, nnz=4, rows=None, ws=FAKE, wsz=None, grad=FAKE, state=None,
         tables=None, flags=0):
     rows = rows if rows is not None else [10] * T

@@ -348,6 +348,16 @@ def test_adagrad_long_segments_partial_lane_groups():
     run_adagrad([30], 384, "f32", 1500, "multi", True, seed=17, max_len=10, hot=1, label="hot-f32-D384")
 
 
+def test_adagrad_batches_on_both_chunk_lengths():
+    """Batches of 2^18 lookups or more walk 64-position chunks at D = 128 (16 per lane group of 4
+    lanes at D = 16), smaller ones chunks of half that; both against the oracle, with segments of
+    thousands of lookups (a 50-row table) beside mostly single ones (200000 rows)."""
+    run_adagrad([50, 200000], 128, "f32", 8000, "multi", True, seed=21, max_len=60, label="long chunks f32")
+    run_adagrad([50, 200000], 200, "bf16", 8000, "multi", False, seed=22, max_len=60, label="long chunks bf16 D200")
+    run_adagrad([30, 100000], 16, "f32", 131072, "onehot", False, seed=23, label="2^18 lookups: long chunks")
+    run_adagrad([30, 100000], 16, "f32", 131071, "onehot", True, seed=24, label="2^18 - 2 lookups: short chunks")
+
+
 def test_adagrad_onehot_and_zipf_like():
     run_adagrad([100000, 20, 3000], 128, "f32", 4000, "onehot", False, seed=13, label="onehot")
     run_adagrad([5, 6, 7], 16, "f32", 3000, "multi", True, seed=14, max_len=40, label="few rows")
