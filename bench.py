@@ -339,14 +339,36 @@ def bench_train_onehot(wl, dev, steps: int, rotate: int):
     ms_bwd = ev_ms(bwd, nb, steps)
     kern = traced(step, nb, steps)
     launches = sum(v["launches_per_call"] for v in kern.values())
-    del tabs, states
+    # the same steps replayed as HIP graphs, one captured per batch: the library calls allocate
+    # nothing and never synchronize, so a step records as is; a replay launches its kernels without
+    # the host-side work of the four calls, which at this size is close to the kernels' own time
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream(dev))
+    graphs = []
+    for i in range(nb):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) / steps * 1e3
+    del graphs, tabs, states
     torch.cuda.empty_cache()
     return {"workload": wl.note, "B": wl.B, "tables": wl.T, "D": wl.D, "table_dtype": "f32",
             "ms_per_step": ms_step, "samples_per_s": wl.B / (ms_step / 1e3),
+            "ms_per_step_graph": ms_graph, "samples_per_s_graph": wl.B / (ms_graph / 1e3),
             "ms_backward": ms_bwd, "backward_samples_per_s": wl.B / (ms_bwd / 1e3),
             "kernel_launches_per_step": launches,
             "kernel_ms_sum_per_step": sum(v["ms_per_call"] for v in kern.values()), "kernels": kern,
-            "note": "wall clock over the timed steps; every call of the step on one stream"}
+            "note": "wall clock over the timed steps; every call of the step on one stream; _graph: "
+                    "the same steps replayed as HIP graphs (one per batch)"}
 
 
 # ---------------------------------------------------------------- the multi-hot step (headline)

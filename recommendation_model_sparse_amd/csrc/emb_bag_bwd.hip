@@ -341,10 +341,16 @@ struct SortIO {
     uint32_t *pout[3];
 };
 
+// Sorts of at most kInlineScanTiles tiles skip the scan launch: each scatter block adds up the raw
+// per-tile counts of its digits itself (at most 16 per digit, loaded together), which costs less
+// than a launch when the whole pass is a few microseconds.
+constexpr uint32_t kInlineScanTiles = 16;
+
 // NP payload words travel with each key.  Each 256-thread block ranks its tile of 4096 keys
 // stably with wavefront ballots, stages the tile in LDS in sorted order, and writes it out in
-// runs of equal digits, so the global stores are contiguous.
-template <int NP, int RB>
+// runs of equal digits, so the global stores are contiguous.  INL: counts are the raw per-tile
+// counts (no scan ran; nblk <= kInlineScanTiles) and totals is unused.
+template <int NP, int RB, bool INL>
 __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, int shift,
                                                        const uint32_t *__restrict__ counts,
                                                        uint32_t nblk,
@@ -376,11 +382,32 @@ __global__ __launch_bounds__(256) void k_radix_scatter(SortIO io, uint32_t n, in
     {
         // digits tid*K .. tid*K+K-1: global base = exclusive scan of totals + this block's prefix
         uint32_t tv[K], cv[K], sum = 0;
+        if constexpr (INL) {
+            // the digit's total and its count over the tiles before this one, from the raw counts
+            uint32_t c[K][kInlineScanTiles];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            tv[k] = totals[tid * K + k];
-            cv[k] = counts[(tid * K + k) * nblk + tile];
-            sum += tv[k];
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (uint32_t i = 0; i < kInlineScanTiles; ++i)
+                    c[k][i] = counts[(tid * K + k) * nblk + min(i, nblk - 1)];  // clamped in bounds
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                tv[k] = 0, cv[k] = 0;
+#pragma unroll
+                for (uint32_t i = 0; i < kInlineScanTiles; ++i) {
+                    const uint32_t x = i < nblk ? c[k][i] : 0u;
+                    tv[k] += x;
+                    cv[k] += i < tile ? x : 0u;
+                }
+                sum += tv[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                tv[k] = totals[tid * K + k];
+                cv[k] = counts[(tid * K + k) * nblk + tile];
+                sum += tv[k];
+            }
         }
         uint32_t tot;
         uint32_t run = block_exclusive_scan(sum, &tot);
@@ -1115,17 +1142,29 @@ void launch_radix_pass(const SortIO &io, int NP, uint32_t n, int shift, uint32_t
                        uint32_t nblk, uint32_t *totals, hipStream_t stream) {
     DLRM_LAUNCH("radix_hist", k_radix_hist<RB>, dim3(round_up_xcd(nblk)), dim3(256), 0, stream, io.kin, n, shift,
                 counts, nblk);
-    DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(1 << RB), dim3(256), 0, stream, counts, nblk, totals);
     const dim3 sgrid(round_up_xcd(nblk));
+    if (nblk <= kInlineScanTiles) {
+        if (NP == 3)
+            DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB, true>), sgrid, dim3(256), 0, stream, io, n, shift,
+                        counts, nblk, totals);
+        else if (NP == 2)
+            DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB, true>), sgrid, dim3(256), 0, stream, io, n, shift,
+                        counts, nblk, totals);
+        else
+            DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB, true>), sgrid, dim3(256), 0, stream, io, n, shift,
+                        counts, nblk, totals);
+        return;
+    }
+    DLRM_LAUNCH("radix_scan", k_radix_scan, dim3(1 << RB), dim3(256), 0, stream, counts, nblk, totals);
     if (NP == 3)
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
-                    nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<3, RB, false>), sgrid, dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
     else if (NP == 2)
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
-                    nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<2, RB, false>), sgrid, dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
     else
-        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB>), sgrid, dim3(256), 0, stream, io, n, shift, counts,
-                    nblk, totals);
+        DLRM_LAUNCH("radix_scatter", (k_radix_scatter<1, RB, false>), sgrid, dim3(256), 0, stream, io, n, shift,
+                    counts, nblk, totals);
 }
 
 }  // namespace

@@ -334,6 +334,14 @@ def test_adagrad_sort_passes(rows, label):
                 random_state=True, label=label)
 
 
+@pytest.mark.parametrize("B", [4096 * 16, 4096 * 16 + 1])
+def test_adagrad_sort_tiles_around_inline_scan(B):
+    """16 sort tiles (each scatter block adds up the raw tile counts itself) and 17 (a scan launch
+    per pass), with 17-bit keys (two passes)."""
+    run_adagrad([70000], 4, "f32", B, "onehot", True, seed=B % 1000, random_state=True,
+                label=f"{B} lookups: {(B + 4095) // 4096} sort tiles")
+
+
 def test_adagrad_long_segments_cross_chunks():
     """One row hit by every lookup: one segment over ~150 chunks (finisher path)."""
     run_adagrad([50], 128, "f32", 2000, "multi", True, seed=11, max_len=10, hot=3, label="hot-f32")
