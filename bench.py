@@ -796,10 +796,32 @@ def time_full_step(tabs, states, batches, host_batches, steps, wl, max_nnz):
 
     ms_one = region(False)
     ms = region(True)
+    # the same steps (sort on the second stream) replayed as HIP graphs, one captured per batch
+    # after the regions above have run every call once (hipBLASLt picks its algorithms on a
+    # shape's first call, which must not happen inside a capture)
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(torch.cuda.current_stream(dev))
+    graphs = []
+    for i in range(len(batches)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            run(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) / steps * 1e3
+    del graphs
     dims_b = [(16, 512), (512, 256), (256, wl.D)]
     dims_t = [(m.Ip, 1024), (1024, 1024), (1024, 512), (512, 256), (256, 1)]
     flops = 3 * 2 * wl.B * sum(k * n for k, n in dims_b + dims_t)  # forward + two backward GEMMs
     return {"ms_per_step": ms, "samples_per_s": wl.B / (ms / 1e3), "ms_per_step_one_stream": ms_one,
+            "ms_per_step_graph": ms_graph, "samples_per_s_graph": wl.B / (ms_graph / 1e3),
             "dense_gemm_tflop_per_step": flops / 1e12,
             "loss_after": float(m.head_out["loss"].item()),
             "layers": "bottom 13(16)-512-256-128, top 480-1024-1024-512-256-1, bf16 GEMMs (hipBLASLt), fp32 accumulation"}
