@@ -132,60 +132,112 @@ __global__ __launch_bounds__(256) void k_colsum(const float *__restrict__ partia
 
 // ---------------------------------------------------------------- sigmoid head + BCE
 
-constexpr int kHeadCPL = kHeadMaxK / kWave;  // columns per lane (at most)
-
 // Layout of the head's partials: [kHeadBlocks][K + 2] (dw columns, then db, then loss).
+// Lane l holds the CPL consecutive columns l*CPL .. l*CPL+CPL-1 of a row (one vector access of
+// 2*CPL bytes of x, 4*CPL of dx); CPL = K/64 rounded up to a power of two.  K % 8 == 0, so for
+// CPL >= 8 each 8-column piece is either wholly inside the row or wholly past it, and for CPL <= 4
+// a lane's columns are all inside iff its first one is.  Each wave takes kHeadRows rows at once
+// (its grid-stride rows m, m + nw, ...), whose loads are in flight together.
+constexpr int kHeadRows = 4;
+
+template <int CPL>
+__device__ __forceinline__ void head_load(const uint16_t *p, int lane, int32_t K, float *x) {
+    const int c0 = lane * CPL;
+    if constexpr (CPL >= 8) {
+#pragma unroll
+        for (int j = 0; j < CPL / 8; ++j) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c0 + 8 * j < K) v = *reinterpret_cast<const uint4 *>(p + c0 + 8 * j);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * j + 2 * e] = __uint_as_float(q[e] << 16);
+                x[8 * j + 2 * e + 1] = __uint_as_float(q[e] & 0xffff0000u);
+            }
+        }
+    } else if constexpr (CPL == 4) {
+        uint2 v = make_uint2(0, 0);
+        if (c0 < K) v = *reinterpret_cast<const uint2 *>(p + c0);
+        x[0] = __uint_as_float(v.x << 16), x[1] = __uint_as_float(v.x & 0xffff0000u);
+        x[2] = __uint_as_float(v.y << 16), x[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else if constexpr (CPL == 2) {
+        uint32_t v = 0;
+        if (c0 < K) v = *reinterpret_cast<const uint32_t *>(p + c0);
+        x[0] = __uint_as_float(v << 16), x[1] = __uint_as_float(v & 0xffff0000u);
+    } else {
+        x[0] = c0 < K ? bf16_to_f32(p[c0]) : 0.f;
+    }
+}
+
+template <int CPL>
 __global__ __launch_bounds__(256) void k_bce_head(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                   const float *__restrict__ b, const float *__restrict__ t,
                                                   int64_t M, int32_t K, float *__restrict__ p,
                                                   float *__restrict__ dx, float *__restrict__ partial) {
     __shared__ float red[4][kHeadMaxK + 2];
     const int lane = threadIdx.x & 63, wv = static_cast<int>(wave_id());
+    const int c0 = lane * CPL;
     const float bias = b[0];
     const float invM = 1.0f / static_cast<float>(M);
-    float wl[kHeadCPL], dwl[kHeadCPL];
+    float wl[CPL], dwl[CPL];
+    head_load<CPL>(w, lane, K, wl);
 #pragma unroll
-    for (int i = 0; i < kHeadCPL; ++i) {
-        const int c = lane + i * kWave;
-        wl[i] = c < K ? bf16_to_f32(w[c]) : 0.f;
-        dwl[i] = 0.f;
-    }
+    for (int i = 0; i < CPL; ++i) dwl[i] = 0.f;
     float dbl = 0.f, lossl = 0.f;
     const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
-    for (int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + wv; m < M; m += nw) {  // wave-uniform
-        const uint16_t *xr = x + static_cast<uint64_t>(m) * K;
-        float xv[kHeadCPL];
-        float z = 0.f;
+    for (int64_t m0 = static_cast<int64_t>(blockIdx.x) * 4 + wv; m0 < M; m0 += nw * kHeadRows) {  // wave-uniform
+        float xv[kHeadRows][CPL], z[kHeadRows], tm[kHeadRows];
 #pragma unroll
-        for (int i = 0; i < kHeadCPL; ++i) {
-            const int c = lane + i * kWave;
-            xv[i] = c < K ? bf16_to_f32(xr[c]) : 0.f;
-            z = fmaf(xv[i], wl[i], z);
+        for (int r = 0; r < kHeadRows; ++r) {  // rows past M re-read the last row; their results are dropped
+            const int64_t m = min(m0 + r * nw, M - 1);
+            head_load<CPL>(x + static_cast<uint64_t>(m) * K, lane, K, xv[r]);
+            tm[r] = t[m];
         }
 #pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1) z += __shfl_xor(z, sh);  // every lane: the same bits
-        z += bias;
-        const float tm = t[m];
-        const float pm = 1.0f / (1.0f + expf(-z));
-        const float loss = fmaxf(z, 0.f) - z * tm + log1pf(expf(-fabsf(z)));
-        const float dz = (pm - tm) * invM;
-        if (lane == 0) p[m] = pm;
-        float *dxr = dx + static_cast<uint64_t>(m) * K;
+        for (int r = 0; r < kHeadRows; ++r) {
+            float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < kHeadCPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < K) dxr[c] = dz * wl[i];
-            dwl[i] = fmaf(dz, xv[i], dwl[i]);
+            for (int i = 0; i < CPL; ++i) s = fmaf(xv[r][i], wl[i], s);
+            z[r] = s;
         }
-        dbl += dz;
-        lossl += loss;
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1)
+#pragma unroll
+            for (int r = 0; r < kHeadRows; ++r) z[r] += __shfl_xor(z[r], sh);  // every lane: the same bits
+#pragma unroll
+        for (int r = 0; r < kHeadRows; ++r) {
+            const int64_t m = m0 + r * nw;
+            if (m >= M) break;  // wave-uniform
+            const float zr = z[r] + bias;
+            const float pm = 1.0f / (1.0f + expf(-zr));
+            const float loss = fmaxf(zr, 0.f) - zr * tm[r] + log1pf(expf(-fabsf(zr)));
+            const float dz = (pm - tm[r]) * invM;
+            if (lane == 0) p[m] = pm;
+            float *dxr = dx + static_cast<uint64_t>(m) * K + c0;
+            float o[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                o[i] = dz * wl[i];
+                dwl[i] = fmaf(dz, xv[r][i], dwl[i]);
+            }
+            if constexpr (CPL >= 4) {
+#pragma unroll
+                for (int j = 0; j < CPL / 4; ++j)
+                    if (c0 + 4 * j < K)
+                        *reinterpret_cast<float4 *>(dxr + 4 * j) = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+            } else if constexpr (CPL == 2) {
+                if (c0 < K) *reinterpret_cast<float2 *>(dxr) = make_float2(o[0], o[1]);
+            } else {
+                if (c0 < K) dxr[0] = o[0];
+            }
+            dbl += dz;
+            lossl += loss;
+        }
     }
     // combine the block's 4 waves in order, then write the block's partials
 #pragma unroll
-    for (int i = 0; i < kHeadCPL; ++i) {
-        const int c = lane + i * kWave;
-        if (c < K) red[wv][c] = dwl[i];
-    }
+    for (int i = 0; i < CPL; ++i)
+        if (c0 + i < K) red[wv][c0 + i] = dwl[i];
     if (lane == 0) {
         red[wv][K] = dbl;
         red[wv][K + 1] = lossl;
@@ -197,7 +249,6 @@ __global__ __launch_bounds__(256) void k_bce_head(const uint16_t *__restrict__ x
     }
 }
 
-// dw[c], db, loss = sums over the blocks' partials (loss divided by M); one wavefront per column.
 __global__ __launch_bounds__(256) void k_bce_final(const float *__restrict__ partial, int32_t nblk, int32_t K,
                                                    int64_t M, float *__restrict__ dw, float *__restrict__ db,
                                                    float *__restrict__ loss) {
@@ -524,7 +575,16 @@ extern "C" int dlrm_bce_head(const uint16_t *x, const uint16_t *w, const float *
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < dlrm_bce_head_workspace_size(M, K))
         return DLRM_ERR_WORKSPACE;
     float *partial = static_cast<float *>(workspace);
-    DLRM_LAUNCH("bce_head", k_bce_head, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    if (K <= 64)
+        DLRM_LAUNCH("bce_head", k_bce_head<1>, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    else if (K <= 128)
+        DLRM_LAUNCH("bce_head", k_bce_head<2>, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    else if (K <= 256)
+        DLRM_LAUNCH("bce_head", k_bce_head<4>, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    else if (K <= 512)
+        DLRM_LAUNCH("bce_head", k_bce_head<8>, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
+    else
+        DLRM_LAUNCH("bce_head", k_bce_head<16>, dim3(kHeadBlocks), dim3(256), 0, stream, x, w, b, t, M, K, p, dx, partial);
     DLRM_LAUNCH("bce_final", k_bce_final, dim3((K + 2 + 3) / 4), dim3(256), 0, stream, partial, kHeadBlocks, K, M,
                 dw, db, loss);
     return launch_status();

@@ -97,7 +97,8 @@ def test_linear_fwd_bwd(M, K, N, act, ydt):
             assert dx_d is None
 
 
-@pytest.mark.parametrize("M,K", [(1, 8), (300, 256), (16384, 256), (1000, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 8), (300, 256), (16384, 256), (1000, 1024), (2051, 64), (257, 120),
+                                 (777, 200), (4099, 512), (130, 520), (5, 1016)])
 def test_bce_head(M, K):
     rng = np.random.default_rng(M * 7 + K)
     x_d, x = bf16_pair(np.maximum(rng.standard_normal((M, K)), 0))
