@@ -12,9 +12,11 @@
 //   - SGD on fp32 master weights refreshing their bf16 copies, and a row cast / pad.
 #include <hipblaslt/hipblaslt.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 
 #include "common.h"
 #include "dlrm_mlp.h"
@@ -304,21 +306,77 @@ __global__ __launch_bounds__(256) void k_sgd_dense_multi(SgdMulti a) {
     }
 }
 
-template <int ST, int DT>
-__global__ __launch_bounds__(256) void k_cast_rows(const void *__restrict__ src, int64_t src_ld, int64_t M,
-                                                   int32_t cols, void *__restrict__ dst, int32_t dst_cols) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= M * dst_cols) return;
-    const int64_t m = i / dst_cols;
-    const int32_t c = static_cast<int32_t>(i - m * dst_cols);
-    float v = 0.f;
-    if (c < cols) {
-        const uint64_t s = static_cast<uint64_t>(m) * src_ld + c;
-        v = ST == DLRM_F32 ? static_cast<const float *>(src)[s] : bf16_to_f32(static_cast<const uint16_t *>(src)[s]);
-    }
-    if constexpr (DT == DLRM_F32) static_cast<float *>(dst)[i] = v;
-    else static_cast<uint16_t *>(dst)[i] = f32_to_bf16(v);
+// Block (bx, by) casts columns [by*1024, by*1024 + 1024) of its rows; its 256 threads are G column
+// groups (G = 256, or a narrower row's (dst_cols + 3) / 4) times RL = 256 / G row lanes, and lane j
+// takes the rows bx*RL*NR + j + RL*u, u < NR, all NR rows' loads in flight together (NR = 8, fewer
+// for narrow rows so the launch keeps enough blocks).  Columns from `cols` to dst_cols are zero.
+// VEC (dst_cols % 4 == 0, 16-byte aligned dst): group g holds 4 consecutive columns, stored as one
+// vector; otherwise group g holds columns g, g + G, g + 2G, g + 3G, so each scalar access of the
+// wavefront is contiguous.
+constexpr int kCastRowsPerLane = 8;
+
+inline int32_t cast_groups(int32_t dst_cols) { return std::min((dst_cols + 3) / 4, 256); }
+inline int cast_rows_per_lane(int32_t dst_cols) {
+    const int RL = 256 / cast_groups(dst_cols);
+    return RL >= 64 ? 1 : std::min(kCastRowsPerLane, 64 / RL);
 }
+
+template <int ST, int DT, bool VEC>
+__global__ __launch_bounds__(256) void k_cast_rows(const void *__restrict__ src, int64_t src_ld, int64_t M,
+                                                   int32_t cols, void *__restrict__ dst, int32_t dst_cols,
+                                                   int32_t rows_per_lane) {
+    constexpr int R = kCastRowsPerLane;
+    const int32_t G = min((dst_cols + 3) / 4, 256);
+    const int RL = 256 / G;
+    const int tid = threadIdx.x, j = tid / G, g = tid % G;
+    if (j >= RL) return;  // no barrier follows
+    const int32_t t0 = static_cast<int32_t>(blockIdx.y) * 1024;
+    int32_t col[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) col[e] = t0 + (VEC ? 4 * g + e : g + e * G);
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RL * rows_per_lane + j;
+    float v[R][4];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t m = r0 + static_cast<int64_t>(u) * RL;
+        const bool row = u < rows_per_lane && m < M;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[u][e] = 0.f;
+            if (row && col[e] < cols) {
+                const uint64_t s = static_cast<uint64_t>(m) * src_ld + col[e];
+                v[u][e] = ST == DLRM_F32 ? static_cast<const float *>(src)[s]
+                                         : bf16_to_f32(static_cast<const uint16_t *>(src)[s]);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t m = r0 + static_cast<int64_t>(u) * RL;
+        if (u >= rows_per_lane || m >= M) break;
+        const uint64_t d = static_cast<uint64_t>(m) * dst_cols;
+        if constexpr (VEC) {
+            if (col[0] < dst_cols) {
+                if constexpr (DT == DLRM_F32) {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(dst) + d + col[0]) =
+                        make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                } else {
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + d + col[0]) = make_uint2(
+                        static_cast<uint32_t>(f32_to_bf16(v[u][0])) | (static_cast<uint32_t>(f32_to_bf16(v[u][1])) << 16),
+                        static_cast<uint32_t>(f32_to_bf16(v[u][2])) | (static_cast<uint32_t>(f32_to_bf16(v[u][3])) << 16));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (col[e] >= dst_cols) continue;
+                if constexpr (DT == DLRM_F32) static_cast<float *>(dst)[d + col[e]] = v[u][e];
+                else static_cast<uint16_t *>(dst)[d + col[e]] = f32_to_bf16(v[u][e]);
+            }
+        }
+    }
+}
+
 
 // ---------------------------------------------------------------- hipBLASLt
 
@@ -636,14 +694,26 @@ extern "C" int dlrm_cast_rows(const void *src, int32_t src_dtype, int64_t src_ld
     const int64_t total = M * dst_cols;
     if (total == 0) return DLRM_OK;
     if (!src || !dst || total >= (int64_t(1) << 40)) return DLRM_ERR_INVALID_ARG;
-    const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
-    if (src_dtype == DLRM_F32 && dst_dtype == DLRM_BF16)
-        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_F32, DLRM_BF16>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
-    else if (src_dtype == DLRM_F32)
-        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_F32, DLRM_F32>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
-    else if (dst_dtype == DLRM_BF16)
-        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_BF16, DLRM_BF16>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
-    else
-        DLRM_LAUNCH("cast_rows", (k_cast_rows<DLRM_BF16, DLRM_F32>), grid, dim3(256), 0, stream, src, src_ld, M, cols, dst, dst_cols);
+    const int rpl = cast_rows_per_lane(dst_cols);
+    const int64_t rows_per_block = static_cast<int64_t>(256 / cast_groups(dst_cols)) * rpl;
+    const int64_t row_blocks = (M + rows_per_block - 1) / rows_per_block;
+    if (row_blocks >= (int64_t(1) << 31)) return DLRM_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<uint32_t>(row_blocks), static_cast<uint32_t>((dst_cols + 1023) / 1024));
+    const bool vec = dst_cols % 4 == 0 && aligned(dst, 16);
+    auto go = [&](auto st, auto dt) {
+        constexpr int ST = decltype(st)::value, DT = decltype(dt)::value;
+        if (vec)
+            DLRM_LAUNCH("cast_rows", (k_cast_rows<ST, DT, true>), grid, dim3(256), 0, stream, src, src_ld, M, cols,
+                        dst, dst_cols, rpl);
+        else
+            DLRM_LAUNCH("cast_rows", (k_cast_rows<ST, DT, false>), grid, dim3(256), 0, stream, src, src_ld, M, cols,
+                        dst, dst_cols, rpl);
+    };
+    using F = std::integral_constant<int, DLRM_F32>;
+    using H = std::integral_constant<int, DLRM_BF16>;
+    if (src_dtype == DLRM_F32 && dst_dtype == DLRM_BF16) go(F{}, H{});
+    else if (src_dtype == DLRM_F32) go(F{}, F{});
+    else if (dst_dtype == DLRM_BF16) go(H{}, H{});
+    else go(H{}, F{});
     return launch_status();
 }

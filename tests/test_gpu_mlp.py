@@ -151,6 +151,31 @@ def test_sgd_dense_and_cast_rows():
     assert np.array_equal(crop.cpu().numpy(), a)
 
 
+@pytest.mark.parametrize("M,src_ld,cols,dst_cols,sdt,ddt", [
+    (70000, 13, 13, 16, "f32", "bf16"),   # more rows than the grid's 65535: each block takes several
+    (5, 7, 3, 5, "bf16", "f32"),          # odd destination width: element stores
+    (300, 104, 100, 100, "bf16", "bf16"),
+    (1, 1, 1, 1, "f32", "f32"),
+    (33, 480, 479, 480, "f32", "f32")])
+def test_cast_rows_shapes(M, src_ld, cols, dst_cols, sdt, ddt):
+    rng = np.random.default_rng(M + cols)
+    a = rng.standard_normal((M, src_ld)).astype(np.float32)
+    if sdt == "bf16":
+        src, a64 = bf16_pair(a)
+        a = a64.astype(np.float32)
+    else:
+        src = to_dev(a)
+    say(f"[mlp] cast rows M={M} {sdt}[{src_ld}] -> {ddt}[{dst_cols}] ({cols} columns)")
+    out = dlrm_cast_rows(src, cols, dst_cols, torch.bfloat16 if ddt == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    want = np.zeros((M, dst_cols), np.float32)
+    want[:, :cols] = a[:, :cols]
+    if ddt == "bf16":
+        assert np.array_equal(to_host(out), synth.f32_to_bf16_bits(want))
+    else:
+        assert np.array_equal(out.cpu().numpy(), want)
+
+
 def test_sgd_dense_multi_equals_single():
     """One launch over many parameters (sizes 0, 1, ragged, several blocks) gives the bits of the
     per-parameter call."""
