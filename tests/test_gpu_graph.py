@@ -81,3 +81,60 @@ def test_step_graph_replays_match_eager():
         got = state(batches[i]["nnz"])
         for k, (a, b) in enumerate(zip(ref, got)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: tensor {k} differs"
+
+
+def test_full_step_graph_replays_match_eager():
+    """The full DLRM step (bottom and top MLPs through hipBLASLt, the sparse path, the embedding
+    backward's sort on a second stream, SGD and Adagrad) recorded as a HIP graph per batch, after
+    every call has run once eagerly (hipBLASLt picks its algorithms on a shape's first call).  Each
+    replay starts from the parameters, tables and states of an eager step of the same batch and
+    must leave them, the loss and the predictions bit-identical."""
+    from recommendation_model_sparse_amd.dlrm_step import DlrmStep
+    from recommendation_model_sparse_amd.synth import Workload
+    from gpu_util import device_tables
+
+    wl = Workload(name="graph-step", seed=99, T=4, D=32, dtype="bf16", B=256, rows=[500, 7000, 40, 3000],
+                  init="hash", bags="geom", bag_lo=1, bag_hi=12, bag_mean=4.0, dist="zipf", alpha=1.05)
+    host = [wl.batch(i) for i in range(2)]
+    tabs = device_tables(wl)
+    states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
+    m = DlrmStep(tabs, states, wl.B, 13, bottom=[32, 32], top=[64, 16], lr_dense=0.05, lr_emb=0.01, eps=1e-8,
+                 seed=3, max_nnz=max(b.nnz for b in host), overlap=True)
+    inputs = [(to_dev(b.indices), to_dev(b.offsets), to_dev(b.features(13)), to_dev(b.labels())) for b in host]
+
+    def tensors():
+        layers = m.bottom + m.top + [m.head]
+        return [t for l in layers for t in (l.W32, l.W16, l.b)] + m.tables + m.states
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+    def snapshot():
+        return [t.clone() for t in tensors()] + [m.head_out["loss"].clone(), m.head_out["p"].clone()]
+
+    for i in range(2):
+        m.step(*inputs[i])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for i in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            m.step(*inputs[i])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep, i in enumerate([0, 1, 1, 0]):
+        say(f"[graph] full step replay {rep} of batch {i}")
+        start = [t.clone() for t in tensors()]
+        m.step(*inputs[i])
+        torch.cuda.synchronize()
+        ref = snapshot()
+        for t, c in zip(tensors(), start):
+            t.copy_(c)
+        torch.cuda.synchronize()
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(bits(a), bits(b)), f"replay {rep}: tensor {k} differs from the eager step"
