@@ -205,9 +205,9 @@ def gather_entry(wl, workload: str, kernel: str, ms: float, nnz: float) -> dict:
 def bench_forward(wl, workload: str, dev, steps: int, rotate: int, probe_gather: bool = False):
     """Lookup alone, the interaction alone, the two calls, and the fused call (HIP events)."""
     import torch
-    from recommendation_model_sparse_amd import dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
+    from recommendation_model_sparse_amd import TableSet, dlrm_interact_fwd, emb_bag_fwd, emb_bag_interact_fwd
     t0 = time.time()
-    tabs = device_tables(wl, dev)
+    tabs = TableSet(device_tables(wl, dev))
     batches, _ = device_batches(wl, dev, rotate)
     pooled = torch.empty((wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
     inter = torch.empty((wl.B, wl.P + wl.D), dtype=torch.float32, device=dev)
@@ -301,10 +301,11 @@ def bench_train_onehot(wl, dev, steps: int, rotate: int):
     """The training step on the one-hot fp32 shapes: lookup, interaction forward and backward, and
     the embedding backward with row-wise Adagrad in place (no integer outputs requested)."""
     import torch
-    from recommendation_model_sparse_amd import (dlrm_interact_bwd, dlrm_interact_fwd, emb_bag_bwd_adagrad,
+    from recommendation_model_sparse_amd import (TableSet, dlrm_interact_bwd, dlrm_interact_fwd, emb_bag_bwd_adagrad,
                                                  emb_bag_bwd_workspace_size, emb_bag_fwd)
-    tabs = device_tables(wl, dev)
     states = [torch.zeros(v, dtype=torch.float32, device=dev) for v in wl.rows]
+    # checked once; each call then only re-reads the tensors' pointers and row counts
+    tabs = TableSet(device_tables(wl, dev), states)
     batches, _ = device_batches(wl, dev, rotate, grads=True)
     nb = len(batches)
     max_nnz = max(b["nnz"] for b in batches)
@@ -425,7 +426,7 @@ def cpu_baseline(wl, batches, n_samples: int, min_seconds: float = 10.0, one_cor
 
 def bench_headline(args, dev):
     import torch
-    from recommendation_model_sparse_amd import (DLRM_OPT_ADAGRAD, AdagradOutputs, dlrm_interact_bwd,
+    from recommendation_model_sparse_amd import (DLRM_OPT_ADAGRAD, AdagradOutputs, TableSet, dlrm_interact_bwd,
                                                  dlrm_interact_fwd, emb_bag_bwd_adagrad, emb_bag_bwd_apply,
                                                  emb_bag_bwd_plan, emb_bag_bwd_workspace_size, emb_bag_fwd)
     from recommendation_model_sparse_amd.configs import make_config
@@ -433,8 +434,9 @@ def bench_headline(args, dev):
     wl = make_config(3)
     log(f"[bench] workload {wl.name}: {wl.note}")
     t0 = time.time()
-    tabs = device_tables(wl, dev)
     states = [torch.zeros(v, dtype=torch.float32, device=dev) for v in wl.rows]
+    # checked once; each call then only re-reads the tensors' pointers and row counts
+    tabs = TableSet(device_tables(wl, dev), states)
     torch.cuda.synchronize()
     log(f"[bench] tables {wl.table_bytes() / 1e9:.2f} GB filled in {time.time() - t0:.1f}s")
     batches, host_batches = device_batches(wl, dev, 1 if args.only == "multihot-uniform" else args.rotate,

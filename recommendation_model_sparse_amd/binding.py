@@ -116,20 +116,25 @@ def _ptr(t: Optional[torch.Tensor]):
 # Every wrapper therefore checks each tensor (type, dtype, exact shape, contiguity, one CUDA device,
 # workspace and output sizes) and raises ValueError before it calls the library.
 
-def _need(t, name: str, dtype=None, shape=None, min_numel: Optional[int] = None) -> torch.Tensor:
+def _need(t, name, dtype=None, shape=None, min_numel: Optional[int] = None) -> torch.Tensor:
+    """`name` is a string, or a callable giving it (only called to word an error)."""
     if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        raise TypeError(f"{_name(name)} must be a torch.Tensor, got {type(t).__name__}")
     if dtype is not None:
         ok = dtype if isinstance(dtype, tuple) else (dtype,)
         if t.dtype not in ok:
-            raise ValueError(f"{name} must be {' or '.join(str(d) for d in ok)}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
-        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+            raise ValueError(f"{_name(name)} must be {' or '.join(str(d) for d in ok)}, got {t.dtype}")
+    if shape is not None and t.shape != shape:  # torch.Size compares with a tuple of ints
+        raise ValueError(f"{_name(name)} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
     if min_numel is not None and t.numel() < min_numel:
-        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+        raise ValueError(f"{_name(name)} must hold at least {min_numel} elements, got {t.numel()}")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+        raise ValueError(f"{_name(name)} must be contiguous")
     return t
+
+
+def _name(name) -> str:
+    return name() if callable(name) else name
 
 
 def _opt(t, name: str, dtype=None, shape=None, min_numel: Optional[int] = None):
@@ -181,8 +186,71 @@ def _states(state, tables, required: bool):
     if len(state) != len(tables):
         raise ValueError("one state vector per table")
     for i, (st, t) in enumerate(zip(state, tables)):
-        _need(st, f"state[{i}]", torch.float32, (t.shape[0],))
+        _need(st, lambda: f"state[{i}]", torch.float32, (t.shape[0],))
     return (ctypes.c_void_p * len(state))(*[st.data_ptr() for st in state])
+
+
+class TableSet:
+    """Tables, and optionally their row-wise Adagrad states, checked once for repeated calls.
+
+    Every wrapper that takes a list of tables also takes a TableSet, and then takes its states
+    when its `state` argument is None or the set's own list.  The per-call checks then reduce to
+    re-reading the tensors' data pointers and row counts; if one changed (a tensor replaced in the
+    set's lists, re-allocated or resized), the set is checked again in full before the call.  It
+    behaves as the sequence of its tables."""
+
+    def __init__(self, tables: Sequence[torch.Tensor], states: Optional[Sequence[torch.Tensor]] = None):
+        # the caller's own lists are kept (not copies), so passing that state list to a call is
+        # recognized as the set's, and a tensor swapped into either list is seen by the next call
+        self.tables = tables if isinstance(tables, list) else list(tables)
+        self.states = None if states is None else (states if isinstance(states, list) else list(states))
+        self._build()
+
+    def _pointers(self):
+        return ([t.data_ptr() for t in self.tables] + [t.shape[0] for t in self.tables] +
+                [s.data_ptr() for s in (self.states or ())] + [s.shape[0] for s in (self.states or ())])
+
+    def _build(self):
+        self.T, self.D, self.code, self.ptrs, self.rows = _tables(self.tables)
+        self.row_counts = [int(t.shape[0]) for t in self.tables]
+        self.sptrs = None if self.states is None else _states(self.states, self.tables, True)
+        self.device = _device(*self.tables, *(self.states or ()))
+        self._key = self._pointers()
+
+    def refresh(self) -> "TableSet":
+        if self._pointers() != self._key:
+            self._build()
+        return self
+
+    def __len__(self):
+        return len(self.tables)
+
+    def __iter__(self):
+        return iter(self.tables)
+
+    def __getitem__(self, i):
+        return self.tables[i]
+
+
+def _prepared(tables, state=None, need_state=False, with_state=False):
+    """(T, D, dtype code, table pointers, row counts as C array and as list, state pointers, the
+    tensors whose device the call must check) of a table list or a TableSet."""
+    if isinstance(tables, TableSet):
+        tables.refresh()
+        sptrs, extra = None, ()
+        if with_state:
+            if state is None or state is tables.states:
+                if tables.sptrs is None and need_state:
+                    raise ValueError("row-wise Adagrad needs one state vector per table")
+                sptrs = tables.sptrs
+            else:
+                sptrs, extra = _states(state, tables.tables, need_state), tuple(state)
+        return (tables.T, tables.D, tables.code, tables.ptrs, tables.rows, tables.row_counts, sptrs,
+                (tables.tables[0],) + extra)
+    T, D, code, ptrs, rows = _tables(tables)
+    sptrs = _states(state, tables, need_state) if with_state else None
+    dev_tensors = tuple(tables) + (tuple(state) if with_state and state is not None else ())
+    return T, D, code, ptrs, rows, [int(t.shape[0]) for t in tables], sptrs, dev_tensors
 
 
 def _batch(T: int, indices, offsets, per_sample_weights, index_dtypes=(torch.int64,)):
@@ -224,10 +292,10 @@ def emb_bag_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, offsets: 
                 per_sample_weights: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
     """Pooled embeddings [B, T, D] fp32 (C: emb_bag_fwd)."""
-    T, D, code, ptrs, rows = _tables(tables)
+    T, D, code, ptrs, rows, _, _, dt = _prepared(tables)
     indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
     out = _opt(out, "out", torch.float32, (B, T, D))
-    dev = _device(*tables, indices, offsets, w, out)
+    dev = _device(*dt, indices, offsets, w, out)
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     _check(lib().emb_bag_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
@@ -240,14 +308,14 @@ def emb_bag_fwd_ex(tables: Sequence[torch.Tensor], indices: torch.Tensor, offset
                    out_dtype: torch.dtype = torch.float32, flags: int = 0) -> torch.Tensor:
     """Pooled embeddings [B, T, D] in out_dtype (fp32 or bf16), int64 or int32 indices and
     offsets (C: emb_bag_fwd_ex)."""
-    T, D, code, ptrs, rows = _tables(tables)
+    T, D, code, ptrs, rows, _, _, dt = _prepared(tables)
     indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
                                                 (torch.int64, torch.int32))
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     ocode = DLRM_F32 if out_dtype == torch.float32 else DLRM_BF16
     out = _opt(out, "out", out_dtype, (B, T, D))
-    dev = _device(*tables, indices, offsets, w, out)
+    dev = _device(*dt, indices, offsets, w, out)
     if out is None:
         out = torch.empty((B, T, D), dtype=out_dtype, device=dev)
     _check(lib().emb_bag_fwd_ex(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B,
@@ -297,12 +365,12 @@ def emb_bag_interact_fwd(tables: Sequence[torch.Tensor], indices: torch.Tensor, 
                          per_sample_weights: Optional[torch.Tensor], dense: torch.Tensor,
                          out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
     """[B, N(N-1)/2 + D] fp32, N = T + 1: lookup fused with the interaction (C: emb_bag_interact_fwd)."""
-    T, D, code, ptrs, rows = _tables(tables)
+    T, D, code, ptrs, rows, _, _, dt = _prepared(tables)
     indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
     _need(dense, "dense", torch.float32, (B, D))
     N = T + 1
     out = _opt(out, "out", torch.float32, (B, N * (N - 1) // 2 + D))
-    dev = _device(*tables, indices, offsets, w, dense, out)
+    dev = _device(*dt, indices, offsets, w, dense, out)
     if out is None:
         out = torch.empty((B, N * (N - 1) // 2 + D), dtype=torch.float32, device=dev)
     _check(lib().emb_bag_interact_fwd(ptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B,
@@ -362,15 +430,15 @@ def emb_bag_bwd_adagrad(tables: Sequence[torch.Tensor], state: Sequence[torch.Te
                         per_sample_weights: Optional[torch.Tensor], grad_pooled: torch.Tensor,
                         lr: float, eps: float, workspace: Optional[torch.Tensor] = None,
                         outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
-    """Row-wise Adagrad on the tables and states, in place (C: emb_bag_bwd_adagrad)."""
-    T, D, code, ptrs, rows = _tables(tables)
-    sptrs = _states(state, tables, True)
+    """Row-wise Adagrad on the tables and states, in place (C: emb_bag_bwd_adagrad); `state` may
+    be None when `tables` is a TableSet with states."""
+    T, D, code, ptrs, rows, counts, sptrs, dt = _prepared(tables, state, True, True)
     indices, offsets, w, _, B, nnz = _batch(T, indices, offsets, per_sample_weights)
     _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
     o = _outputs(outputs, nnz)
-    need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
+    need = emb_bag_bwd_workspace_size(counts, D, B, nnz)
     workspace = _opt(workspace, "workspace", torch.uint8, min_numel=need)
-    dev = _device(*tables, *state, indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
+    dev = _device(*dt, indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
     workspace = _workspace(workspace, need, dev)
     _check(lib().emb_bag_bwd_adagrad(
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), _ptr(w), B, nnz,
@@ -387,15 +455,14 @@ def emb_bag_bwd_update(tables: Sequence[torch.Tensor], state: Optional[Sequence[
                        flags: int = 0) -> Optional[AdagradOutputs]:
     """Embedding backward with DLRM_OPT_ADAGRAD (state required) or DLRM_OPT_SGD (state may be
     None), int64 or int32 indices and offsets (C: emb_bag_bwd_update)."""
-    T, D, code, ptrs, rows = _tables(tables)
-    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    T, D, code, ptrs, rows, counts, sptrs, dt = _prepared(tables, state, optimizer == DLRM_OPT_ADAGRAD, True)
     indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
                                                 (torch.int64, torch.int32))
     _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
     o = _outputs(outputs, nnz)
-    need = emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz)
+    need = emb_bag_bwd_workspace_size(counts, D, B, nnz)
     workspace = _opt(workspace, "workspace", torch.uint8, min_numel=need)
-    dev = _device(*tables, *(state or ()), indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
+    dev = _device(*dt, indices, offsets, w, grad_pooled, workspace, *_out_tensors(o))
     workspace = _workspace(workspace, need, dev)
     _check(lib().emb_bag_bwd_update(
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
@@ -415,13 +482,12 @@ def emb_bag_bwd_update_noalloc(tables: Sequence[torch.Tensor], state: Optional[S
                                outputs: Optional[AdagradOutputs] = None, flags: int = 0) -> Optional[AdagradOutputs]:
     """emb_bag_bwd_update with the library's fixed per-GPU scratch as the workspace: allocates
     nothing (C: emb_bag_bwd_update_noalloc).  Calls that overlap on one GPU race."""
-    T, D, code, ptrs, rows = _tables(tables)
-    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    T, D, code, ptrs, rows, _, sptrs, dt = _prepared(tables, state, optimizer == DLRM_OPT_ADAGRAD, True)
     indices, offsets, w, icode, B, nnz = _batch(T, indices, offsets, per_sample_weights,
                                                 (torch.int64, torch.int32))
     _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
     o = _outputs(outputs, nnz)
-    dev = _device(*tables, *(state or ()), indices, offsets, w, grad_pooled, *_out_tensors(o))
+    dev = _device(*dt, indices, offsets, w, grad_pooled, *_out_tensors(o))
     _check(lib().emb_bag_bwd_update_noalloc(
         ptrs, sptrs, rows, T, D, code, _ptr(indices), _ptr(offsets), icode, _ptr(w), B, nnz,
         _ptr(grad_pooled), int(optimizer), float(lr), float(eps), *_out_ptrs(o), flags, _stream(dev)),
@@ -452,16 +518,14 @@ def emb_bag_bwd_apply(tables: Sequence[torch.Tensor], state: Optional[Sequence[t
                       workspace: torch.Tensor, outputs: Optional[AdagradOutputs] = None) -> None:
     """The update half of the embedding backward from a planned workspace (C: emb_bag_bwd_apply);
     `outputs` is the plan's, when it was given one (its segment offsets are read)."""
-    T, D, code, ptrs, rows = _tables(tables)
-    sptrs = _states(state, tables, optimizer == DLRM_OPT_ADAGRAD)
+    T, D, code, ptrs, rows, counts, sptrs, dt = _prepared(tables, state, optimizer == DLRM_OPT_ADAGRAD, True)
     B, nnz = int(B), int(nnz)
     _need(grad_pooled, "grad_pooled", torch.float32, (B, T, D))
     seg = None
     if outputs is not None:
         seg = _need(outputs.segment_offsets, "outputs.segment_offsets", torch.int64, min_numel=nnz + 1)
-    _need(workspace, "workspace", torch.uint8,
-          min_numel=emb_bag_bwd_workspace_size([t.shape[0] for t in tables], D, B, nnz))
-    dev = _device(*tables, *(state or ()), grad_pooled, workspace, seg)
+    _need(workspace, "workspace", torch.uint8, min_numel=emb_bag_bwd_workspace_size(counts, D, B, nnz))
+    dev = _device(*dt, grad_pooled, workspace, seg)
     _check(lib().emb_bag_bwd_apply(
         ptrs, sptrs, rows, T, D, code, B, nnz, 1 if weighted else 0, _ptr(grad_pooled), int(optimizer),
         float(lr), float(eps), _ptr(workspace), workspace.numel(), _ptr(seg), _stream(dev)),

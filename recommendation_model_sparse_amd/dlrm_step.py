@@ -56,6 +56,9 @@ class DlrmStep:
                  bottom: Sequence[int], top: Sequence[int], lr_dense: float, lr_emb: float, eps: float,
                  seed: int, max_nnz: int, overlap: bool = True):
         self.tables, self.states = list(tables), list(states)
+        # the tables and states checked once for the step's calls (each call re-reads only their
+        # pointers and row counts)
+        self.tabset = L.TableSet(self.tables, self.states)
         # overlap: the batch-only half of the embedding backward (key sort and segments) runs on a
         # second stream while the top MLP and interaction backward run on the caller's stream
         self.overlap = overlap
@@ -120,7 +123,7 @@ class DlrmStep:
         for i, layer in enumerate(self.bottom):
             L.dlrm_linear_fwd(x, layer.W16, layer.b, L.DLRM_ACT_RELU, y=self.hb[i], workspace=self.ws)
             x = self.hb[i]
-        L.emb_bag_fwd(self.tables, idx, off, None, out=self.pooled)
+        L.emb_bag_fwd(self.tabset, idx, off, None, out=self.pooled)
         L.dlrm_interact_fwd(self.hb[-1], self.pooled, out=self.inter)
         L.dlrm_cast_rows(self.inter, self.I, self.Ip, torch.bfloat16, dst=self.t0)
         x = self.t0
@@ -157,10 +160,10 @@ class DlrmStep:
         L.dlrm_interact_bwd(self.dinter, self.hb[-1], self.pooled, grad_dense=self.gdense, grad_pooled=self.gpooled)
         if self.overlap:
             main.wait_event(self.plan_done)
-            L.emb_bag_bwd_apply(self.tables, self.states, B, idx.numel(), False, self.gpooled, L.DLRM_OPT_ADAGRAD,
+            L.emb_bag_bwd_apply(self.tabset, self.states, B, idx.numel(), False, self.gpooled, L.DLRM_OPT_ADAGRAD,
                                 self.lr_emb, self.eps, self.emb_ws, outputs=outputs)
         else:
-            L.emb_bag_bwd_adagrad(self.tables, self.states, idx, off, None, self.gpooled, self.lr_emb, self.eps,
+            L.emb_bag_bwd_adagrad(self.tabset, self.states, idx, off, None, self.gpooled, self.lr_emb, self.eps,
                                   workspace=self.emb_ws, outputs=outputs)
         dy = self.gdense
         ins = [self.x0] + self.hb[:-1]

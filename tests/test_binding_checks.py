@@ -171,3 +171,74 @@ def test_dense_layer_checks():
     bad("CUDA", L.dlrm_cast_rows, src, 13, 16, bf16)
     bad("cols", L.dlrm_cast_rows, src, 14, 16, bf16)
     bad("dst must have shape", L.dlrm_cast_rows, src, 13, 16, bf16, dst=torch.zeros(M, 15, dtype=bf16))
+
+
+class _Recorder:
+    """Stands in for the library and records each call's arguments (size queries answer)."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        if name.endswith("workspace_size"):
+            return lambda *a: 1024
+
+        def call(*a):
+            self.calls.append((name, a))
+            return 0
+        return call
+
+
+def test_table_set_rejects_what_the_list_form_rejects():
+    bad("CUDA", L.TableSet, tables())                     # CPU tensors
+    bad("one dtype", L.TableSet, tables()[:2] + [torch.zeros(V, D, dtype=bf16)])
+
+
+def test_table_set_caches_and_rechecks_moved_tensors(monkeypatch):
+    """With the device check and stream lookup opened to CPU tensors (the library recorded, never
+    run), a TableSet hands the same pointers the list form does, takes its own states when the call
+    passes none, and checks itself again when a tensor it holds was re-allocated."""
+    rec = _Recorder()
+    monkeypatch.setattr(L, "_lib", rec)
+    monkeypatch.setattr(L, "_device", lambda *ts: torch.device("cpu"))
+    monkeypatch.setattr(L, "_stream", lambda dev: None)
+    tabs = tables()
+    states = [torch.zeros(V) for _ in range(T)]
+    s = L.TableSet(tabs, states)
+    idx, off = batch()
+    grad = torch.zeros(B, T, D)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+
+    def table_ptrs(call):
+        return [p for p in call[1][0]]
+
+    L.emb_bag_fwd(tabs, idx, off, out=torch.zeros(B, T, D))
+    L.emb_bag_fwd(s, idx, off, out=torch.zeros(B, T, D))
+    assert table_ptrs(rec.calls[0]) == table_ptrs(rec.calls[1]) == [t.data_ptr() for t in tabs]
+    L.emb_bag_bwd_adagrad(s, None, idx, off, None, grad, 0.01, 1e-8, workspace=ws)
+    assert [p for p in rec.calls[-1][1][1]] == [x.data_ptr() for x in states]
+    other = [torch.zeros(V) for _ in range(T)]
+    L.emb_bag_bwd_adagrad(s, other, idx, off, None, grad, 0.01, 1e-8, workspace=ws)
+    assert [p for p in rec.calls[-1][1][1]] == [x.data_ptr() for x in other]
+    bad("state", L.emb_bag_bwd_adagrad, s, other[:2], idx, off, None, grad, 0.01, 1e-8, workspace=ws)
+    # a table and its state re-allocated in place: the next call sees their new pointers and rows
+    tabs[1].resize_(3 * V, D)
+    states[1].resize_(3 * V)
+    L.emb_bag_fwd(s, idx, off, out=torch.zeros(B, T, D))
+    assert table_ptrs(rec.calls[-1]) == [t.data_ptr() for t in tabs]
+    assert [r for r in rec.calls[-1][1][1]] == [V, 3 * V, V]
+    # shrunk in place (same pointers): the row counts are read again too
+    tabs[1].resize_(2 * V, D)
+    states[1].resize_(2 * V)
+    L.emb_bag_fwd(s, idx, off, out=torch.zeros(B, T, D))
+    assert [r for r in rec.calls[-1][1][1]] == [V, 2 * V, V]
+    # a table re-allocated without its state: the set's own check fails before any call
+    n = len(rec.calls)
+    tabs[1].resize_(4 * V, D)
+    bad("state", L.emb_bag_fwd, s, idx, off, out=torch.zeros(B, T, D))
+    bad("state", L.emb_bag_bwd_adagrad, s, None, idx, off, None, grad, 0.01, 1e-8, workspace=ws)
+    assert len(rec.calls) == n
+    # a table set without states cannot run Adagrad unless the call brings them
+    s2 = L.TableSet(tables())
+    bad("state", L.emb_bag_bwd_adagrad, s2, None, idx, off, None, grad, 0.01, 1e-8, workspace=ws)
+    assert len(rec.calls) == n
