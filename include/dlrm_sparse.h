@@ -300,8 +300,8 @@ int emb_bag_bwd_apply(void *const *tables, float *const *state, const int64_t *r
  * kept until the process ends); the results are emb_bag_bwd_update's, bit for bit.
  *   Arguments: as emb_bag_bwd_update, without the workspace.
  *   A batch whose workspace (emb_bag_bwd_workspace_size) exceeds the array is refused with
- *   DLRM_ERR_WORKSPACE before anything is enqueued (at D = 128 about 1.1M lookups fit; the
- *   one-hot training batch of 26 tables x 2048 samples needs 3 MB).
+ *   DLRM_ERR_WORKSPACE before anything is enqueued (at D = 128 about 1.17M lookups fit; the
+ *   one-hot training batch of 26 tables x 2048 samples needs 3.7 MiB).
  *   Every call on one GPU uses that GPU's single array: calls that overlap in time on one GPU
  *   (two streams, two host threads) race, and the caller must order them.  The first call on a
  *   device looks the array's address up there; no call allocates memory.
