@@ -588,6 +588,7 @@ def bench_headline(args, dev):
     dom = max(kern_ms, key=lambda k: kern_ms[k])
     dk = kernels.get(dom)
     traffic = measured_traffic(dom, "multihot-bf16-zipf")
+    floor = gradient_gather_floor(wl, batches[0], gpooled, args.steps) if dom == "seg_reduce_adagrad" else None
     lk = lookup_kernel(kern)
     res = {
         "metric": "samples/sec + gathered-embedding GB/s (fraction of HBM peak), 1 MI355X",
@@ -631,7 +632,12 @@ def bench_headline(args, dev):
                      "traffic_GBps": traffic["bytes"] / (kern_launch_ms[dom] / 1e3) / 1e9 if traffic else None,
                      "ms_per_launch": kern_launch_ms[dom],
                      "requested_bytes_per_launch": requested.get(dom),
-                     "algorithmic_bytes_per_launch": dk["algorithmic_bytes"] if dk else None},
+                     "algorithmic_bytes_per_launch": dk["algorithmic_bytes"] if dk else None,
+                     # the kernel's own gradient-row loads alone, read with no other work in the
+                     # same order (a probe gather): what this access pattern costs on the GPU
+                     "gradient_gather_floor": floor,
+                     "frac_of_gradient_gather_floor":
+                         floor["sorted_order_ms"] / kern_launch_ms[dom] if floor else None},
         "kernels": kernels,
     }
     res.update(extras)
@@ -697,6 +703,33 @@ def bench_multihot_uniform(wl3, dev, args, tabs, states, ws, outs, pooled, inter
 
 
 # ---------------------------------------------------------------- headline extras (inference, variants, full step)
+
+def gradient_gather_floor(wl, b, grad_pooled, steps):
+    """How fast the GPU reads the segment reduce's gradient rows in its own order and nothing else:
+    dlrm_probe_gather over the pooled gradient [B*T, D] (fp32) at the grad-row index of every
+    lookup, (i) in stable key-sorted order, as the segment reduce walks them, and (ii) in lookup
+    order, where a bag's row repeats for each of its lookups (cache hits: the request rate's
+    floor).  The index sequences are built here with torch (measurement only)."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_probe_gather
+    dev = grad_pooled.device
+    T, B = wl.T, wl.B
+    idx, off = b["idx"], b["off"]
+    bag = torch.repeat_interleave(torch.arange(T * B, device=dev), off[1:] - off[:-1])
+    t, s = bag // B, bag % B
+    base = torch.tensor(np.concatenate([[0], np.cumsum(wl.rows)[:-1]]), dtype=torch.int64, device=dev)
+    grow = (s * T + t).contiguous()
+    sorted_grow = grow[torch.argsort(base[t] + idx, stable=True)].contiguous()
+    table = grad_pooled.view(B * T, wl.D)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    out = {}
+    for name, g in (("sorted_order_ms", sorted_grow), ("lookup_order_ms", grow)):
+        out[name] = ev_ms(lambda i: dlrm_probe_gather(table, g, sink), 1, steps, warm=3)
+    out["rows"] = int(grow.numel())
+    out["row_bytes"] = wl.D * 4
+    del bag, t, s, grow, sorted_grow
+    return out
+
 
 def time_inference(tabs, batches, steps, pooled, inter):
     """Mean ms of emb_bag_interact_fwd and of emb_bag_fwd + dlrm_interact_fwd (HIP events)."""
