@@ -642,6 +642,10 @@ def bench_headline(args, dev):
     }
     res.update(extras)
     gat = gather_entry(wl, "multihot-bf16-zipf", lk, kern_launch_ms[lk], nnz_avg)
+    # the lookup's row reads alone, in its own order: what that access pattern costs on the GPU
+    fl = row_gather_floor(wl, batches[0], args.steps)
+    gat["row_gather_floor"] = fl
+    gat["frac_of_row_gather_floor"] = fl["ms"] / kern_launch_ms[lk]
 
     # the same step with uniform rows: the cache-cold control of the lookup and the backward
     uni = gat_u = None
@@ -728,6 +732,29 @@ def gradient_gather_floor(wl, b, grad_pooled, steps):
     out["rows"] = int(grow.numel())
     out["row_bytes"] = wl.D * 4
     del bag, t, s, grow, sorted_grow
+    return out
+
+
+def row_gather_floor(wl, b, steps):
+    """The lookup's row reads alone: dlrm_probe_gather over one buffer that holds all T tables one
+    after another (its contents do not matter), at every lookup's global row (table base + index)
+    in lookup order; it reads the indices and the rows and writes nothing (the lookup also writes
+    the pooled output).  The index sequence is built here with torch (measurement only)."""
+    import torch
+    from recommendation_model_sparse_amd import dlrm_probe_gather
+    idx, off = b["idx"], b["off"]
+    dev = idx.device
+    T, B = wl.T, wl.B
+    big = torch.empty((int(sum(wl.rows)), wl.D), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32,
+                      device=dev)
+    t = torch.repeat_interleave(torch.arange(T * B, device=dev) // B, off[1:] - off[:-1])
+    base = torch.tensor(np.concatenate([[0], np.cumsum(wl.rows)[:-1]]), dtype=torch.int64, device=dev)
+    gidx = (base[t] + idx).contiguous()
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    ms = ev_ms(lambda i: dlrm_probe_gather(big, gidx, sink), 1, steps, warm=3)
+    out = {"ms": ms, "rows": int(gidx.numel()), "row_bytes": wl.D * wl.elem_size}
+    del big, gidx, t
+    torch.cuda.empty_cache()
     return out
 
 
