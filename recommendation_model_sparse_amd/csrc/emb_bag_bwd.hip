@@ -320,15 +320,33 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t *__restrict__
     for (int d = threadIdx.x; d < NBK; d += 256) counts[d * nblk + tile] = h[d];
 }
 
-// Block d: exclusive scan of counts[d][0..nblk) in place; totals[d] = row sum.
+// Block d: exclusive scan of counts[d][0..nblk) in place; totals[d] = row sum.  Thread i takes
+// the consecutive entries [i*per, i*per + per); up to 16 of them stay in registers between the
+// sum and the prefix (one round of loads), more are loaded again for the prefix.
 __global__ __launch_bounds__(256) void k_radix_scan(uint32_t *__restrict__ counts, uint32_t nblk,
                                                     uint32_t *__restrict__ totals) {
+    constexpr uint32_t KR = 16;
     uint32_t *row = counts + static_cast<size_t>(blockIdx.x) * nblk;
     const uint32_t per = (nblk + 255) / 256;
     const uint32_t b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
     uint32_t tot;
-    const uint32_t run = block_exclusive_scan(range_sum<16>(row, b0, b1), &tot);
-    range_exclusive<16>(row, b0, b1, run);
+    if (per <= KR) {  // block-uniform
+        uint32_t v[KR], sum = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < KR; ++k) v[k] = row[min(b0 + k, nblk - 1)];  // clamped in bounds
+#pragma unroll
+        for (uint32_t k = 0; k < KR; ++k) sum += b0 + k < b1 ? v[k] : 0u;
+        uint32_t run = block_exclusive_scan(sum, &tot);  // its barrier orders every load before any store
+#pragma unroll
+        for (uint32_t k = 0; k < KR; ++k)
+            if (b0 + k < b1) {
+                row[b0 + k] = run;
+                run += v[k];
+            }
+    } else {
+        const uint32_t run = block_exclusive_scan(range_sum<16>(row, b0, b1), &tot);
+        range_exclusive<16>(row, b0, b1, run);
+    }
     if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
