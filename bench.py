@@ -24,7 +24,8 @@ The same JSON line also carries:
                     [--only SECTION]
 
 --only runs one section and prints its object (for profiling runs): headline, tiny, onehot,
-multihot-uniform, bigtables-uniform, bigtables-zipf, train-onehot, probes, interaction, inference.
+multihot-uniform, bigtables-uniform, bigtables-zipf, train-onehot, probes, interaction, inference,
+full-step.
 """
 from __future__ import annotations
 
@@ -41,7 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 SECTIONS = ("headline", "tiny", "onehot", "multihot-uniform", "bigtables-uniform", "bigtables-zipf",
-            "train-onehot", "probes", "interaction", "inference")
+            "train-onehot", "probes", "interaction", "inference", "full-step")
 
 
 def traffic_profile(workload: str) -> str:
@@ -491,6 +492,10 @@ def bench_headline(args, dev):
         # the uniform control alone (its counter profile must hold no Zipf launches)
         uni, gat_u = bench_multihot_uniform(wl, dev, args, tabs, states, ws, outs, pooled, inter, gdense, gpooled)
         return None, None, uni, gat_u, None
+    if args.only == "full-step":
+        # the full DLRM training step alone (for its kernel profile)
+        gpu_spinup(dev)
+        return time_full_step(tabs, states, batches, host_batches, args.steps, wl, max_nnz), None, None, None, None
     if args.only == "inference":
         # the fused lookup + interaction against the two calls alone (for its counter profiles)
         gpu_spinup(dev)
@@ -968,8 +973,11 @@ def main():
     only = args.only
     out = {}
     configs, gather = {}, {}
-    if only in (None, "headline", "multihot-uniform", "inference"):
+    if only in (None, "headline", "multihot-uniform", "inference", "full-step"):
         res, gat, uni, gat_u, cpu = bench_headline(args, dev)
+        if only == "full-step":
+            print(json.dumps({"full_step": res}), flush=True)
+            return
         if only == "inference":
             print(json.dumps({"inference": res}), flush=True)
             return
