@@ -113,23 +113,25 @@ __global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy,
 }
 
 // Sum over blocks of partial[blk][c] (row stride `ld`) for column c: one wavefront per column;
-// lane l adds blocks l, l+64, ... in order, then a fixed butterfly adds the 64 lane sums.
+// lane l adds blocks l, l+64, ... in order, then a fixed butterfly adds the 64 lane sums.  A lane's
+// blocks are loaded CU at a time (clamped in bounds) before they are added, so CU of them make one
+// round trip together; the order of the additions is the same.
 __device__ __forceinline__ float wave_colsum(const float *__restrict__ partial, int32_t nblk, int64_t ld,
                                              int64_t c) {
+    constexpr int CU = 8;
     const int lane = threadIdx.x & 63;
     float s = 0.f;
-    for (int32_t k = lane; k < nblk; k += kWave) s += partial[static_cast<uint64_t>(k) * ld + c];
+    for (int32_t k0 = lane; k0 < nblk; k0 += CU * kWave) {
+        float v[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) v[u] = partial[static_cast<uint64_t>(min(k0 + u * kWave, nblk - 1)) * ld + c];
+#pragma unroll
+        for (int u = 0; u < CU; ++u)
+            if (k0 + u * kWave < nblk) s += v[u];
+    }
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) s += __shfl_xor(s, sh);
     return s;
-}
-
-__global__ __launch_bounds__(256) void k_colsum(const float *__restrict__ partial, int32_t nblk, int32_t N,
-                                                float *__restrict__ out) {
-    const int32_t c = blockIdx.x * 4 + static_cast<int32_t>(wave_id());
-    if (c >= N) return;  // wave-uniform
-    const float s = wave_colsum(partial, nblk, N, c);
-    if ((threadIdx.x & 63) == 0) out[c] = s;
 }
 
 // ---------------------------------------------------------------- sigmoid head + BCE
@@ -512,14 +514,31 @@ int dw_split(int64_t M) {
     return s;
 }
 
-// out[i] = sum over s of part[s][i], slices in order.
-__global__ __launch_bounds__(256) void k_sum_slices(const float *__restrict__ part, int32_t S, int64_t n,
-                                                    float *__restrict__ out) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+// The two sums that end a layer's backward, in one launch.  Blocks [0, ncb): the bias gradient,
+// db[c] = sum over the row blocks of partial[blk][c], one column per wavefront (four per block).
+// Blocks past them: the weight gradient, dW[i] = sum over s of part[s][i] (slices in order, all S
+// loaded before the first add), 256 elements per block; none when S == 1 (the GEMM wrote dW).
+__global__ __launch_bounds__(256) void k_grad_sums(const float *__restrict__ partial, int32_t nblk, int32_t N,
+                                                   float *__restrict__ db, uint32_t ncb,
+                                                   const float *__restrict__ part, int32_t S, int64_t n,
+                                                   float *__restrict__ dW) {
+    if (blockIdx.x < ncb) {  // block-uniform
+        const int32_t c = blockIdx.x * 4 + static_cast<int32_t>(wave_id());
+        if (c >= N) return;  // wave-uniform
+        const float s = wave_colsum(partial, nblk, N, c);
+        if ((threadIdx.x & 63) == 0) db[c] = s;
+        return;
+    }
+    const int64_t i = static_cast<int64_t>(blockIdx.x - ncb) * 256 + threadIdx.x;
     if (i >= n) return;
-    float s = part[i];
-    for (int32_t q = 1; q < S; ++q) s += part[static_cast<uint64_t>(q) * n + i];
-    out[i] = s;
+    float v[kMaxSplit];
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q) v[q] = part[static_cast<uint64_t>(min(q, S - 1)) * n + i];
+    float s = v[0];
+#pragma unroll
+    for (int q = 1; q < kMaxSplit; ++q)
+        if (q < S) s += v[q];
+    dW[i] = s;
 }
 
 bool layer_dims_ok(int64_t M, int32_t N, int32_t K) {
@@ -587,7 +606,6 @@ extern "C" int dlrm_linear_bwd(const float *dy, const void *y, int32_t y_dtype, 
     } else {
         DLRM_LAUNCH("relu_grad", (k_relu_grad<false, DLRM_F32>), grid, dim3(256), 0, stream, dy, y, M, N, dz_bf16, partial);
     }
-    DLRM_LAUNCH("colsum", k_colsum, dim3((N + 3) / 4), dim3(256), 0, stream, partial, nblk, N, db);
     if (hipGetLastError() != hipSuccess) return DLRM_ERR_HIP;
     int rc;
     if (dx) {
@@ -599,21 +617,22 @@ extern "C" int dlrm_linear_bwd(const float *dy, const void *y, int32_t y_dtype, 
     // row-major dW[N][K] = dz^T x  <=>  column-major dW^T (K x N) = x^T(K x M, stored as x) dz (M x N);
     // split over S slices of the rows (a strided batch), then the slices summed in order
     const int S = dw_split(M);
+    float *part = nullptr;
     if (S == 1) {
         rc = lt_gemm(stream, false, true, K, N, M, x, K, dz_bf16, N, dW, HIP_R_32F, nullptr, false, workspace,
                      kGemmScratch);
     } else {
         const int64_t Ms = M / S;
-        float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kGemmScratch + partials_bytes(M, N));
+        part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kGemmScratch + partials_bytes(M, N));
         rc = lt_gemm(stream, false, true, K, N, Ms, x, K, dz_bf16, N, part, HIP_R_32F, nullptr, false, workspace,
                      kGemmScratch, S, Ms * K, Ms * N, static_cast<int64_t>(K) * N);
-        if (rc == DLRM_OK) {
-            const int64_t n = static_cast<int64_t>(K) * N;
-            DLRM_LAUNCH("sum_slices", k_sum_slices, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream,
-                        part, S, n, dW);
-        }
     }
     if (rc != DLRM_OK) return rc;
+    // the bias gradient's column sums and (split GEMM) the sum of the slices
+    const uint32_t ncb = static_cast<uint32_t>((N + 3) / 4);
+    const int64_t n = S > 1 ? static_cast<int64_t>(K) * N : 0;
+    DLRM_LAUNCH("grad_sums", k_grad_sums, dim3(ncb + static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream,
+                partial, nblk, N, db, ncb, part, S, n, dW);
     return launch_status();
 }
 
