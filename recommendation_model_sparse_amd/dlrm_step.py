@@ -59,8 +59,10 @@ class DlrmStep:
         # the tables and states checked once for the step's calls (each call re-reads only their
         # pointers and row counts)
         self.tabset = L.TableSet(self.tables, self.states)
-        # overlap: the batch-only half of the embedding backward (key sort and segments) runs on a
-        # second stream while the top MLP and interaction backward run on the caller's stream
+        # overlap: a second stream takes the bottom MLP's forward (beside the lookup), the
+        # batch-only half of the embedding backward (key sort and segments, beside the top MLP's
+        # and the interaction's backward) and the bottom MLP's backward (beside the embedding
+        # update); events order each against the caller's stream
         self.overlap = overlap
         dev = self.tables[0].device
         self.dev = dev
@@ -112,18 +114,26 @@ class DlrmStep:
         self.emb_ws = torch.empty(L.emb_bag_bwd_workspace_size(rows, self.D, B, max_nnz), dtype=torch.uint8, device=dev)
         self.side = torch.cuda.Stream(device=dev)  # default priority
         self.plan_done = torch.cuda.Event()
+        self.dense_ready = torch.cuda.Event()
+        self.bottom_fwd_done = torch.cuda.Event()
+        self.bottom_done = torch.cuda.Event()
 
     def _mat(self, flat: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
         return flat[:rows * cols].view(rows, cols)
 
     def forward(self, idx: torch.Tensor, off: torch.Tensor, dense_x: torch.Tensor, labels: torch.Tensor):
-        B = self.B
-        L.dlrm_cast_rows(dense_x, self.F, self.Fp, torch.bfloat16, dst=self.x0)
-        x = self.x0
-        for i, layer in enumerate(self.bottom):
-            L.dlrm_linear_fwd(x, layer.W16, layer.b, L.DLRM_ACT_RELU, y=self.hb[i], workspace=self.ws)
-            x = self.hb[i]
-        L.emb_bag_fwd(self.tabset, idx, off, None, out=self.pooled)
+        if self.overlap:
+            # the bottom MLP runs on the second stream while the lookup runs here
+            main = torch.cuda.current_stream(self.dev)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                self._bottom_forward(dense_x)
+                self.bottom_fwd_done.record(self.side)
+            L.emb_bag_fwd(self.tabset, idx, off, None, out=self.pooled)
+            main.wait_event(self.bottom_fwd_done)
+        else:
+            self._bottom_forward(dense_x)
+            L.emb_bag_fwd(self.tabset, idx, off, None, out=self.pooled)
         L.dlrm_interact_fwd(self.hb[-1], self.pooled, out=self.inter)
         L.dlrm_cast_rows(self.inter, self.I, self.Ip, torch.bfloat16, dst=self.t0)
         x = self.t0
@@ -159,12 +169,38 @@ class DlrmStep:
         L.dlrm_cast_rows(dy, self.I, self.I, torch.float32, dst=self.dinter)  # drop the pad column
         L.dlrm_interact_bwd(self.dinter, self.hb[-1], self.pooled, grad_dense=self.gdense, grad_pooled=self.gpooled)
         if self.overlap:
+            # the bottom MLP's backward needs only the dense gradient: it runs on the second stream
+            # (after the sort) while the embedding update runs here; the two share no buffer
+            self.dense_ready.record(main)
             main.wait_event(self.plan_done)
             L.emb_bag_bwd_apply(self.tabset, self.states, B, idx.numel(), False, self.gpooled, L.DLRM_OPT_ADAGRAD,
                                 self.lr_emb, self.eps, self.emb_ws, outputs=outputs)
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(self.dense_ready)
+                self._bottom_backward(bufs)
+                self.bottom_done.record(self.side)
+            main.wait_event(self.bottom_done)
         else:
             L.emb_bag_bwd_adagrad(self.tabset, self.states, idx, off, None, self.gpooled, self.lr_emb, self.eps,
                                   workspace=self.emb_ws, outputs=outputs)
+            self._bottom_backward(bufs)
+        # SGD on every dense parameter, in one launch
+        params = []
+        for layer in self.bottom + self.top:
+            params += [(layer.W32, layer.W16, layer.dW), (layer.b, None, layer.db)]
+        h = self.head
+        params += [(h.W32.view(-1), h.W16.view(-1), self.head_out["dw"]), (h.b, None, self.head_out["db"])]
+        L.dlrm_sgd_dense_multi(params, self.lr_dense)
+
+    def _bottom_forward(self, dense_x):
+        L.dlrm_cast_rows(dense_x, self.F, self.Fp, torch.bfloat16, dst=self.x0)
+        x = self.x0
+        for i, layer in enumerate(self.bottom):
+            L.dlrm_linear_fwd(x, layer.W16, layer.b, L.DLRM_ACT_RELU, y=self.hb[i], workspace=self.ws)
+            x = self.hb[i]
+
+    def _bottom_backward(self, bufs):
+        B = self.B
         dy = self.gdense
         ins = [self.x0] + self.hb[:-1]
         for i in range(len(self.bottom) - 1, -1, -1):
@@ -175,13 +211,6 @@ class DlrmStep:
                               dz_bf16=self._mat(self.dz, B, layer.W16.shape[0]), dx=dx, dW=layer.dW, db=layer.db,
                               workspace=self.ws)
             dy = dx
-        # SGD on every dense parameter, in one launch
-        params = []
-        for layer in self.bottom + self.top:
-            params += [(layer.W32, layer.W16, layer.dW), (layer.b, None, layer.db)]
-        h = self.head
-        params += [(h.W32.view(-1), h.W16.view(-1), self.head_out["dw"]), (h.b, None, self.head_out["db"])]
-        L.dlrm_sgd_dense_multi(params, self.lr_dense)
 
     def step(self, idx, off, dense_x, labels, outputs=None):
         out = self.forward(idx, off, dense_x, labels)

@@ -217,3 +217,34 @@ def test_full_training_step(overlap):
         f"gate {worst[2]} * 2^-8)")
     del tabs, states
     torch.cuda.empty_cache()
+
+
+def test_overlapped_step_matches_one_stream():
+    """The step with the sort and the bottom MLP's backward on a second stream, against the same
+    model stepped on one stream: every kernel and its order within each stream are the same, so
+    two steps leave every dense parameter, table row and state bit for bit equal (a missing wait
+    between the streams would let a kernel read a buffer before it is written, or after it is
+    reused)."""
+    wl = Workload(name="ovl", seed=99, T=6, D=64, dtype="bf16", B=2048,
+                  rows=[5000, 300, 80000, 17, 4096, 1200], init="hash", bags="geom",
+                  bag_lo=1, bag_hi=24, bag_mean=6.0, dist="zipf", alpha=1.05)
+    batches = [wl.batch(i) for i in range(2)]
+    models = []
+    for overlap in (True, False):
+        tabs = device_tables(wl)
+        states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
+        m = DlrmStep(tabs, states, wl.B, 13, bottom=[128, 64], top=[256, 128, 64], lr_dense=0.05, lr_emb=0.01,
+                     eps=1e-8, seed=11, max_nnz=max(b.nnz for b in batches), overlap=overlap)
+        say(f"[step] overlap={overlap} B={wl.B} nnz={[b.nnz for b in batches]}")
+        for b in batches:
+            m.step(to_dev(b.indices), to_dev(b.offsets), to_dev(b.features(13)), to_dev(b.labels()))
+        torch.cuda.synchronize()
+        models.append((m, tabs, states))
+    (a, ta, sa), (c, tc, sc) = models
+    for la, lc in zip(a.bottom + a.top + [a.head], c.bottom + c.top + [c.head]):
+        assert torch.equal(la.W32, lc.W32) and torch.equal(la.b, lc.b) and torch.equal(la.W16, lc.W16)
+    for t in range(wl.T):
+        assert torch.equal(ta[t], tc[t]), f"table {t}"
+        assert torch.equal(sa[t], sc[t]), f"state {t}"
+    del models, a, c, ta, tc, sa, sc
+    torch.cuda.empty_cache()
