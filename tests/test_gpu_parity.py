@@ -366,6 +366,16 @@ def test_adagrad_batches_on_both_chunk_lengths():
     run_adagrad([30, 100000], 16, "f32", 131071, "onehot", True, seed=24, label="2^18 - 2 lookups: short chunks")
 
 
+def test_adagrad_64_tables():
+    """64 tables (the limit), from one row to a few thousand each, with empty bags: every table's
+    row base in the keys, and tables whose keys are all one value."""
+    rng = np.random.default_rng(31)
+    rows = [int(x) for x in rng.integers(1, 3000, 64)]
+    rows[5] = rows[40] = 1
+    run_adagrad(rows, 16, "f32", 300, "multi", True, seed=31, max_len=8, label="T64 f32")
+    run_adagrad(rows, 64, "bf16", 300, "multi", False, seed=32, max_len=8, label="T64 bf16")
+
+
 def test_adagrad_onehot_and_zipf_like():
     run_adagrad([100000, 20, 3000], 128, "f32", 4000, "onehot", False, seed=13, label="onehot")
     run_adagrad([5, 6, 7], 16, "f32", 3000, "multi", True, seed=14, max_len=40, label="few rows")

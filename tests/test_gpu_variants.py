@@ -161,3 +161,30 @@ def test_update_int32_equals_int64(opt, dtype, weighted):
     assert U == int(ob.num_unique.item())
     for f in ("unique_keys", "segment_offsets", "sorted_pos"):
         assert torch.equal(getattr(oa, f)[:U], getattr(ob, f)[:U])
+
+
+def test_sgd_int32_64_tables():
+    """64 tables (the limit) with int32 indices and offsets and empty bags, against the oracle's
+    SGD step: integer outputs bit for bit, rows within the bf16 row gate."""
+    rng = np.random.default_rng(41)
+    rows = [int(x) for x in rng.integers(1, 2000, 64)]
+    B = 200
+    tables, _, (idx, off, w, gp), new, _, outs = run_update(rows, 32, "bf16", B, "multi", True, 41, DLRM_OPT_SGD,
+                                                            True, max_len=8, label="T64 int32")
+    r = oracle.emb_bag_bwd_sgd(tables, idx, off, w, B, gp, 0.01)
+    U = int(outs.num_unique.item())
+    assert U == r.U
+    assert np.array_equal(outs.unique_keys.cpu().numpy()[:U], r.unique_keys)
+    assert np.array_equal(outs.segment_offsets.cpu().numpy()[:U + 1], r.seg_offsets)
+    assert np.array_equal(outs.sorted_pos.cpu().numpy()[:len(idx)], r.perm)
+    tt, rr = r.table_and_row()
+    for t in range(len(rows)):
+        sel = tt == t
+        touched = np.zeros(rows[t], dtype=bool)
+        touched[rr[sel]] = True
+        assert np.array_equal(new[t][~touched].view(np.uint8), tables[t][~touched].view(np.uint8))
+        if not sel.any():
+            continue
+        got, ref = as_f64(new[t][rr[sel]]), r.new_rows[sel]
+        tol = bf16_half_ulp(ref) * 1.0001 + 1e-4 * np.max(np.abs(ref), axis=1, keepdims=True)
+        assert np.all(np.abs(got - ref) <= tol)
