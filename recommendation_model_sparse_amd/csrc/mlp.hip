@@ -114,19 +114,19 @@ __global__ __launch_bounds__(256) void k_relu_grad(const float *__restrict__ dy,
 
 // Sum over blocks of partial[blk][c] (row stride `ld`) for column c: one wavefront per column;
 // lane l adds blocks l, l+64, ... in order, then a fixed butterfly adds the 64 lane sums.  A lane's
-// blocks are loaded CU at a time (clamped in bounds) before they are added, so CU of them make one
+// blocks are loaded LB at a time (clamped in bounds) before they are added, so LB of them make one
 // round trip together; the order of the additions is the same.
 __device__ __forceinline__ float wave_colsum(const float *__restrict__ partial, int32_t nblk, int64_t ld,
                                              int64_t c) {
-    constexpr int CU = 8;
+    constexpr int LB = 8;
     const int lane = threadIdx.x & 63;
     float s = 0.f;
-    for (int32_t k0 = lane; k0 < nblk; k0 += CU * kWave) {
-        float v[CU];
+    for (int32_t k0 = lane; k0 < nblk; k0 += LB * kWave) {
+        float v[LB];
 #pragma unroll
-        for (int u = 0; u < CU; ++u) v[u] = partial[static_cast<uint64_t>(min(k0 + u * kWave, nblk - 1)) * ld + c];
+        for (int u = 0; u < LB; ++u) v[u] = partial[static_cast<uint64_t>(min(k0 + u * kWave, nblk - 1)) * ld + c];
 #pragma unroll
-        for (int u = 0; u < CU; ++u)
+        for (int u = 0; u < LB; ++u)
             if (k0 + u * kWave < nblk) s += v[u];
     }
 #pragma unroll
