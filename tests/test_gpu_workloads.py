@@ -180,27 +180,29 @@ def test_workload_training_step():
     torch.cuda.empty_cache()
 
 
-def test_workload_multihot_backward():
+@pytest.mark.parametrize("weighted", [False, True])
+def test_workload_multihot_backward(weighted):
     """The timed backward at its full size: 26 bf16 tables (D = 128), B = 16384 multi-hot bags
     (~8.5M lookups, Zipf rows, so hot rows make segments over hundreds of chunks), row-wise Adagrad
-    in place with every integer output requested.  The gradient is a seeded stand-alone one (not the
-    GPU's interaction backward), so the oracle's inputs are all host-generated.  Integer outputs are
-    compared whole and bit-exactly; every touched row and state against the oracle."""
+    in place with every integer output requested; also with the workload's per-sample weights (the
+    weighted segment reduce).  The gradient is a seeded stand-alone one (not the GPU's interaction
+    backward), so the oracle's inputs are all host-generated.  Integer outputs are compared whole and
+    bit-exactly; every touched row and state against the oracle."""
     wl = make_config(3)
-    b = wl.batch(0)
+    b = wl.batch(1, weighted=True) if weighted else wl.batch(0)
     gp = b.grad_pooled()
     tabs = device_tables(wl)
     states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
-    say(f"[workload] {wl.name} multi-hot backward B={wl.B} nnz={b.nnz}")
+    say(f"[workload] {wl.name} multi-hot backward B={wl.B} nnz={b.nnz} weighted={weighted}")
     outs = AdagradOutputs(b.nnz, DEV)
-    emb_bag_bwd_adagrad(tabs, states, to_dev(b.indices), to_dev(b.offsets), None, to_dev(gp), wl.lr, wl.eps,
-                        outputs=outs)
+    emb_bag_bwd_adagrad(tabs, states, to_dev(b.indices), to_dev(b.offsets),
+                        to_dev(b.weights) if weighted else None, to_dev(gp), wl.lr, wl.eps, outputs=outs)
     torch.cuda.synchronize()
 
     sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
     host_tabs = subset_tables(wl, row_ids)
     r = oracle.emb_bag_bwd_adagrad(host_tabs, [np.zeros(len(x), np.float32) for x in row_ids], sub.indices,
-                                   sub.offsets, None, wl.B, gp, wl.lr, wl.eps)
+                                   sub.offsets, sub.weights, wl.B, gp, wl.lr, wl.eps)
     U = int(outs.num_unique.item())
     assert U == r.U
     assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
