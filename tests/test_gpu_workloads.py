@@ -16,11 +16,14 @@ import torch
 
 import oracle
 from recommendation_model_sparse_amd import (
+    DLRM_OPT_ADAGRAD,
+    DLRM_OPT_SGD,
     AdagradOutputs,
     dlrm_interact_bwd,
     dlrm_interact_fwd,
     dlrm_synth_fill_table,
     emb_bag_bwd_adagrad,
+    emb_bag_bwd_update,
     emb_bag_fwd,
     emb_bag_interact_fwd,
     synth,
@@ -180,29 +183,34 @@ def test_workload_training_step():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("weighted", [False, True])
-def test_workload_multihot_backward(weighted):
+@pytest.mark.parametrize("weighted,opt", [(False, DLRM_OPT_ADAGRAD), (True, DLRM_OPT_ADAGRAD), (False, DLRM_OPT_SGD)])
+def test_workload_multihot_backward(weighted, opt):
     """The timed backward at its full size: 26 bf16 tables (D = 128), B = 16384 multi-hot bags
     (~8.5M lookups, Zipf rows, so hot rows make segments over hundreds of chunks), row-wise Adagrad
     in place with every integer output requested; also with the workload's per-sample weights (the
-    weighted segment reduce).  The gradient is a seeded stand-alone one (not the GPU's interaction
-    backward), so the oracle's inputs are all host-generated.  Integer outputs are compared whole and
-    bit-exactly; every touched row and state against the oracle."""
+    weighted segment reduce), and the SGD update.  The gradient is a seeded stand-alone one (not the
+    GPU's interaction backward), so the oracle's inputs are all host-generated.  Integer outputs are
+    compared whole and bit-exactly; every touched row (and Adagrad state) against the oracle."""
+    adagrad = opt == DLRM_OPT_ADAGRAD
     wl = make_config(3)
     b = wl.batch(1, weighted=True) if weighted else wl.batch(0)
     gp = b.grad_pooled()
     tabs = device_tables(wl)
     states = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
-    say(f"[workload] {wl.name} multi-hot backward B={wl.B} nnz={b.nnz} weighted={weighted}")
+    say(f"[workload] {wl.name} multi-hot backward B={wl.B} nnz={b.nnz} weighted={weighted} opt={opt}")
     outs = AdagradOutputs(b.nnz, DEV)
-    emb_bag_bwd_adagrad(tabs, states, to_dev(b.indices), to_dev(b.offsets),
-                        to_dev(b.weights) if weighted else None, to_dev(gp), wl.lr, wl.eps, outputs=outs)
+    emb_bag_bwd_update(tabs, states if adagrad else None, to_dev(b.indices), to_dev(b.offsets),
+                       to_dev(b.weights) if weighted else None, to_dev(gp), opt, wl.lr, wl.eps if adagrad else 0.0,
+                       outputs=outs)
     torch.cuda.synchronize()
 
     sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
     host_tabs = subset_tables(wl, row_ids)
-    r = oracle.emb_bag_bwd_adagrad(host_tabs, [np.zeros(len(x), np.float32) for x in row_ids], sub.indices,
-                                   sub.offsets, sub.weights, wl.B, gp, wl.lr, wl.eps)
+    if adagrad:
+        r = oracle.emb_bag_bwd_adagrad(host_tabs, [np.zeros(len(x), np.float32) for x in row_ids], sub.indices,
+                                       sub.offsets, sub.weights, wl.B, gp, wl.lr, wl.eps)
+    else:
+        r = oracle.emb_bag_bwd_sgd(host_tabs, sub.indices, sub.offsets, sub.weights, wl.B, gp, wl.lr)
     U = int(outs.num_unique.item())
     assert U == r.U
     assert np.array_equal(outs.sorted_pos.cpu().numpy(), r.perm)
@@ -221,9 +229,10 @@ def test_workload_multihot_backward(weighted):
         got = as_f64(to_host(tabs[t][rows_t]))
         tol = bf16_half_ulp(ref) * 1.0001 + 1e-4 * np.max(np.abs(ref), axis=1, keepdims=True)
         assert np.all(np.abs(got - ref) <= tol), f"table {t}"
-        gs = states[t][rows_t].cpu().numpy().astype(np.float64)
-        rs = r.new_state[sel]
-        assert np.all(np.abs(gs - rs) <= 1e-4 * np.abs(rs)), f"table {t} state"
+        if adagrad:
+            gs = states[t][rows_t].cpu().numpy().astype(np.float64)
+            rs = r.new_state[sel]
+            assert np.all(np.abs(gs - rs) <= 1e-4 * np.abs(rs)), f"table {t} state"
         cand = np.setdiff1d(rng.integers(0, wl.rows[t], 512), row_ids[t])
         if len(cand):
             dc = torch.from_numpy(cand).to(DEV)
