@@ -90,6 +90,15 @@ def check_forward(wl, batch, tabs, n_samples=256):
     ierr = rel_err(igot, iref, iscale)
     say(f"   interaction max rel err {ierr:.3e}")
     assert ierr <= 1e-5
+    # its backward at full size, on the same pooled input and a seeded gradient of the output
+    g = (np.random.default_rng(wl.seed + 29).standard_normal((wl.B, wl.P + wl.D)) * 1e-3).astype(np.float32)
+    gd, gp = dlrm_interact_bwd(to_dev(g), dense, to_dev(pz))
+    torch.cuda.synchronize()
+    rd, rp, md, mp = oracle.interact_bwd(g[S], batch.dense[S], pz[S])
+    sel = torch.from_numpy(S).to(DEV)
+    berr = max(rel_err(gd[sel].cpu().numpy(), rd, md), rel_err(gp[sel].cpu().numpy(), rp, mp))
+    say(f"   interaction backward max rel err {berr:.3e}")
+    assert berr <= 1e-5
     return pooled, inter
 
 
