@@ -25,6 +25,7 @@ from recommendation_model_sparse_amd import (
     emb_bag_bwd_adagrad,
     emb_bag_bwd_update,
     emb_bag_fwd,
+    emb_bag_fwd_ex,
     emb_bag_interact_fwd,
     synth,
 )
@@ -72,6 +73,10 @@ def check_forward(wl, batch, tabs, n_samples=256):
     torch.cuda.synchronize()
     # the fused inference call runs the same arithmetic without the pooled round trip
     assert torch.equal(fused.view(torch.int32), inter.view(torch.int32)), "fused != two-call path"
+    # int32 indices and offsets: the same bits as int64
+    pooled32 = emb_bag_fwd_ex(tabs, di.to(torch.int32), do.to(torch.int32), dw)
+    torch.cuda.synchronize()
+    assert torch.equal(pooled32.view(torch.int32), pooled.view(torch.int32)), "int32 indices != int64"
     S = sample_rows(wl.B, n_samples, wl.seed)
     sub_wl, sub, row_ids = batch.sample_subset(S)
     host_tabs = subset_tables(wl, row_ids)
@@ -212,6 +217,17 @@ def test_workload_multihot_backward(weighted, opt):
                        to_dev(b.weights) if weighted else None, to_dev(gp), opt, wl.lr, wl.eps if adagrad else 0.0,
                        outputs=outs)
     torch.cuda.synchronize()
+    if not weighted and adagrad:
+        # the same update from int32 indices and offsets, on fresh tables: the same bits
+        tabs32 = device_tables(wl)
+        states32 = [torch.zeros(v, dtype=torch.float32, device=DEV) for v in wl.rows]
+        emb_bag_bwd_update(tabs32, states32, to_dev(b.indices.astype(np.int32)), to_dev(b.offsets.astype(np.int32)),
+                           None, to_dev(gp), opt, wl.lr, wl.eps)
+        torch.cuda.synchronize()
+        for x, y in zip(tabs + states, tabs32 + states32):
+            assert torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
+                               y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)), "int32 != int64"
+        del tabs32, states32
 
     sub_wl, sub, row_ids = b.sample_subset(np.arange(wl.B))
     host_tabs = subset_tables(wl, row_ids)
