@@ -77,6 +77,10 @@ def check_forward(wl, batch, tabs, n_samples=256):
     pooled32 = emb_bag_fwd_ex(tabs, di.to(torch.int32), do.to(torch.int32), dw)
     torch.cuda.synchronize()
     assert torch.equal(pooled32.view(torch.int32), pooled.view(torch.int32)), "int32 indices != int64"
+    # bf16 pooled output: the round-to-nearest-even of the fp32 output, bit for bit
+    pooled16 = emb_bag_fwd_ex(tabs, di, do, dw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(pooled16.view(torch.int16), pooled.to(torch.bfloat16).view(torch.int16)), "bf16 output != RNE"
     S = sample_rows(wl.B, n_samples, wl.seed)
     sub_wl, sub, row_ids = batch.sample_subset(S)
     host_tabs = subset_tables(wl, row_ids)
